@@ -1,0 +1,278 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU oracle for the fused
+ * attention forward pass.  TEST INFRASTRUCTURE ONLY: it is loaded by the
+ * tests, by the smoke check and by the benchmark's CPU-baseline leg, never by
+ * the product path.  It shares no code, header, table or helper with the HIP
+ * library; both sides see only the same seeded input tensors.
+ *
+ * Arithmetic is fp64 throughout.  Inputs arrive already widened to double
+ * (a bf16 or fp16 value widens to double exactly), outputs are double.
+ *
+ * What is computed (the plain definition the tiled online-softmax method
+ * reaches up to rounding order):
+ *
+ *   JAX Pallas Mosaic-GPU "FlashAttention3" page, function
+ *   `attention_reference`: upcast, logits = q.k per (query, key) with the
+ *   q-heads of one kv-head taken as a contiguous group (q reshaped to
+ *   (B, Sq, Hkv, Hq/Hkv, D)), mask, row max m, unnormalized = exp(logits - m),
+ *   l = row sum, weights = unnormalized / l, out = weights . v, and the
+ *   residual lse = m + log(l) (that page writes it in base 2; here it is the
+ *   natural log, see the header of oracle/__init__.py for the reading).
+ *
+ *   The logits are multiplied by `scale` (the Croqtile `flash_atten` page
+ *   folds 1/sqrt(128) into its exponent; the JAX reference applies none,
+ *   i.e. scale = 1).  The causal mask is aligned bottom-right: key j is
+ *   visible from query i iff j <= i + (Skv - Sq).  For Sq == Skv this is the
+ *   JAX reference's `arange(Sq)[:, None] >= arange(Skv)[None, :]`.  A row
+ *   with no visible key gets O = 0 and LSE = -inf (the log of an empty sum;
+ *   the same (-inf, 0, 0) identity the kernbench merge is seeded with).
+ *
+ * Two passes per row, as the definition reads: pass 1 computes every visible
+ * logit and the max, pass 2 the exponentials, their sum and the weighted sum
+ * of V rows, then one division.
+ *
+ * Parallelism: rows are independent; an OpenMP loop over rows changes no
+ * arithmetic (each row is computed start to finish by one thread, in key
+ * order).
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, o : [B, Sq, Hq, D]      k, v : [B, Skv, Hkv, D]      lse : [B, Hq, Sq]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of threads the OpenMP loops use; 0 means the OpenMP default. */
+static int g_threads = 0;
+
+void oracle_set_threads(int n) { g_threads = n; }
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Largest visible key index + 1 for query row i (0 if none is visible). */
+static int64_t visible_end(int64_t i, int64_t Sq, int64_t Skv, int causal) {
+  if (!causal) return Skv;
+  int64_t last = i + (Skv - Sq); /* bottom-right alignment */
+  if (last < 0) return 0;
+  if (last >= Skv) return Skv;
+  return last + 1;
+}
+
+/*
+ * One output row (b, hq, i).  `s` is caller-provided scratch of Skv doubles.
+ * Visible keys are the range [j_lo, j_hi) intersected with the causal set;
+ * the full definition uses j_lo = 0, j_hi = Skv.
+ *
+ * Writes m (the max logit, -inf if no key is visible), l (sum of
+ * exp(logit - m), 0 if none) and acc[D] (sum of exp(logit - m) * V_j,
+ * unnormalized).
+ */
+static void row_partial(const double* q, const double* k, const double* v,
+                        int64_t b, int64_t hq, int64_t i, int64_t Sq,
+                        int64_t Skv, int64_t Hq, int64_t Hkv, int64_t D,
+                        int causal, double scale, int64_t j_lo, int64_t j_hi,
+                        double* s, double* m_out, double* l_out, double* acc) {
+  const int64_t group = Hq / Hkv;  /* q-heads per kv-head */
+  const int64_t hk = hq / group;   /* contiguous grouping */
+  int64_t end = visible_end(i, Sq, Skv, causal);
+  if (j_hi > end) j_hi = end;
+  if (j_lo < 0) j_lo = 0;
+
+  const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
+
+  /* pass 1: logits and their max */
+  double m = -INFINITY;
+  for (int64_t j = j_lo; j < j_hi; ++j) {
+    const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += qrow[d] * krow[d];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+
+  /* pass 2: exponentials, their sum and the weighted sum of V rows */
+  double l = 0.0;
+  for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+  for (int64_t j = j_lo; j < j_hi; ++j) {
+    double p = exp(s[j] - m);
+    l += p;
+    const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
+    for (int64_t d = 0; d < D; ++d) acc[d] += p * vrow[d];
+  }
+  *m_out = m;
+  *l_out = l;
+}
+
+static int check_shape(int64_t B, int64_t Sq, int64_t Skv, int64_t Hq,
+                       int64_t Hkv, int64_t D) {
+  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1) return -1;
+  if (Hq % Hkv != 0) return -1;
+  return 0;
+}
+
+/*
+ * Full forward: every (b, hq, i) row.  lse may be NULL.
+ * Returns 0, or -1 on a bad shape, -2 if scratch cannot be allocated.
+ */
+int oracle_attn_fwd(const double* q, const double* k, const double* v,
+                    double* o, double* lse, int64_t B, int64_t Sq, int64_t Skv,
+                    int64_t Hq, int64_t Hkv, int64_t D, int causal,
+                    double scale) {
+  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
+  const int64_t rows = B * Hq * Sq;
+  int failed = 0;
+#pragma omp parallel num_threads(oracle_threads())
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / (Hq * Sq);
+        int64_t hq = (r / Sq) % Hq;
+        int64_t i = r % Sq;
+        double m, l;
+        row_partial(q, k, v, b, hq, i, Sq, Skv, Hq, Hkv, D, causal, scale, 0,
+                    Skv, s, &m, &l, acc);
+        double* orow = o + ((b * Sq + i) * Hq + hq) * D;
+        if (l > 0.0) {
+          for (int64_t d = 0; d < D; ++d) orow[d] = acc[d] / l;
+          if (lse) lse[(b * Hq + hq) * Sq + i] = m + log(l);
+        } else {
+          for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+          if (lse) lse[(b * Hq + hq) * Sq + i] = -INFINITY;
+        }
+      }
+    }
+    free(s);
+    free(acc);
+  }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Selected rows only, for checks at sizes where the full forward is too slow.
+ * rows_bhi holds n triples (b, hq, i).  o_rows is [n, D], lse_rows is [n].
+ */
+int oracle_attn_rows(const double* q, const double* k, const double* v,
+                     int64_t B, int64_t Sq, int64_t Skv, int64_t Hq,
+                     int64_t Hkv, int64_t D, int causal, double scale,
+                     const int64_t* rows_bhi, int64_t n, double* o_rows,
+                     double* lse_rows) {
+  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t b = rows_bhi[3 * r], hq = rows_bhi[3 * r + 1],
+            i = rows_bhi[3 * r + 2];
+    if (b < 0 || b >= B || hq < 0 || hq >= Hq || i < 0 || i >= Sq) return -1;
+  }
+  int failed = 0;
+#pragma omp parallel num_threads(oracle_threads())
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < n; ++r) {
+        int64_t b = rows_bhi[3 * r], hq = rows_bhi[3 * r + 1],
+                i = rows_bhi[3 * r + 2];
+        double m, l;
+        row_partial(q, k, v, b, hq, i, Sq, Skv, Hq, Hkv, D, causal, scale, 0,
+                    Skv, s, &m, &l, acc);
+        double* orow = o_rows + r * D;
+        if (l > 0.0) {
+          for (int64_t d = 0; d < D; ++d) orow[d] = acc[d] / l;
+          lse_rows[r] = m + log(l);
+        } else {
+          for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+          lse_rows[r] = -INFINITY;
+        }
+      }
+    }
+    free(s);
+    free(acc);
+  }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Unnormalized partial state of every row over the keys [j_lo, j_hi) (still
+ * subject to the causal mask): m [B,Hq,Sq], l [B,Hq,Sq], acc [B,Sq,Hq,D].
+ * This is the (m, l, O) triple of one tile of the kernbench tile sweep, whose
+ * O is left unnormalized until the root divides by l.
+ */
+int oracle_attn_partial(const double* q, const double* k, const double* v,
+                        int64_t B, int64_t Sq, int64_t Skv, int64_t Hq,
+                        int64_t Hkv, int64_t D, int causal, double scale,
+                        int64_t j_lo, int64_t j_hi, double* m_out,
+                        double* l_out, double* acc_out) {
+  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
+  const int64_t rows = B * Hq * Sq;
+  int failed = 0;
+#pragma omp parallel num_threads(oracle_threads())
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / (Hq * Sq);
+        int64_t hq = (r / Sq) % Hq;
+        int64_t i = r % Sq;
+        double* acc = acc_out + ((b * Sq + i) * Hq + hq) * D;
+        row_partial(q, k, v, b, hq, i, Sq, Skv, Hq, Hkv, D, causal, scale,
+                    j_lo, j_hi, s, &m_out[r], &l_out[r], acc);
+      }
+    }
+    free(s);
+  }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Online-softmax merge of two partial triples, following the kernbench
+ * prefill page, `_merge_running`: the new max is the larger of the two, each
+ * side is weighted by exp(its max - new max), the sums and the unnormalized
+ * outputs are added with those weights.  One guard is added: when both maxima
+ * are -inf (neither side saw a visible key) the result is the identity
+ * (-inf, 0, 0) instead of exp(-inf - -inf) = NaN.
+ *
+ * n rows; acc arrays are [n, D].  Output arrays may alias the first input.
+ */
+void oracle_merge(int64_t n, int64_t D, const double* m1, const double* l1,
+                  const double* acc1, const double* m2, const double* l2,
+                  const double* acc2, double* m_out, double* l_out,
+                  double* acc_out) {
+  for (int64_t r = 0; r < n; ++r) {
+    double m = m1[r] > m2[r] ? m1[r] : m2[r];
+    if (m == -INFINITY) {
+      m_out[r] = -INFINITY;
+      l_out[r] = 0.0;
+      for (int64_t d = 0; d < D; ++d) acc_out[r * D + d] = 0.0;
+      continue;
+    }
+    double a = exp(m1[r] - m);
+    double c = exp(m2[r] - m);
+    l_out[r] = l1[r] * a + l2[r] * c;
+    for (int64_t d = 0; d < D; ++d)
+      acc_out[r * D + d] = acc1[r * D + d] * a + acc2[r * D + d] * c;
+    m_out[r] = m;
+  }
+}
