@@ -1,0 +1,131 @@
+// fa_api.cpp -- the C-ABI entry points of libfa (declared in include/fa.h).
+//
+// Argument checks follow the split the JAX Pallas FlashAttention3 page draws
+// in `_attention_forward`: malformed arguments (shapes that do not agree, a
+// q-head count that is not a multiple of the kv-head count) are errors,
+// well-formed requests outside what the kernel implements (head dimensions
+// other than 64 and 128 here) are "not implemented".  Unlike that page, any
+// sequence lengths >= 1 are accepted; the kernel masks ragged tails.
+//
+// Every check runs before the first HIP call, so invalid calls never touch
+// the device.
+
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "fa.h"
+#include "fa_kernel.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p + bytes) and [r, r + rbytes) overlap?
+bool overlap(const void* p, uint64_t bytes, const void* r, uint64_t rbytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(r);
+  return a < b + rbytes && b < a + bytes;
+}
+
+int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o,
+        float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,
+        float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID;
+  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1) return FA_ERR_INVALID;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (!isfinite(scale)) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID;
+
+  // element counts in 64 bits, rejecting overflow
+  uint64_t nq_el, nkv_el, nlse;
+  if (__builtin_mul_overflow((uint64_t)B, (uint64_t)Sq, &nq_el) ||
+      __builtin_mul_overflow(nq_el, (uint64_t)Hq, &nq_el) ||
+      __builtin_mul_overflow(nq_el, (uint64_t)D, &nq_el) ||
+      __builtin_mul_overflow((uint64_t)B, (uint64_t)Skv, &nkv_el) ||
+      __builtin_mul_overflow(nkv_el, (uint64_t)Hkv, &nkv_el) ||
+      __builtin_mul_overflow(nkv_el, (uint64_t)D, &nkv_el) ||
+      __builtin_mul_overflow((uint64_t)B, (uint64_t)Hq, &nlse) ||
+      __builtin_mul_overflow(nlse, (uint64_t)Sq, &nlse) || nq_el > (UINT64_MAX >> 2) ||
+      nkv_el > (UINT64_MAX >> 2) || nlse > (UINT64_MAX >> 3))
+    return FA_ERR_INVALID;
+
+  // o must not overlap any input (nor lse)
+  const uint64_t qb = nq_el * 2, kvb = nkv_el * 2;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kvb) || overlap(o, qb, v, kvb))
+    return FA_ERR_INVALID;
+  if (lse && overlap(o, qb, lse, nlse * 4)) return FA_ERR_INVALID;
+
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
+  // index arithmetic inside the kernel is 32-bit for positions
+  if (Sq > INT_MAX - 1024 || Skv > INT_MAX - 1024) return FA_ERR_UNSUPPORTED;
+  if (fa::grid_blocks(B, Sq, Hq) > (int64_t)INT_MAX) return FA_ERR_UNSUPPORTED;
+
+  // exponent constant: scale * log2(e), folded so that p = exp2(s*c - m*c).
+  // A zero (or sub-FLT_MIN) scale is taken as FLT_MIN: every exp2 argument
+  // then rounds to 0 in fp32, which is exactly the scale = 0 result, while
+  // masked logits (-inf) still map to -inf instead of 0 * inf.
+  double cd = (double)scale * 1.4426950408889634074;
+  float c = (float)cd;
+  if (!(c >= FLT_MIN)) c = FLT_MIN;
+  if (!isfinite(c)) return FA_ERR_UNSUPPORTED;
+
+  fa::LaunchArgs a;
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.causal = causal;
+  a.c = c;
+  a.stream = stream;
+  return fa::launch(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+           int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
+           hipStream_t stream) {
+  return fwd(fa::DType::kBF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale,
+             stream);
+}
+
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
+               hipStream_t stream) {
+  return fwd(fa::DType::kF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale,
+             stream);
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK:
+      return "success";
+    case FA_ERR_INVALID:
+      return "invalid argument";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported argument (D must be 64 or 128, scale >= 0)";
+    case FA_ERR_HIP:
+      return "HIP runtime error at kernel launch";
+    default:
+      return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+/*
+ * fa.h -- libfa: fused attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every batch b, query head hq and query row i,
+ *
+ *     O[b,i,hq,:] = sum_j softmax_j( scale * Q[b,i,hq,:] . K[b,j,hk,:] ) * V[b,j,hk,:]
+ *     LSE[b,hq,i] = ln sum_j exp( scale * Q[b,i,hq,:] . K[b,j,hk,:] )
+ *
+ * over the visible keys j, with hk = hq / (Hq / Hkv) (grouped-query heads:
+ * each kv-head serves a contiguous group of Hq/Hkv query heads).
+ *
+ * The operation is the one every page on the tiled online-softmax ("flash")
+ * attention forward pass implements: the JAX Pallas Mosaic-GPU
+ * FlashAttention3 page (`attention_reference` gives the definition; `kv_loop`
+ * the running max m, running sum l and rescaled accumulator; its
+ * `_memory_wg` maps q-head to kv-head by integer division), the Croqtile
+ * tutorial's non-persistent `flash_atten` (scale folded into an exp2
+ * exponent, causal tiles) and the kernbench GQA prefill page
+ * (`_merge_running`, the online-softmax merge of partial (m, l, O) triples).
+ *
+ * Masking: with causal = 0 every key 0 <= j < Skv is visible.  With
+ * causal = 1 the mask is aligned bottom-right: key j is visible from query i
+ * iff j <= i + (Skv - Sq).  When Sq == Skv this is the pages' j <= i.  A row
+ * with no visible key (only possible when Sq > Skv) gets O = 0, LSE = -inf.
+ *
+ * LSE is the natural-log log-sum-exp of the scaled logits (the JAX page
+ * stores the base-2 value m*log2(e) + log2(l); multiply ours by log2(e) to
+ * get it).
+ *
+ * Arithmetic: both products on MFMA with fp32 accumulation; the softmax in
+ * fp32 with hardware exp2; the probabilities are rounded to the input dtype
+ * (round-to-nearest-even) before the second product; O is rounded once to
+ * the input dtype at the end.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every argument check runs on the host before any HIP call,
+ * so an invalid call returns without touching the device. */
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,     /* bad argument: NULL pointer, size < 1, Hq % Hkv != 0,
+                              causal not 0/1, scale not finite, pointer not
+                              16-byte aligned, o overlapping q/k/v, size overflow */
+  FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64 or 128,
+                              scale < 0, grid larger than the launch limit */
+  FA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * fa_fwd -- bf16 inputs and output.
+ *
+ *   q    : device pointer, [B, Sq, Hq, D] bf16, contiguous (row-major, "BSHD")
+ *   k, v : device pointers, [B, Skv, Hkv, D] bf16, contiguous
+ *   o    : device pointer, [B, Sq, Hq, D] bf16, written; must not overlap q, k or v
+ *   lse  : device pointer, [B, Hq, Sq] fp32, written; may be NULL (not written)
+ *   B, Sq, Skv, Hq, Hkv : sizes >= 1, Hq a multiple of Hkv
+ *   D    : head dimension, 64 or 128
+ *   causal : 0 (no mask) or 1 (bottom-right aligned causal mask)
+ *   scale  : multiplies the logits before the softmax; finite and >= 0
+ *            (usually 1/sqrt(D))
+ *   stream : HIP stream to enqueue on (NULL = the default stream)
+ *
+ * All pointers are owned by the caller and must be 16-byte aligned.  The
+ * library allocates no memory and keeps no state between calls; calls on
+ * different streams may run concurrently.  The call is asynchronous: it
+ * returns once the kernel is enqueued, and o / lse are valid after the
+ * stream has been synchronised.
+ *
+ * Returns FA_OK or one of the error codes above.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,
+           float scale, hipStream_t stream);
+
+/* fa_fwd_f16 -- identical to fa_fwd, with fp16 q, k, v and o. */
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o,
+               float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
+               int causal, float scale, hipStream_t stream);
+
+/* fa_strerror -- a static, NUL-terminated description of a status code
+ * (never NULL; unknown codes give "unknown fa_status"). */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */
