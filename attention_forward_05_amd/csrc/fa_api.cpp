@@ -63,9 +63,16 @@ int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o,
 
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
-  // index arithmetic inside the kernel is 32-bit for positions
-  if (Sq > INT_MAX - 1024 || Skv > INT_MAX - 1024) return FA_ERR_UNSUPPORTED;
-  if (fa::grid_blocks(B, Sq, Hq) > (int64_t)INT_MAX) return FA_ERR_UNSUPPORTED;
+  // Size limits of the kernel's 32-bit address arithmetic and launch grid:
+  // grid y (query tiles) and z (batch) at most 65535; one batch slice of q/o
+  // below 2 GiB; key tiles below 65536; B*Sq*Hq and B*Skv below 2^31.
+  if (fa::query_tiles(Sq) > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)Sq * (uint64_t)Hq * (uint64_t)D * 2u >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * (uint64_t)Sq * (uint64_t)Hq >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * (uint64_t)Skv >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+  if (fa::key_tiles(Skv) >= 65536) return FA_ERR_UNSUPPORTED;
+  uint32_t magic;
+  if (!fa::group_magic(Hq, Hkv, &magic)) return FA_ERR_UNSUPPORTED;
 
   // exponent constant: scale * log2(e), folded so that p = exp2(s*c - m*c).
   // A zero (or sub-FLT_MIN) scale is taken as FLT_MIN: every exp2 argument
@@ -120,7 +127,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_INVALID:
       return "invalid argument";
     case FA_ERR_UNSUPPORTED:
-      return "unsupported argument (D must be 64 or 128, scale >= 0)";
+      return "unsupported argument (D must be 64 or 128, scale >= 0, sizes within the kernel's limits)";
     case FA_ERR_HIP:
       return "HIP runtime error at kernel launch";
     default:

@@ -1,5 +1,5 @@
 // fa_kernel.h -- internal interface between the C-ABI entry points and the
-// gfx950 kernel (not installed, not part of the public ABI).
+// gfx950 kernel launcher (not installed, not part of the public ABI).
 #pragma once
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -20,10 +20,17 @@ struct LaunchArgs {
   hipStream_t stream;
 };
 
-// Number of workgroups the kernel launches for these sizes.
+// Workgroups launched for these sizes.
 int64_t grid_blocks(int B, int Sq, int Hq);
+// Query tiles of 256 rows and key tiles of 64 keys.
+int query_tiles(int Sq);
+int key_tiles(int Skv);
+// Multiplier m with (hq * m) >> 20 == hq / (Hq / Hkv) for every hq < Hq,
+// or false when no 32-bit product does it.
+bool group_magic(int Hq, int Hkv, uint32_t* magic);
 
-// Enqueue the kernel; returns hipGetLastError() after the launch.
+// Enqueue the kernel (loading the code object on first use on the current
+// device); returns the launch status.
 hipError_t launch(const LaunchArgs& a);
 
 }  // namespace fa

@@ -1,0 +1,127 @@
+// fa_launch.cpp -- loads the gfx950 attention kernels (assembled from the
+// generator in attention_forward_05_amd/asm and embedded in this library as a
+// code object) and launches them.
+//
+// Grid: x = q-head slot (Hq), y = query tile of 256 rows (nq), z = batch.
+// Workgroups are handed to the 8 XCDs round-robin by linear id, whose
+// residue mod 8 is x mod 8 when Hq % 8 == 0; the kernel then maps slot x to
+// head (x % 8) * (Hq / 8) + x / 8 so each XCD serves a contiguous run of
+// heads (whole GQA groups), whose K/V its L2 keeps.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "fa_kernel.h"
+
+extern "C" const unsigned char fa_hsaco_data[];
+extern "C" const unsigned long fa_hsaco_size;
+
+namespace fa {
+namespace {
+
+constexpr int kBM = 256;       // query rows per workgroup
+constexpr int kBN = 64;        // keys per tile
+constexpr int kMaxDevices = 64;
+
+struct alignas(8) KernArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t B, Sq, Skv, Hq, Hkv, causal;
+  float c;
+  int32_t nq;
+  uint32_t gmagic;  // hk = (hq * gmagic) >> 20
+  uint32_t hq_xcd;  // Hq / 8 when Hq % 8 == 0, else 0
+};
+static_assert(sizeof(KernArgs) == 80, "kernarg layout of the generated kernels");
+
+const char* kNames[4] = {"fa_fwd_bf16_d128_gfx950", "fa_fwd_bf16_d64_gfx950",
+                         "fa_fwd_f16_d128_gfx950", "fa_fwd_f16_d64_gfx950"};
+
+struct DeviceKernels {
+  bool loaded = false;
+  hipModule_t mod = nullptr;
+  hipFunction_t fn[4] = {};
+};
+
+std::mutex g_mu;
+DeviceKernels g_dev[kMaxDevices];
+
+hipError_t kernels_for_current_device(DeviceKernels** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceKernels& d = g_dev[dev];
+  if (!d.loaded) {
+    e = hipModuleLoadData(&d.mod, fa_hsaco_data);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < 4; ++i) {
+      e = hipModuleGetFunction(&d.fn[i], d.mod, kNames[i]);
+      if (e != hipSuccess) return e;
+    }
+    d.loaded = true;
+  }
+  *out = &d;
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool group_magic(int Hq, int Hkv, uint32_t* magic) {
+  const uint32_t g = (uint32_t)(Hq / Hkv);
+  const uint64_t m = (1ull << 20) / g + 1;
+  for (int hq = 0; hq < Hq; ++hq) {
+    const uint64_t p = (uint64_t)hq * m;
+    if (p >> 32) return false;
+    if ((uint32_t)(p >> 20) != (uint32_t)hq / g) return false;
+  }
+  *magic = (uint32_t)m;
+  return true;
+}
+
+int64_t grid_blocks(int B, int Sq, int Hq) {
+  return (int64_t)((Sq + kBM - 1) / kBM) * B * Hq;
+}
+
+int query_tiles(int Sq) { return (Sq + kBM - 1) / kBM; }
+int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
+
+hipError_t launch(const LaunchArgs& a) {
+  DeviceKernels* dk = nullptr;
+  hipError_t e = kernels_for_current_device(&dk);
+  if (e != hipSuccess) return e;
+  const int variant = (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
+  KernArgs ka;
+  memset(&ka, 0, sizeof(ka));
+  ka.q = a.q;
+  ka.k = a.k;
+  ka.v = a.v;
+  ka.o = a.o;
+  ka.lse = a.lse;
+  ka.B = a.B;
+  ka.Sq = a.Sq;
+  ka.Skv = a.Skv;
+  ka.Hq = a.Hq;
+  ka.Hkv = a.Hkv;
+  ka.causal = a.causal;
+  ka.c = a.c;
+  ka.nq = query_tiles(a.Sq);
+  if (!group_magic(a.Hq, a.Hkv, &ka.gmagic)) return hipErrorInvalidValue;
+  ka.hq_xcd = (a.Hq % 8 == 0) ? (uint32_t)(a.Hq / 8) : 0u;
+  size_t size = sizeof(ka);
+  void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &ka, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
+                    HIP_LAUNCH_PARAM_END};
+  e = hipModuleLaunchKernel(dk->fn[variant], (unsigned)a.Hq, (unsigned)ka.nq, (unsigned)a.B, 256,
+                            1, 1, 0, a.stream, nullptr, config);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+One step = one call of the library's forward entry point over the whole
+workload (all of: Q/K/V tile loads, both MFMA products, the online softmax,
+the masked tiles and the epilogue run inside that one kernel).  Inputs are
+synthetic (seeded N(0,1), rounded to the working dtype) and resident in HBM
+before the timed region starts.
+
+Prints ONE JSON line on stdout:
+  metric / value / unit   causal-adjusted TFLOP/s of the workload
+  roofline                the kernel's achieved TFLOP/s against the dense
+                          MFMA peak of its dtype (from per-launch HIP events on
+                          the stream the kernel is launched on), plus measured
+                          HBM traffic when the counter file matches the kernel
+  cpu_baseline            the CPU oracle timed on a bounded sample of rows of
+                          the same workload, on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 GPU"
+# Published dense MFMA peak of one MI355X for bf16 and fp16 (TFLOP/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
+# the kernels are generated from these sources; a traffic file taken on other
+# sources no longer describes the kernel
+KERNEL_SRCS = [os.path.join(ROOT, "attention_forward_05_amd", "asm", n)
+               for n in ("fa_fwd_gen.py", "regs.py")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """Bytes per launch from the committed counter summary, or None when the
+    file is absent or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    entry = t.get("workloads", {}).get(workload_name)
+    if not entry:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w: workloads.Workload, q, k, v, target_s: float = 12.0):
+    """Time the CPU oracle on uniformly sampled rows of the workload and
+    scale to TFLOP/s with the same per-row FLOP count as the GPU metric."""
+    import numpy as np
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    n_rows_total = w.B * w.Hq * w.Sq
+
+    def rows_and_flops(n):
+        r = np.stack([rng.integers(0, w.B, n), rng.integers(0, w.Hq, n),
+                      rng.integers(0, w.Sq, n)], axis=1).astype(np.int64)
+        i = r[:, 2]
+        if w.causal:
+            vis = np.clip(i + (w.Skv - w.Sq) + 1, 0, w.Skv)
+        else:
+            vis = np.full(n, w.Skv)
+        return r, float((4.0 * w.D * vis).sum())
+
+    # widen once (not timed: the oracle's inputs are fp64 arrays)
+    qd, kd, vd = oracle._f64(q), oracle._f64(k), oracle._f64(v)
+    pilot = 64
+    r, fl = rows_and_flops(pilot)
+    t0 = time.perf_counter()
+    oracle.attn_rows(qd, kd, vd, w.causal, w.scale, r)
+    t_pilot = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(n_rows_total, max(pilot, pilot * target_s / t_pilot)))
+    r, fl = rows_and_flops(n)
+    t0 = time.perf_counter()
+    oracle.attn_rows(qd, kd, vd, w.causal, w.scale, r)
+    dt = time.perf_counter() - t0
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {n_rows_total} query rows drawn uniformly over (b, hq, i); "
+                  f"{fl / 1e9:.1f} GFLOP in {dt:.2f} s (fp64, OpenMP over rows)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=workloads.HEADLINE.name,
+                    choices=[w.name for w in workloads.WORKLOADS])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the kernel has no multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_forward_05_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+
+    w = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    entry = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f16
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        st = entry(qd, kd, vd, od, lsed, w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D,
+                   int(w.causal), w.scale, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole timed region
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # per-launch durations (same stream), for the roofline figure
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    launch_avg_ms = sum(launch_ms) / len(launch_ms)
+
+    flops = workloads.attention_flops(w.B, w.Sq, w.Skv, w.Hq, w.D, w.causal)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(w.name)
+    log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
+        f"({100 * value / peak:.1f}% of {peak:.0f}); launch avg {launch_avg_ms * 1e3:.1f} us, "
+        f"min {launch_ms[0] * 1e3:.1f} us, median {launch_ms[len(launch_ms) // 2] * 1e3:.1f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of rows ...")
+        cpu = cpu_baseline(w, q, k, v)
+        log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs rounded to the dtype, resident in HBM)",
+        "config": {
+            "workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+            "Skv": w.Skv, "D": w.D, "causal": w.causal, "scale": w.scale,
+            "flops_per_step": flops, "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_launch_avg_us": round(launch_avg_ms * 1e3, 2),
+            "kernel": f"fa_fwd_{w.dtype}_d{w.D}_gfx950",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,8 +49,12 @@ typedef enum {
                               causal not 0/1, scale not finite, pointer not
                               16-byte aligned, o overlapping q/k/v, size overflow */
   FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64 or 128,
-                              scale < 0, grid larger than the launch limit */
-  FA_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+                              scale < 0, sizes beyond the kernel's limits
+                              (ceil(Sq/256) and B at most 65535, ceil(Skv/64)
+                              below 65536, Sq*Hq*D*2 bytes, B*Sq*Hq and B*Skv
+                              below 2^31) */
+  FA_ERR_HIP = -3          /* the HIP runtime reported an error loading the
+                              kernels or at launch */
 } fa_status;
 
 /*
@@ -68,10 +72,13 @@ typedef enum {
  *   stream : HIP stream to enqueue on (NULL = the default stream)
  *
  * All pointers are owned by the caller and must be 16-byte aligned.  The
- * library allocates no memory and keeps no state between calls; calls on
- * different streams may run concurrently.  The call is asynchronous: it
- * returns once the kernel is enqueued, and o / lse are valid after the
- * stream has been synchronised.
+ * only state the library keeps is its kernel code: the first call on a
+ * device loads the library's gfx950 code object on that device (under a
+ * lock, so concurrent first calls are safe) and keeps it until the process
+ * ends; a failed load returns FA_ERR_HIP.  No other memory is allocated.
+ * Calls on different streams may run concurrently.  The call is
+ * asynchronous: it returns once the kernel is enqueued, and o / lse are
+ * valid after the stream has been synchronised.
  *
  * Returns FA_OK or one of the error codes above.
  */
