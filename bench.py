@@ -17,7 +17,16 @@ Prints ONE JSON line on stdout:
                           the same workload, on this host's cores
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--calibrate-copy BYTES]
+       python bench.py --traffic-summary FETCH_CSV WRITE_CSV --copy-bytes BYTES
+
+HBM traffic: run the bench twice under `rocprofv3 --pmc FETCH_SIZE` and
+`rocprofv3 --pmc WRITE_SIZE` with --calibrate-copy BYTES, which first copies
+BYTES bytes device-to-device.  The counters read for that plain copy give
+the factor between counter units and bytes moved; --traffic-summary applies
+it to the attention kernel's dispatches and writes profiles/hbm_traffic.json,
+which later bench runs report as roofline.traffic (only while the kernel
+sources still hash to the value recorded there).
 """
 from __future__ import annotations
 
@@ -73,6 +82,58 @@ def measured_traffic(workload_name: str):
     return entry.get("bytes_per_launch")
 
 
+def algorithmic_bytes(w: workloads.Workload) -> int:
+    """Bytes one launch must move at least: Q, K, V read once, O and LSE
+    written once."""
+    el = 2
+    return (2 * w.B * w.Sq * w.Hq * w.D * el + 2 * w.B * w.Skv * w.Hkv * w.D * el
+            + 4 * w.B * w.Hq * w.Sq)
+
+
+def _pmc_rows(path):
+    """(kernel name, dispatch id, counter value) of every row of a rocprofv3
+    counter-collection CSV."""
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            out.append((row["Kernel_Name"], row.get("Dispatch_Id", ""), float(row["Counter_Value"])))
+    return out
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload_name: str):
+    """Scale the attention kernel's FETCH_SIZE / WRITE_SIZE (KiB) by what the
+    same counters read for the calibration copy of `copy_bytes` bytes."""
+    res = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _pmc_rows(path)
+        # per dispatch: sum the counter's rows (one per counter instance)
+        per = {}
+        for name, did, val in rows:
+            per.setdefault((name, did), 0.0)
+            per[(name, did)] += val
+        fa_vals = [v for (n, _), v in per.items() if n.startswith("fa_fwd_")]
+        others = [(v, n) for (n, _), v in per.items() if not n.startswith("fa_fwd_")]
+        if not fa_vals or not others:
+            raise SystemExit(f"{path}: no attention or no copy dispatch found")
+        copy_kib, copy_name = max(others)
+        factor = copy_kib * 1024.0 / copy_bytes
+        res[key] = {"kernel_kib_avg": sum(fa_vals) / len(fa_vals), "dispatches": len(fa_vals),
+                    "copy_kib": copy_kib, "copy_kernel": copy_name,
+                    "factor_counter_bytes_per_byte": factor,
+                    "bytes": sum(fa_vals) / len(fa_vals) * 1024.0 / factor}
+    w = workloads.BY_NAME[workload_name]
+    return {
+        "bytes_per_launch": round(res["fetch"]["bytes"] + res["write"]["bytes"]),
+        "fetch_bytes": round(res["fetch"]["bytes"]),
+        "write_bytes": round(res["write"]["bytes"]),
+        "algorithmic_bytes": algorithmic_bytes(w),
+        "copy_bytes": copy_bytes,
+        "fetch": res["fetch"],
+        "write": res["write"],
+    }
+
+
 def cpu_baseline(w: workloads.Workload, q, k, v, target_s: float = 12.0):
     """Time the CPU oracle on uniformly sampled rows of the workload and
     scale to TFLOP/s with the same per-row FLOP count as the GPU metric."""
@@ -122,7 +183,28 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE.name,
                     choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="first copy BYTES bytes device-to-device (HBM counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--copy-bytes", type=int, default=0)
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        entry = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
+                                args.copy_bytes, args.workload)
+        try:
+            with open(TRAFFIC_FILE) as f:
+                doc = json.load(f)
+        except (OSError, ValueError):
+            doc = {}
+        if doc.get("kernel_source_sha256_16") != kernel_source_hash():
+            doc = {"kernel_source_sha256_16": kernel_source_hash(), "workloads": {}}
+        doc["workloads"][args.workload] = entry
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(doc, f, indent=1, sort_keys=True)
+            f.write("\n")
+        print(json.dumps(entry))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -139,6 +221,13 @@ def main():
 
     w = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
+    if args.calibrate_copy > 0:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     q, k, v = workloads.workload_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     od = torch.empty_like(qd)
