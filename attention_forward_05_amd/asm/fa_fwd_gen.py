@@ -35,18 +35,21 @@ from __future__ import annotations
 
 import math
 
-from .regs import Alloc, Emitter, interleave
+from .regs import Alloc, Emitter, Op, weave
 
 BM = 256          # query rows per workgroup
 BN = 64           # keys per tile
 WAVES = 4
-RESCALE = 8.0     # lazy-rescale threshold (exp2 units)
+KSLOTS = 4        # K tiles held in LDS
+VSLOTS = 5        # V tiles held in LDS
+PREFETCH = 4      # tiles loaded ahead of the tile whose keys are multiplied next
+THRESH = 32768.0  # lazy-rescale trigger: a half-row sum of p above 2^15
 KERNARG_BYTES = 80
 LN2 = 0.6931471805599453
 
 # kernarg offsets
 KA = dict(q=0, k=8, v=16, o=24, lse=32, B=40, Sq=44, Skv=48, Hq=52, Hkv=56,
-          causal=60, c=64, nq=68, gmagic=72, hq_xcd=76)
+          causal=60, c=64, nq_grid=68, gmagic=72, hq_xcd=76)   # nq_grid = nq | G << 16
 
 
 def kernel_name(dtype: str, D: int) -> str:
@@ -72,10 +75,9 @@ class Gen:
         self.CH = D // 8             # 16-byte chunks per row
         self.RPD = 64 // self.CH     # rows per 64-lane DMA instruction
         self.DPW = (BN // WAVES) // self.RPD  # DMA instructions per wave per K (or V) tile
-        self.VSLOTS, self.KSLOTS = 4, 3
         self.VBASE = 0
-        self.KBASE = self.VSLOTS * self.TILE
-        self.LDS = (self.VSLOTS + self.KSLOTS) * self.TILE
+        self.KBASE = VSLOTS * self.TILE
+        self.LDS = (VSLOTS + KSLOTS) * self.TILE
         self.em = Emitter()
         self._lab = 0
 
@@ -93,7 +95,7 @@ class Gen:
     # ------------------------------------------------------------------------
     def alloc(self):
         D, NS, NDB = self.D, self.NS, self.NDB
-        V = Alloc("v", 0, 256)
+        V = Alloc("v", 0, 512)
         A = Alloc("a", 0, 256)
         S = Alloc("s", 28, 102)
         self.v_tid = V.take("tid", 1)          # v0 on entry
@@ -113,39 +115,52 @@ class Gen:
         r["v_mc"] = V.take("mc", 2)
         r["v_mx"] = V.take("mx", 2)
         r["v_t"] = V.take("tmp", 8)
-        r["v_rs"] = V.take("rs", 2)
+        r["v_rs"] = V.take("rs", 2)            # half-row sums of the sub-tile
+        r["v_rb"] = V.take("rsb", 2)           # second partial sums
         r["v_d"] = V.take("dmask", 2)
         r["v_ninf"] = V.take("ninf", 1)       # -inf
-        r["v_resc"] = V.take("resc", 1)       # lazy-rescale threshold
+        r["v_thr"] = V.take("thr", 1)         # lazy-rescale trigger
         r["v_c"] = V.take("c", 1)             # scale * log2(e)
-        # S double buffer: S[buf][qb] 16 regs each
+        # S double buffer: S[buf][qb] 16 regs each; E: fp32 exponentials
         r["v_S"] = [[V.take(f"S{b}{q}", 16, 4) for q in range(2)] for b in range(2)]
+        r["v_E"] = [V.take(f"E{q}", 16, 4) for q in range(2)]
         # P double buffer: P[buf][qb][th] 4 regs each
         r["v_P"] = [[[V.take(f"P{b}{q}{t}", 4, 4) for t in range(2)] for q in range(2)]
                     for b in range(2)]
         r["v_KO"] = [V.take(f"KO{s}", 4, 4) for s in range(NS)]
-        r["v_VO"] = [[V.take(f"VO{t}{d}", 4, 4) for d in range(NDB)] for t in range(2)]
         self.nvgpr = (V.next + 7) // 8 * 8
-        # AGPRs: O^T accumulators and Q
+        # AGPRs: O^T accumulators, Q, and the V operands, double buffered
+        # VO[buf][th][db] (LDS reads may target AGPRs; MFMA reads them as A)
         r["a_O"] = [[A.take(f"O{q}{d}", 16, 4) for d in range(NDB)] for q in range(2)]
         r["a_Q"] = [[A.take(f"Q{q}{s}", 4, 4) for s in range(NS)] for q in range(2)]
+        r["v_VO"] = [[[A.take(f"VO{b}{t}{d}", 4, 4) for d in range(NDB)] for t in range(2)]
+                     for b in range(2)]
         self.nagpr = (A.next + 7) // 8 * 8
+        assert self.nvgpr <= 256 and self.nagpr <= 256, (self.nvgpr, self.nagpr)
         # SGPRs (s0:1 kernarg ptr, s2..s4 workgroup ids, s8..s27 kernargs)
         t = S.take
         r["s_hq"], r["s_qt"], r["s_b"], r["s_hk"] = t("hq", 1), t("qt", 1), t("b", 1), t("hk", 1)
         r["s_w"], r["s_qw0"], r["s_off"], r["s_ntiles"] = t("w", 1), t("qw0", 1), t("off", 1), t("nt", 1)
         r["s_kvfull"], r["s_rowlim"], r["s_rowb"], r["s_t"] = t("kvf", 1), t("rowlim", 1), t("rowb", 1), t("t", 1)
-        r["s_rq"] = t("rq", 4, 4)
         r["s_ro"] = t("ro", 4, 4)
         r["s_rl"] = t("rl", 4, 4)
         r["s_rk"] = t("rk", 4, 4)
+        # Q is loaded before the first K DMA descriptor is built: same registers
+        r["s_rq"] = r["s_rk"]
+        r["s_g"], r["s_r"] = t("wg", 1), t("round", 1)
+        r["s_nitems"], r["s_P"] = t("nitems", 1), t("pairs", 1)
         r["s_rv"] = t("rv", 4, 4)
         r["s_kb"] = t("kbase", 2, 2)
         r["s_vb"] = t("vbase", 2, 2)
-        r["s_ksl"], r["s_kdsl"] = t("ksl", 1), t("kdsl", 1)   # K slot read (t+1), K slot DMA (t+3)
+        # ring slots (byte offsets): K read slot of tile t+1 (relative to KBASE),
+        # K DMA slot of tile t+PREFETCH (relative), V slots of tiles t, t+1 and
+        # t+PREFETCH; the DMA slots with the wave's 16-row offset folded in
+        r["s_ksl"], r["s_kdsl"] = t("ksl", 1), t("kdsl", 1)
         r["s_vsl0"], r["s_vsl1"], r["s_vdsl"] = t("vsl0", 1), t("vsl1", 1), t("vdsl", 1)
+        r["s_kdw"], r["s_vdw"], r["s_wrow"] = t("kdw", 1), t("vdw", 1), t("wrow", 1)
         r["s_k0"] = t("k0", 1)
         r["s_x"] = [t(f"x{i}", 1) for i in range(6)]
+        r["s_y"] = [t(f"y{i}", 1) for i in range(6)]   # DMA stream scratch
         r["s_m1"], r["s_m2"] = t("msk1", 2, 2), t("msk2", 2, 2)
         r["s_neg"] = t("neginf", 1)
         r["s_row"] = t("row", 1)
@@ -161,9 +176,14 @@ class Gen:
     # ------------------------------------------------------------------------
     # prologue: kernargs, block mapping, ranges, descriptors, per-lane constants
     # ------------------------------------------------------------------------
-    def prologue(self):
+    # Persistent schedule: workgroup g of G takes, in round r, item
+    # r*G + (g if r is even else G-1-g) of the list of (batch, q-head, q-tile)
+    # items sorted longest first (causal: last q-tile first); the snake order
+    # gives every workgroup about the same number of key tiles.
+    # ------------------------------------------------------------------------
+    def kernel_setup(self):
+        """Once per workgroup: kernel arguments, wave index, constants."""
         em, D = self.em, self.D
-        x = self.s_x
         em.comment("kernel arguments")
         em.salu("s_load_dwordx16 s[8:23], s[0:1], 0x0")
         em.salu("s_load_dwordx4 s[24:27], s[0:1], 0x40")
@@ -171,27 +191,80 @@ class Gen:
         em.valu(f"v_readfirstlane_b32 {self.s_w}, v0", src=["v0"])
         em.salu(f"s_lshr_b32 {self.s_w}, {self.s_w}, 6")
         em.valu("v_and_b32 v0, 63, v0", dst=["v0"], src=["v0"])  # lane
+        em.salu(f"s_mov_b32 {self.s_g}, s2")
+        em.salu(f"s_mov_b32 {self.s_r}, 0")
         em.salu("s_waitcnt lgkmcnt(0)")
         em.salu(f"s_mov_b32 {self.s_neg}, 0xff800000")
         em.salu(f"s_mov_b32 {self.s_row}, {self.ROW}")
-        # hq: spread contiguous head groups over the 8 XCDs (workgroup x -> XCD x % 8)
-        l_no, l_done = self.lab("noxcd"), self.lab("xcd")
+        em.salu(f"s_mul_i32 {self.s_rowb}, s22, {D * 2}")          # K/V row stride
+        em.salu(f"s_mul_i32 {self.s_P}, s18, s21")                 # (batch, head) pairs
+        em.salu(f"s_and_b32 {self.s_x[0]}, s25, 0xffff")           # query tiles
+        em.salu(f"s_mul_i32 {self.s_nitems}, {self.s_P}, {self.s_x[0]}")
+        em.salu(f"s_mul_i32 {self.s_wrow}, {self.s_w}, {16 * self.ROW}")
+
+    def emit_div(self, num, den, q, rem):
+        """q = num / den, rem = num - q*den for num, den < 2^24 (VGPR num,
+        SGPR den): float reciprocal estimate, then one correction each way."""
+        em, t = self.em, self.v_t
+        dv = t.r(6)
+        em.valu(f"v_mov_b32 {dv}, {den}", dst=[dv])
+        em.valu(f"v_cvt_f32_u32 {q}, {num}", dst=[q], src=[num])
+        em.valu(f"v_cvt_f32_u32 {rem}, {dv}", dst=[rem], src=[dv])
+        em.valu(f"v_rcp_f32 {rem}, {rem}", dst=[rem], src=[rem], trans=True)
+        em.valu(f"v_mul_f32 {q}, {q}, {rem}", dst=[q], src=[q, rem])
+        em.valu(f"v_cvt_u32_f32 {q}, {q}", dst=[q], src=[q])
+        em.valu(f"v_mul_lo_u32 {rem}, {q}, {dv}", dst=[rem], src=[q, dv])
+        em.valu(f"v_sub_u32 {rem}, {num}, {rem}", dst=[rem], src=[num, rem])
+        # rem < 0 (as signed): q -= 1, rem += den
+        em.valu(f"v_cmp_gt_i32 vcc, 0, {rem}", src=[rem])
+        em.valu(f"v_cndmask_b32 {t.r(7)}, 0, -1, vcc", dst=[t.r(7)])
+        em.valu(f"v_add_u32 {q}, {q}, {t.r(7)}", dst=[q], src=[q, t.r(7)])
+        em.valu(f"v_cndmask_b32 {t.r(7)}, 0, {dv}, vcc", dst=[t.r(7)], src=[dv])
+        em.valu(f"v_add_u32 {rem}, {rem}, {t.r(7)}", dst=[rem], src=[rem, t.r(7)])
+        # rem >= den: q += 1, rem -= den
+        em.valu(f"v_cmp_le_u32 vcc, {dv}, {rem}", src=[rem, dv])
+        em.valu(f"v_cndmask_b32 {t.r(7)}, 0, 1, vcc", dst=[t.r(7)])
+        em.valu(f"v_add_u32 {q}, {q}, {t.r(7)}", dst=[q], src=[q, t.r(7)])
+        em.valu(f"v_cndmask_b32 {t.r(7)}, 0, {dv}, vcc", dst=[t.r(7)], src=[dv])
+        em.valu(f"v_sub_u32 {rem}, {rem}, {t.r(7)}", dst=[rem], src=[rem, t.r(7)])
+
+    def item_setup(self, l_exit):
+        """Decode this round's item; set the block's rows, key range and
+        buffer resources.  Jumps to l_exit when the workgroup has no item left."""
+        em, D = self.em, self.D
+        x, t = self.s_x, self.v_t
+        # idx = r*G + (r odd ? G-1-g : g)
+        em.salu(f"s_lshr_b32 {x[1]}, s25, 16")                     # G
+        em.salu(f"s_mul_i32 {x[0]}, {self.s_r}, {x[1]}")
+        em.salu(f"s_sub_u32 {x[2]}, {x[1]}, 1")
+        em.salu(f"s_sub_u32 {x[2]}, {x[2]}, {self.s_g}")            # G-1-g
+        em.salu(f"s_bitcmp1_b32 {self.s_r}, 0")
+        em.salu(f"s_cselect_b32 {x[2]}, {x[2]}, {self.s_g}")
+        em.salu(f"s_add_u32 {x[0]}, {x[0]}, {x[2]}")                # idx
+        em.salu(f"s_cmp_ge_u32 {x[0]}, {self.s_nitems}")
+        em.salu(f"s_cbranch_scc1 {l_exit}")
+        # level = idx / P, within = idx % P; b = within / Hq, slot = within % Hq
+        em.valu(f"v_mov_b32 {t.r(0)}, {x[0]}", dst=[t.r(0)])
+        self.emit_div(t.r(0), self.s_P, t.r(1), t.r(2))
+        self.emit_div(t.r(2), "s21", t.r(4), t.r(5))
+        em.valu(f"v_readfirstlane_b32 {x[3]}, {t.r(1)}", src=[t.r(1)])    # level
+        em.valu(f"v_readfirstlane_b32 {self.s_b}, {t.r(4)}", src=[t.r(4)])  # b
+        em.valu(f"v_readfirstlane_b32 {x[4]}, {t.r(5)}", src=[t.r(5)])    # head slot
+        # hq: spread contiguous head groups over the 8 XCDs (workgroup g -> XCD g % 8)
         em.salu("s_cmp_eq_u32 s27, 0")
-        em.salu(f"s_cbranch_scc1 {l_no}")
-        em.salu(f"s_and_b32 {self.s_hq}, s2, 7")
+        em.salu(f"s_cselect_b32 {x[5]}, 0, 7")
+        em.salu(f"s_and_b32 {self.s_hq}, {x[4]}, {x[5]}")
         em.salu(f"s_mul_i32 {self.s_hq}, {self.s_hq}, s27")
-        em.salu(f"s_lshr_b32 {x[0]}, s2, 3")
-        em.salu(f"s_add_u32 {self.s_hq}, {self.s_hq}, {x[0]}")
-        em.salu(f"s_branch {l_done}")
-        em.label(l_no)
-        em.salu(f"s_mov_b32 {self.s_hq}, s2")
-        em.label(l_done)
+        em.salu(f"s_cmp_eq_u32 s27, 0")
+        em.salu(f"s_cselect_b32 {x[5]}, 0, 3")
+        em.salu(f"s_lshr_b32 {x[5]}, {x[4]}, {x[5]}")
+        em.salu(f"s_add_u32 {self.s_hq}, {self.s_hq}, {x[5]}")
         # query tile: longest causal tiles first
-        em.salu(f"s_sub_u32 {x[0]}, s25, 1")
-        em.salu(f"s_sub_u32 {x[0]}, {x[0]}, s3")
+        em.salu(f"s_and_b32 {x[5]}, s25, 0xffff")
+        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, 1")
+        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, {x[3]}")
         em.salu("s_cmp_eq_u32 s23, 0")
-        em.salu(f"s_cselect_b32 {self.s_qt}, s3, {x[0]}")
-        em.salu(f"s_mov_b32 {self.s_b}, s4")
+        em.salu(f"s_cselect_b32 {self.s_qt}, {x[3]}, {x[5]}")
         # kv-head: hq / (Hq / Hkv) as (hq * magic) >> 20
         em.salu(f"s_mul_i32 {self.s_hk}, {self.s_hq}, s26")
         em.salu(f"s_lshr_b32 {self.s_hk}, {self.s_hk}, 20")
@@ -218,8 +291,7 @@ class Gen:
         em.salu(f"s_min_i32 {x[0]}, {x[0]}, s20")
         em.salu("s_cmp_eq_u32 s23, 0")
         em.salu(f"s_cselect_b32 {self.s_kvfull}, s20, {x[0]}")
-        # K/V row stride and batch/head bases (bytes)
-        em.salu(f"s_mul_i32 {self.s_rowb}, s22, {D * 2}")
+        # K/V batch/head bases (bytes)
         em.salu(f"s_mul_i32 {x[0]}, {self.s_b}, s20")              # b*Skv
         em.salu(f"s_mul_i32 {x[2]}, {x[0]}, {self.s_rowb}")
         em.salu(f"s_mul_hi_u32 {x[3]}, {x[0]}, {self.s_rowb}")
@@ -255,18 +327,77 @@ class Gen:
         em.salu(f"s_and_b32 {self.s_rl.r(1)}, {self.s_rl.r(1)}, 0xffff")
         em.salu(f"s_lshl_b32 {self.s_rl.r(2)}, s19, 2")
         em.salu(f"s_mov_b32 {self.s_rl.r(3)}, 0x20000")
-        em.salu("s_or_b32 s16, s16, s17")
-        em.salu("s_cmp_eq_u32 s16, 0")
+        em.salu(f"s_or_b32 {x[0]}, s16, s17")
+        em.salu(f"s_cmp_eq_u32 {x[0]}, 0")
         em.salu(f"s_cselect_b32 {self.s_rl.r(2)}, 0, {self.s_rl.r(2)}")
 
-    def lane_constants(self):
+    def lane_rows(self):
+        """Per-lane query rows: Q/O and LSE byte offsets, last visible key."""
         em, D = self.em, self.D
-        if self.debug_point == "start":
-            vals = ["v0"]
-            for i, sg in enumerate(["s32", "s19", "s21", "s14", "s15", "s44", "s45", "s46", "s47", "s2", "s3", "s4"]):
-                em.valu(f"v_mov_b32 v{100 + i}, {sg}", dst=[f"v{100 + i}"])
-                vals.append(f"v{100 + i}")
-            self.debug_dump("start", vals)
+        t = self.v_t
+        lane = "v0"
+        # l32 = lane & 31 -> t0 ; h = lane >> 5 -> t1
+        em.valu(f"v_and_b32 {t.r(0)}, 31, {lane}", dst=[t.r(0)], src=[lane])
+        em.valu(f"v_lshrrev_b32 {t.r(1)}, 5, {lane}", dst=[t.r(1)], src=[lane])
+        # rows of the two query blocks: q = qw0 + 32 qb + l32
+        em.valu(f"v_add_u32 {t.r(2)}, {self.s_qw0}, {t.r(0)}", dst=[t.r(2)], src=[t.r(0)])
+        em.valu(f"v_add_u32 {t.r(3)}, 32, {t.r(2)}", dst=[t.r(3)], src=[t.r(2)])
+        em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {D * 2}")   # Q/O row stride bytes
+        em.salu(f"s_sub_i32 {self.s_x[1]}, s20, 1")          # Skv - 1
+        for qb in range(2):
+            q = t.r(2 + qb)
+            # Q/O byte offset of row q (+ 16 bytes for lanes of the upper half: dims 8h..)
+            em.valu(f"v_mul_lo_u32 {self.v_qoff.r(qb)}, {q}, {self.s_x[0]}", dst=[self.v_qoff.r(qb)], src=[q])
+            em.valu(f"v_lshlrev_b32 {self.v_lseoff.r(qb)}, 2, {q}", dst=[self.v_lseoff.r(qb)], src=[q])
+            # last visible key: causal ? min(q + off, Skv-1) : Skv-1 ; then minus 4h
+            em.valu(f"v_add_u32 {t.r(4)}, {self.s_off}, {q}", dst=[t.r(4)], src=[q])
+            em.valu(f"v_min_i32 {t.r(4)}, {self.s_x[1]}, {t.r(4)}", dst=[t.r(4)], src=[t.r(4)])
+            em.valu(f"v_mov_b32 {t.r(5)}, {self.s_x[1]}", dst=[t.r(5)])
+            em.salu("s_cmp_eq_u32 s23, 0")
+            em.salu(f"s_cselect_b64 {self.s_m1}, -1, 0")
+            em.valu(f"v_cndmask_b32 {t.r(4)}, {t.r(4)}, {t.r(5)}, {self.s_m1}", dst=[t.r(4)], src=[t.r(4), t.r(5)])
+            em.valu(f"v_lshlrev_b32 {self.v_limh.r(qb)}, 2, {t.r(1)}", dst=[self.v_limh.r(qb)], src=[t.r(1)])
+            em.valu(f"v_sub_u32 {self.v_limh.r(qb)}, {t.r(4)}, {self.v_limh.r(qb)}",
+                    dst=[self.v_limh.r(qb)], src=[t.r(4), self.v_limh.r(qb)])
+
+    def lane_dma(self):
+        """Per-lane source offsets of the K/V DMA rows (with the LDS swizzles)."""
+        em, D = self.em, self.D
+        t = self.v_t
+        lane = "v0"
+        # l32 = lane & 31 -> t0 ; h = lane >> 5 -> t1
+        em.valu(f"v_and_b32 {t.r(0)}, 31, {lane}", dst=[t.r(0)], src=[lane])
+        em.valu(f"v_lshrrev_b32 {t.r(1)}, 5, {lane}", dst=[t.r(1)], src=[lane])
+        # DMA source offsets: row r = 16w + RPD*i + lane/CH, physical chunk p = lane % CH
+        CH = self.CH
+        em.valu(f"v_lshrrev_b32 {t.r(2)}, {int(math.log2(CH))}, {lane}", dst=[t.r(2)], src=[lane])
+        em.valu(f"v_and_b32 {t.r(3)}, {CH - 1}, {lane}", dst=[t.r(3)], src=[lane])
+        em.salu(f"s_lshl_b32 {self.s_x[0]}, {self.s_w}, 4")
+        em.valu(f"v_add_u32 {t.r(2)}, {self.s_x[0]}, {t.r(2)}", dst=[t.r(2)], src=[t.r(2)])  # r (i=0)
+        for i in range(self.DPW):
+            em.valu(f"v_add_u32 {t.r(4)}, {self.RPD * i}, {t.r(2)}", dst=[t.r(4)], src=[t.r(2)])
+            em.valu(f"v_mul_lo_u32 {t.r(5)}, {t.r(4)}, {self.s_rowb}", dst=[t.r(5)], src=[t.r(4)])
+            # K swizzle of row r
+            if D == 128:
+                em.valu(f"v_and_b32 {t.r(6)}, 15, {t.r(4)}", dst=[t.r(6)], src=[t.r(4)])
+            else:
+                em.valu(f"v_bfe_u32 {t.r(6)}, {t.r(4)}, 1, 3", dst=[t.r(6)], src=[t.r(4)])
+            em.valu(f"v_xor_b32 {t.r(6)}, {t.r(6)}, {t.r(3)}", dst=[t.r(6)], src=[t.r(6), t.r(3)])
+            em.valu(f"v_lshl_add_u32 {self.v_kdma.r(i)}, {t.r(6)}, 4, {t.r(5)}",
+                    dst=[self.v_kdma.r(i)], src=[t.r(6), t.r(5)])
+            # V swizzle of row r
+            if D == 128:
+                em.valu(f"v_and_b32 {t.r(6)}, 3, {t.r(4)}", dst=[t.r(6)], src=[t.r(4)])
+            else:
+                em.valu(f"v_bfe_u32 {t.r(6)}, {t.r(4)}, 1, 1", dst=[t.r(6)], src=[t.r(4)])
+            em.valu(f"v_lshlrev_b32 {t.r(6)}, 2, {t.r(6)}", dst=[t.r(6)], src=[t.r(6)])
+            em.valu(f"v_xor_b32 {t.r(6)}, {t.r(6)}, {t.r(3)}", dst=[t.r(6)], src=[t.r(6), t.r(3)])
+            em.valu(f"v_lshl_add_u32 {self.v_vdma.r(i)}, {t.r(6)}, 4, {t.r(5)}",
+                    dst=[self.v_vdma.r(i)], src=[t.r(6), t.r(5)])
+
+    def lane_kv(self):
+        """Per-lane LDS read offsets of the K and V operands."""
+        em, D = self.em, self.D
         t = self.v_t
         lane = "v0"
         # l32 = lane & 31 -> t0 ; h = lane >> 5 -> t1
@@ -306,159 +437,116 @@ class Gen:
             em.valu(f"v_xor_b32 {t.r(6)}, {t.r(6)}, {t.r(3)}", dst=[t.r(6)], src=[t.r(6), t.r(3)])
             em.valu(f"v_lshl_add_u32 {self.v_voff.r(db)}, {t.r(6)}, 4, {t.r(5)}",
                     dst=[self.v_voff.r(db)], src=[t.r(6), t.r(5)])
-        # DMA source offsets: row r = 16w + RPD*i + lane/CH, physical chunk p = lane % CH
-        CH = self.CH
-        em.valu(f"v_lshrrev_b32 {t.r(2)}, {int(math.log2(CH))}, {lane}", dst=[t.r(2)], src=[lane])
-        em.valu(f"v_and_b32 {t.r(3)}, {CH - 1}, {lane}", dst=[t.r(3)], src=[lane])
-        em.salu(f"s_lshl_b32 {self.s_x[0]}, {self.s_w}, 4")
-        em.valu(f"v_add_u32 {t.r(2)}, {self.s_x[0]}, {t.r(2)}", dst=[t.r(2)], src=[t.r(2)])  # r (i=0)
-        for i in range(self.DPW):
-            em.valu(f"v_add_u32 {t.r(4)}, {self.RPD * i}, {t.r(2)}", dst=[t.r(4)], src=[t.r(2)])
-            em.valu(f"v_mul_lo_u32 {t.r(5)}, {t.r(4)}, {self.s_rowb}", dst=[t.r(5)], src=[t.r(4)])
-            # K swizzle of row r
-            if D == 128:
-                em.valu(f"v_and_b32 {t.r(6)}, 15, {t.r(4)}", dst=[t.r(6)], src=[t.r(4)])
-            else:
-                em.valu(f"v_bfe_u32 {t.r(6)}, {t.r(4)}, 1, 3", dst=[t.r(6)], src=[t.r(4)])
-            em.valu(f"v_xor_b32 {t.r(6)}, {t.r(6)}, {t.r(3)}", dst=[t.r(6)], src=[t.r(6), t.r(3)])
-            em.valu(f"v_lshl_add_u32 {self.v_kdma.r(i)}, {t.r(6)}, 4, {t.r(5)}",
-                    dst=[self.v_kdma.r(i)], src=[t.r(6), t.r(5)])
-            # V swizzle of row r
-            if D == 128:
-                em.valu(f"v_and_b32 {t.r(6)}, 3, {t.r(4)}", dst=[t.r(6)], src=[t.r(4)])
-            else:
-                em.valu(f"v_bfe_u32 {t.r(6)}, {t.r(4)}, 1, 1", dst=[t.r(6)], src=[t.r(4)])
-            em.valu(f"v_lshlrev_b32 {t.r(6)}, 2, {t.r(6)}", dst=[t.r(6)], src=[t.r(6)])
-            em.valu(f"v_xor_b32 {t.r(6)}, {t.r(6)}, {t.r(3)}", dst=[t.r(6)], src=[t.r(6), t.r(3)])
-            em.valu(f"v_lshl_add_u32 {self.v_vdma.r(i)}, {t.r(6)}, 4, {t.r(5)}",
-                    dst=[self.v_vdma.r(i)], src=[t.r(6), t.r(5)])
-        # rows of the two query blocks: q = qw0 + 32 qb + l32
-        em.valu(f"v_add_u32 {t.r(2)}, {self.s_qw0}, {t.r(0)}", dst=[t.r(2)], src=[t.r(0)])
-        em.valu(f"v_add_u32 {t.r(3)}, 32, {t.r(2)}", dst=[t.r(3)], src=[t.r(2)])
-        em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {D * 2}")   # Q/O row stride bytes
-        em.salu(f"s_sub_i32 {self.s_x[1]}, s20, 1")          # Skv - 1
-        for qb in range(2):
-            q = t.r(2 + qb)
-            # Q/O byte offset of row q (+ 16 bytes for lanes of the upper half: dims 8h..)
-            em.valu(f"v_mul_lo_u32 {self.v_qoff.r(qb)}, {q}, {self.s_x[0]}", dst=[self.v_qoff.r(qb)], src=[q])
-            em.valu(f"v_lshlrev_b32 {self.v_lseoff.r(qb)}, 2, {q}", dst=[self.v_lseoff.r(qb)], src=[q])
-            # last visible key: causal ? min(q + off, Skv-1) : Skv-1 ; then minus 4h
-            em.valu(f"v_add_u32 {t.r(4)}, {self.s_off}, {q}", dst=[t.r(4)], src=[q])
-            em.valu(f"v_min_i32 {t.r(4)}, {self.s_x[1]}, {t.r(4)}", dst=[t.r(4)], src=[t.r(4)])
-            em.valu(f"v_mov_b32 {t.r(5)}, {self.s_x[1]}", dst=[t.r(5)])
-            em.salu("s_cmp_eq_u32 s23, 0")
-            em.salu(f"s_cselect_b64 {self.s_m1}, -1, 0")
-            em.valu(f"v_cndmask_b32 {t.r(4)}, {t.r(4)}, {t.r(5)}, {self.s_m1}", dst=[t.r(4)], src=[t.r(4), t.r(5)])
-            em.valu(f"v_lshlrev_b32 {self.v_limh.r(qb)}, 2, {t.r(1)}", dst=[self.v_limh.r(qb)], src=[t.r(1)])
-            em.valu(f"v_sub_u32 {self.v_limh.r(qb)}, {t.r(4)}, {self.v_limh.r(qb)}",
-                    dst=[self.v_limh.r(qb)], src=[t.r(4), self.v_limh.r(qb)])
-        # Q byte offsets also include 16 h (dims 8h .. 8h+7 of each 16-dim step)
-        em.valu(f"v_lshlrev_b32 {t.r(4)}, 4, {t.r(1)}", dst=[t.r(4)], src=[t.r(1)])
-        self.v_h16 = t.r(4)
 
     # ------------------------------------------------------------------------
     # Q load into AGPRs, state init
     # ------------------------------------------------------------------------
-    def load_q_and_init(self):
-        em0 = self.em
-        em0.valu(f"v_mov_b32 {self.v_t.r(7)}, {self.s_w}", dst=[self.v_t.r(7)])
-        em0.valu(f"v_mov_b32 {self.v_t.r(3)}, {self.s_qw0}", dst=[self.v_t.r(3)])
-        self.debug_dump("ids", ["v0", self.v_t.r(7), self.v_t.r(3), self.v_qoff.r(0), self.v_qoff.r(1), self.v_h16])
-        self._load_q_and_init()
-
-    def _load_q_and_init(self):
-        """Q into VGPRs (the S / P buffers are free here), then into AGPRs."""
+    def load_q(self):
+        """Issue the loads of the wave's 64 Q rows straight into the Q AGPRs
+        (lanes of the upper half take dims 8..15 of each 16-dim step)."""
         em, t = self.em, self.v_t
+        em.valu(f"v_lshrrev_b32 {t.r(4)}, 5, v0", dst=[t.r(4)], src=["v0"])
+        em.valu(f"v_lshlrev_b32 {t.r(4)}, 4, {t.r(4)}", dst=[t.r(4)], src=[t.r(4)])
         for qb in range(2):
-            em.valu(f"v_add_u32 {t.r(5 + qb)}, {self.v_qoff.r(qb)}, {self.v_h16}",
-                    dst=[t.r(5 + qb)], src=[self.v_qoff.r(qb), self.v_h16])
-        stage = [self.v_S[0][0], self.v_S[0][1], self.v_S[1][0], self.v_S[1][1]]
-        def qtmp(qb, s):
-            k = qb * self.NS + s           # 4-register slot k of 16
-            return stage[k // 4].r(4 * (k % 4), 4)
+            em.valu(f"v_add_u32 {t.r(5 + qb)}, {self.v_qoff.r(qb)}, {t.r(4)}",
+                    dst=[t.r(5 + qb)], src=[self.v_qoff.r(qb), t.r(4)])
         for qb in range(2):
             for s in range(self.NS):
-                em.vmem_load_to(f"buffer_load_dwordx4 {qtmp(qb, s)}, {t.r(5 + qb)}, {self.s_rq}, 0 offen offset:{32 * s}",
-                                qtmp(qb, s), src=[t.r(5 + qb)])
-        em.salu("s_waitcnt vmcnt(0)")
-        self.debug_dump("qv", [qtmp(qb, s).replace(":", ":").split(":")[0].replace("[", "") + "" for qb in range(2) for s in range(self.NS)])
-        for qb in range(2):
-            for s in range(self.NS):
-                src = qtmp(qb, s)
-                base = int(src[2:src.index(":")])
-                for i in range(4):
-                    em.valu(f"v_accvgpr_write_b32 {self.a_Q[qb][s].r(i)}, v{base + i}",
-                            dst=[self.a_Q[qb][s].r(i)], src=[f"v{base + i}"])
-        for qb in range(2):
-            for db in range(self.NDB):
-                blk = self.a_O[qb][db]
-                for i in range(16):
-                    em.valu(f"v_accvgpr_write_b32 {blk.r(i)}, 0", dst=[blk.r(i)])
+                dst = str(self.a_Q[qb][s])
+                em.vmem_load_to(f"buffer_load_dwordx4 {dst}, {t.r(5 + qb)}, {self.s_rq}, 0 offen offset:{32 * s}",
+                                dst, src=[t.r(5 + qb)])
+
+    def init_state(self):
+        """Constants, m = -inf, l = 0, and O = 0 (by MFMAs of zero operands,
+        eight instructions instead of 128 AGPR writes)."""
+        em = self.em
         em.valu(f"v_mov_b32 {self.v_ninf}, {self.s_neg}", dst=[str(self.v_ninf)])
-        em.valu(f"v_mov_b32 {self.v_resc}, {f32_hex(RESCALE)}", dst=[str(self.v_resc)])
+        em.valu(f"v_mov_b32 {self.v_thr}, {f32_hex(THRESH)}", dst=[str(self.v_thr)])
         em.valu(f"v_mov_b32 {self.v_c}, s24", dst=[str(self.v_c)])
         for qb in range(2):
             em.valu(f"v_mov_b32 {self.v_m.r(qb)}, {self.s_neg}", dst=[self.v_m.r(qb)])
             em.valu(f"v_mov_b32 {self.v_l.r(qb)}, 0", dst=[self.v_l.r(qb)])
             em.valu(f"v_mov_b32 {self.v_mc.r(qb)}, 0", dst=[self.v_mc.r(qb)])
+        z = self.v_KO[0]
+        for i in range(4):
+            em.valu(f"v_mov_b32 {z.r(i)}, 0", dst=[z.r(i)])
+        for qb in range(2):
+            for db in range(self.NDB):
+                em.mfma(self.mfma_op, str(self.a_O[qb][db]), str(z), str(z), "0")
 
     # ------------------------------------------------------------------------
-    # DMA of K(t) and V(t): tile index in sgpr `st`, LDS slot bases in sgprs
+    # K/V DMA: wave w copies rows 16w .. 16w+15 of a 64-key tile into its LDS
+    # slot, RPD rows per buffer_load ... lds (16 bytes per lane).  Loads past
+    # the last visible key return zeros.
     # ------------------------------------------------------------------------
-    def dma_tile(self, st, kslot_sgpr, vslot_sgpr):
-        em, x = self.em, self.s_x
-        # bytes left from the tile's first row to row_lim (0 when past it)
-        em.salu(f"s_lshl_b32 {x[0]}, {st}, 6")                      # key0
-        em.salu(f"s_sub_i32 {x[1]}, {self.s_rowlim}, {x[0]}")
-        em.salu(f"s_max_i32 {x[1]}, {x[1]}, 0")
-        em.salu(f"s_mul_i32 {x[2]}, {x[1]}, {self.s_rowb}")
-        em.salu(f"s_mul_hi_u32 {x[3]}, {x[1]}, {self.s_rowb}")
-        em.salu(f"s_cmp_eq_u32 {x[3]}, 0")
-        em.salu(f"s_cselect_b32 {x[2]}, {x[2]}, 0x7fffffff")
-        em.salu(f"s_min_u32 {x[2]}, {x[2]}, 0x7fffffff")
-        # base = batch base + key0 * rowb
-        em.salu(f"s_mul_i32 {x[4]}, {x[0]}, {self.s_rowb}")
-        em.salu(f"s_mul_hi_u32 {x[5]}, {x[0]}, {self.s_rowb}")
+    def _salu_op(self, *lines):
+        em = self.em
+
+        def f():
+            for l in lines:
+                em.salu(l)
+        return Op(f, 0.25 * len(lines))
+
+    def ops_dma_desc(self, tile):
+        """Buffer resources s_rk / s_rv of the tile whose index is in sgpr
+        `tile`: base = batch/head base + key0 * rowb, size = the bytes up to
+        row_lim (0 past it).  SCC producer/consumer pairs stay in one op."""
+        y, rb, sa = self.s_y, self.s_rowb, self._salu_op
+        ops = [
+            sa(f"s_lshl_b32 {y[0]}, {tile}, 6"),                       # key0
+            sa(f"s_sub_i32 {y[1]}, {self.s_rowlim}, {y[0]}"),
+            sa(f"s_max_i32 {y[1]}, {y[1]}, 0"),
+            sa(f"s_mul_i32 {y[2]}, {y[1]}, {rb}"),
+            sa(f"s_mul_hi_u32 {y[3]}, {y[1]}, {rb}"),
+            sa(f"s_cmp_eq_u32 {y[3]}, 0", f"s_cselect_b32 {y[2]}, {y[2]}, 0x7fffffff"),
+            sa(f"s_min_u32 {y[2]}, {y[2]}, 0x7fffffff"),
+            sa(f"s_mul_i32 {y[3]}, {y[0]}, {rb}"),
+            sa(f"s_mul_hi_u32 {y[4]}, {y[0]}, {rb}"),
+        ]
         for rs, bb in ((self.s_rk, self.s_kb), (self.s_rv, self.s_vb)):
-            em.salu(f"s_add_u32 {rs.r(0)}, {bb.r(0)}, {x[4]}")
-            em.salu(f"s_addc_u32 {rs.r(1)}, {bb.r(1)}, {x[5]}")
-            em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
-            em.salu(f"s_mov_b32 {rs.r(2)}, {x[2]}")
-            em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
-        # wave w fills rows 16w .. 16w+15: M0 = slot + (16w + RPD*i)*ROW
-        em.salu(f"s_mul_i32 {x[0]}, {self.s_w}, {16 * self.ROW}")
+            ops += [
+                sa(f"s_add_u32 {rs.r(0)}, {bb.r(0)}, {y[3]}", f"s_addc_u32 {rs.r(1)}, {bb.r(1)}, {y[4]}"),
+                sa(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff"),
+                sa(f"s_mov_b32 {rs.r(2)}, {y[2]}"),
+                sa(f"s_mov_b32 {rs.r(3)}, 0x20000"),
+            ]
+        return ops
+
+    def ops_dma_issue(self, which):
+        """The wave's DPW loads of the K (or V) rows of the tile described by
+        s_rk (s_rv) into the slot whose wave-adjusted address is s_kdw (s_vdw).
+        M0 is set by the same op that issues the load."""
+        em = self.em
+        desc, slot, voff = ((self.s_rk, self.s_kdw, self.v_kdma) if which == "k"
+                            else (self.s_rv, self.s_vdw, self.v_vdma))
+        ops = []
         for i in range(self.DPW):
-            em.salu(f"s_add_u32 {x[1]}, {kslot_sgpr}, {x[0]}")
-            if i:
-                em.salu(f"s_add_u32 {x[1]}, {x[1]}, {self.RPD * i * self.ROW}")
-            em.salu(f"s_mov_b32 m0, {x[1]}")
-            em.vmem(f"buffer_load_dwordx4 {self.v_kdma.r(i)}, {self.s_rk}, 0 offen lds", src=[self.v_kdma.r(i)])
-        for i in range(self.DPW):
-            em.salu(f"s_add_u32 {x[1]}, {vslot_sgpr}, {x[0]}")
-            if i:
-                em.salu(f"s_add_u32 {x[1]}, {x[1]}, {self.RPD * i * self.ROW}")
-            em.salu(f"s_mov_b32 m0, {x[1]}")
-            em.vmem(f"buffer_load_dwordx4 {self.v_vdma.r(i)}, {self.s_rv}, 0 offen lds", src=[self.v_vdma.r(i)])
+            def f(i=i):
+                em.salu(f"s_add_u32 m0, {slot}, {self.RPD * i * self.ROW}")
+                em.vmem(f"buffer_load_dwordx4 {voff.r(i)}, {desc}, 0 offen lds", src=[voff.r(i)])
+            ops.append(Op(f, 0.75))
+        return ops
 
     def wait_vm(self, n):
         self.em.salu(f"s_waitcnt vmcnt({n})")
 
     # ------------------------------------------------------------------------
-    # building blocks; each returns a list of callables emitting one instruction
+    # building blocks: lists of Op (one instruction, or an indivisible group)
     # ------------------------------------------------------------------------
-    def ops_k_loads(self, kb):
-        """K operands of one sub-tile (kb of the tile in the K read slot)."""
+    def ops_addr(self, dst, off, n, sgpr):
         em = self.em
-        out = []
-        for s in range(self.NS):
-            def f(s=s):
-                em.ds_read(f"ds_read_b128 {self.v_KO[s]}, {self.v_kaddr.r(s)} offset:{kb * 32 * self.ROW}",
-                           str(self.v_KO[s]), self.v_kaddr.r(s))
-            out.append(f)
-        return out
+        return [Op(lambda i=i: em.valu(f"v_add_u32 {dst.r(i)}, {sgpr}, {off.r(i)}",
+                                       dst=[dst.r(i)], src=[off.r(i)]), 1.0) for i in range(n)]
 
-    def ops_v_loads(self, kb):
-        """V operands of one sub-tile (kb of the tile addressed by v_vaddr)."""
+    def ops_k_loads(self, kb):
+        """K operands of sub-tile kb of the tile addressed by v_kaddr."""
+        em = self.em
+        return [Op(lambda s=s: em.ds_read(
+            f"ds_read_b128 {self.v_KO[s]}, {self.v_kaddr.r(s)} offset:{kb * 32 * self.ROW}",
+            str(self.v_KO[s]), self.v_kaddr.r(s)), 0.5) for s in range(self.NS)]
+
+    def ops_v_loads(self, kb, vb):
+        """V operands of sub-tile kb of the tile addressed by v_vaddr, into VO[vb]."""
         em = self.em
         out = []
         for th in range(2):
@@ -466,26 +554,27 @@ class Gen:
                 for e in range(2):
                     def f(th=th, db=db, e=e):
                         off = (32 * kb + 16 * th + 8 * e) * self.ROW
-                        dst = self.v_VO[th][db].r(2 * e, 2)
+                        dst = self.v_VO[vb][th][db].r(2 * e, 2)
                         em.ds_read(f"ds_read_b64_tr_b16 {dst}, {self.v_vaddr.r(db)} offset:{off}",
                                    dst, self.v_vaddr.r(db))
-                    out.append(f)
+                    out.append(Op(f, 0.5))
         return out
 
-    def ops_qk(self, buf):
-        """S^T(sub-tile) = K . Q^T into S[buf]; 2*NS MFMAs."""
+    def mf_qk(self, buf):
+        """S^T = K . Q^T into S[buf], query block 0 first (its result is final
+        half-way through)."""
         em = self.em
         out = []
-        for s in range(self.NS):
-            for qb in range(2):
+        for qb in range(2):
+            for s in range(self.NS):
                 def f(s=s, qb=qb):
-                    d = self.S_(buf, qb)
+                    d = str(self.v_S[buf][qb])
                     em.mfma(self.mfma_op, d, str(self.v_KO[s]), str(self.a_Q[qb][s]), "0" if s == 0 else d)
                 out.append(f)
         return out
 
-    def ops_pv(self, pbuf):
-        """O^T += V^T . P^T with P[pbuf]; 4*NDB MFMAs."""
+    def mf_pv(self, pbuf, vbuf):
+        """O^T += V^T . P^T with P[pbuf] and the V operands VO[vbuf]."""
         em = self.em
         out = []
         for th in range(2):
@@ -493,103 +582,112 @@ class Gen:
                 for qb in range(2):
                     def f(th=th, db=db, qb=qb):
                         o = str(self.a_O[qb][db])
-                        em.mfma(self.mfma_op, o, str(self.v_VO[th][db]), str(self.v_P[pbuf][qb][th]), o)
+                        em.mfma(self.mfma_op, o, str(self.v_VO[vbuf][th][db]), str(self.v_P[pbuf][qb][th]), o)
                     out.append(f)
         return out
 
-    def ops_max(self, buf):
-        """Row max of S[buf] per query block into v_mx (both lane halves)."""
+    def ops_softmax(self, sb, pn):
+        """Softmax numerators of S[sb] against the reference max:
+        E = 2^(c*S - mc) (fp32), rs = per-half row sums, P[pn] = E rounded
+        to the input dtype.  Returns (exponentials, sums, conversions)."""
+        em = self.em
+        ops_e, ops_s, ops_c = [], [], []
+        for qb in range(2):
+            S, E, mc = self.v_S[sb][qb], self.v_E[qb], self.v_mc.r(qb)
+            for c4 in range(4):
+                for i in range(4 * c4, 4 * c4 + 4):
+                    ops_e.append(Op(lambda S=S, E=E, mc=mc, i=i: em.valu(
+                        f"v_fma_f32 {E.r(i)}, {S.r(i)}, s24, -{mc}", dst=[E.r(i)], src=[S.r(i), mc]), 1.0))
+                for i in range(4 * c4, 4 * c4 + 4):
+                    ops_e.append(Op(lambda E=E, i=i: em.valu(
+                        f"v_exp_f32 {E.r(i)}, {E.r(i)}", dst=[E.r(i)], src=[E.r(i)], trans=True), 1.5))
+            ra, rb = self.v_rs.r(qb), self.v_rb.r(qb)
+            ops_s.append(Op(lambda E=E, ra=ra: em.valu(f"v_add_f32 {ra}, {E.r(0)}, {E.r(1)}", dst=[ra], src=[E.r(0), E.r(1)]), 1.0))
+            ops_s.append(Op(lambda E=E, rb=rb: em.valu(f"v_add_f32 {rb}, {E.r(2)}, {E.r(3)}", dst=[rb], src=[E.r(2), E.r(3)]), 1.0))
+            for i in range(4, 16):
+                acc = ra if i % 2 == 0 else rb
+                ops_s.append(Op(lambda E=E, acc=acc, i=i: em.valu(
+                    f"v_add_f32 {acc}, {acc}, {E.r(i)}", dst=[acc], src=[acc, E.r(i)]), 1.0))
+            ops_s.append(Op(lambda ra=ra, rb=rb: em.valu(f"v_add_f32 {ra}, {ra}, {rb}", dst=[ra], src=[ra, rb]), 1.0))
+            for th in range(2):
+                P = self.v_P[pn][qb][th]
+                for jj in range(4):
+                    lo, hi = E.r(8 * th + 2 * jj), E.r(8 * th + 2 * jj + 1)
+                    ops_c.append(Op(lambda P=P, jj=jj, lo=lo, hi=hi: em.valu(
+                        f"{self.cvt_op} {P.r(jj)}, {lo}, {hi}", dst=[P.r(jj)], src=[lo, hi]), 1.0))
+        return ops_e, ops_s, ops_c
+
+    def ops_test(self):
+        """s_m1 / s_m2: lanes whose half-row sum passed the trigger (some p of
+        the sub-tile is above it, so the reference max must move)."""
+        em = self.em
+        return [Op(lambda qb=qb, msk=msk: em.valu(
+            f"v_cmp_gt_f32 {msk}, {self.v_rs.r(qb)}, {self.v_thr}", src=[self.v_rs.r(qb), str(self.v_thr)]), 1.0)
+            for qb, msk in ((0, self.s_m1), (1, self.s_m2))]
+
+    def ops_mask(self, sb):
+        """Set S[sb] entries of keys past each row's last visible key to -inf.
+        Key of register i = k0 + 8*(i>>2) + 4h + (i&3); limh = lim - 4h."""
         em = self.em
         out = []
         for qb in range(2):
-            S = self.v_S[buf][qb]
-            mx = self.v_mx.r(qb)
-            out.append(lambda S=S, mx=mx: em.valu(f"v_max3_f32 {mx}, {S.r(0)}, {S.r(1)}, {S.r(2)}",
-                                                  dst=[mx], src=[S.r(0), S.r(1), S.r(2)]))
-            for i in range(3, 15, 2):
-                out.append(lambda S=S, mx=mx, i=i: em.valu(
-                    f"v_max3_f32 {mx}, {mx}, {S.r(i)}, {S.r(i + 1)}", dst=[mx], src=[mx, S.r(i), S.r(i + 1)]))
-            out.append(lambda S=S, mx=mx: em.valu(f"v_max_f32 {mx}, {mx}, {S.r(15)}", dst=[mx], src=[mx, S.r(15)]))
-            tmp = self.v_t.r(6 + qb)
-            out.append(lambda mx=mx, tmp=tmp: em.valu(f"v_mov_b32 {tmp}, {mx}", dst=[tmp], src=[mx]))
-            out.append(lambda mx=mx, tmp=tmp: em.valu(f"v_permlane32_swap_b32 {mx}, {tmp}", dst=[mx, tmp], src=[mx, tmp]))
-            out.append(lambda mx=mx, tmp=tmp: em.valu(f"v_max_f32 {mx}, {mx}, {tmp}", dst=[mx], src=[mx, tmp]))
+            S = self.v_S[sb][qb]
+            d = self.v_d.r(qb)
+            out.append(lambda d=d, qb=qb: em.valu(f"v_subrev_u32 {d}, {self.s_k0}, {self.v_limh.r(qb)}",
+                                                  dst=[d], src=[self.v_limh.r(qb)]))
+            for i in range(16):
+                ci = 8 * (i >> 2) + (i & 3)
+                out.append(lambda d=d, ci=ci: em.valu(f"v_cmp_lt_i32 vcc, {d}, {ci}", src=[d]))
+                out.append(lambda S=S, i=i: em.valu(f"v_cndmask_b32 {S.r(i)}, {S.r(i)}, {self.v_ninf}, vcc",
+                                                    dst=[S.r(i)], src=[S.r(i), str(self.v_ninf)]))
         return out
 
-    def ops_raise_test(self):
-        """raise[qb] = c*mx > c*m + RESCALE, into s_m1 (qb 0) and s_m2 (qb 1)."""
-        em, t = self.em, self.v_t
-        out = []
-        for qb, msk in ((0, self.s_m1), (1, self.s_m2)):
-            a, b = t.r(2 + 2 * qb), t.r(3 + 2 * qb)
-            out.append(lambda qb=qb, a=a: em.valu(f"v_mul_f32 {a}, s24, {self.v_mx.r(qb)}", dst=[a], src=[self.v_mx.r(qb)]))
-            out.append(lambda qb=qb, b=b: em.valu(f"v_fma_f32 {b}, {self.v_m.r(qb)}, {self.v_c}, {self.v_resc}",
-                                                  dst=[b], src=[self.v_m.r(qb), str(self.v_c), str(self.v_resc)]))
-            out.append(lambda a=a, b=b, msk=msk: em.valu(f"v_cmp_gt_f32 {msk}, {a}, {b}", src=[a, b]))
-        return out
-
-    def ops_exp(self, buf, qb, pbuf):
-        """P[pbuf][qb] = round(2^(c*S - mc)); rs[qb] = sum; S[buf][qb] holds p (fp32)."""
+    def ops_rowmax(self, sb, qb):
+        """Row max of S[sb][qb] over both lane halves into v_mx[qb]."""
         em = self.em
-        S = self.v_S[buf][qb]
-        mc = self.v_mc.r(qb)
-        rs = self.v_rs.r(qb)
-        out = []
-        for i in range(16):
-            out.append(lambda i=i: em.valu(f"v_fma_f32 {S.r(i)}, {S.r(i)}, s24, -{mc}", dst=[S.r(i)], src=[S.r(i), mc]))
-            out.append(lambda i=i: em.valu(f"v_exp_f32 {S.r(i)}, {S.r(i)}", dst=[S.r(i)], src=[S.r(i)], trans=True))
-        out.append(lambda: em.valu(f"v_add_f32 {rs}, {S.r(0)}, {S.r(1)}", dst=[rs], src=[S.r(0), S.r(1)]))
-        for i in range(2, 16):
-            out.append(lambda i=i: em.valu(f"v_add_f32 {rs}, {rs}, {S.r(i)}", dst=[rs], src=[rs, S.r(i)]))
-        out.append(lambda: em.valu(f"v_add_f32 {self.v_l.r(qb)}, {self.v_l.r(qb)}, {rs}",
-                                   dst=[self.v_l.r(qb)], src=[self.v_l.r(qb), rs]))
-        for th in range(2):
-            P = self.v_P[pbuf][qb][th]
-            for jj in range(4):
-                lo, hi = S.r(8 * th + 2 * jj), S.r(8 * th + 2 * jj + 1)
-                out.append(lambda P=P, jj=jj, lo=lo, hi=hi: em.valu(
-                    f"{self.cvt_op} {P.r(jj)}, {lo}, {hi}", dst=[P.r(jj)], src=[lo, hi]))
-        return out
-
-    def ops_mask(self, buf, qb):
-        """Set S[buf][qb] entries with key > last visible key to -inf.
-        key of register i = k0 + 8*(i>>2) + 4h + (i&3); limh = lim - 4h."""
-        em = self.em
-        S = self.v_S[buf][qb]
-        d = self.v_d.r(qb)
-        out = [lambda: em.valu(f"v_subrev_u32 {d}, {self.s_k0}, {self.v_limh.r(qb)}", dst=[d], src=[self.v_limh.r(qb)])]
-        for i in range(16):
-            ci = 8 * (i >> 2) + (i & 3)
-            out.append(lambda i=i, ci=ci: em.valu(f"v_cmp_lt_i32 vcc, {d}, {ci}", src=[d]))
-            out.append(lambda i=i: em.valu(f"v_cndmask_b32 {S.r(i)}, {S.r(i)}, {self.v_ninf}, vcc",
-                                           dst=[S.r(i)], src=[S.r(i), str(self.v_ninf)]))
+        S, mx, tmp = self.v_S[sb][qb], self.v_mx.r(qb), self.v_t.r(6 + qb)
+        out = [lambda: em.valu(f"v_max3_f32 {mx}, {S.r(0)}, {S.r(1)}, {S.r(2)}", dst=[mx], src=[S.r(0), S.r(1), S.r(2)])]
+        for i in range(3, 15, 2):
+            out.append(lambda i=i: em.valu(f"v_max3_f32 {mx}, {mx}, {S.r(i)}, {S.r(i + 1)}",
+                                           dst=[mx], src=[mx, S.r(i), S.r(i + 1)]))
+        out.append(lambda: em.valu(f"v_max_f32 {mx}, {mx}, {S.r(15)}", dst=[mx], src=[mx, S.r(15)]))
+        out.append(lambda: em.valu(f"v_mov_b32 {tmp}, {mx}", dst=[tmp], src=[mx]))
+        out.append(lambda: em.valu(f"v_permlane32_swap_b32 {mx}, {tmp}", dst=[mx, tmp], src=[mx, tmp]))
+        out.append(lambda: em.valu(f"v_max_f32 {mx}, {mx}, {tmp}", dst=[mx], src=[mx, tmp]))
         return out
 
     def emit_all(self, ops):
         for f in ops:
             f()
 
-    # ------------------------------------------------------------------------
-    def rescale(self):
-        """Slow path body: move the reference max of raising rows, rescale O
-        and l by alpha = 2^(c*m_old - c*m_new).  Masks in s_m1 / s_m2."""
+    def emit_set_mc(self, qb):
+        """mc = c*m, or 0 while m = -inf (so masked logits stay -inf)."""
+        em = self.em
+        m, mc = self.v_m.r(qb), self.v_mc.r(qb)
+        em.valu(f"v_mul_f32 {mc}, s24, {m}", dst=[mc], src=[m])
+        em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {m}", src=[m])
+        em.valu(f"v_cndmask_b32 {mc}, {mc}, 0, vcc", dst=[mc], src=[mc])
+
+    def emit_rescale(self, sb, pn):
+        """Slow path: move the reference max of every row to max(m, rowmax of
+        S[sb]), rescale O and l by alpha = 2^(c*m_old - c*m_new), then redo the
+        softmax numerators of S[sb] and add their sums to l."""
         em, t = self.em, self.v_t
         em.drain()
-        for qb, msk in ((0, self.s_m1), (1, self.s_m2)):
-            m, mx = self.v_m.r(qb), self.v_mx.r(qb)
-            a = t.r(2)
-            em.valu(f"v_mul_f32 {t.r(3)}, s24, {m}", dst=[t.r(3)], src=[m])
-            em.valu(f"v_mul_f32 {t.r(4)}, s24, {mx}", dst=[t.r(4)], src=[mx])
-            em.valu(f"v_sub_f32 {a}, {t.r(3)}, {t.r(4)}", dst=[a], src=[t.r(3), t.r(4)])
+        for qb in range(2):
+            self.emit_all(self.ops_rowmax(sb, qb))
+            m, mx, l = self.v_m.r(qb), self.v_mx.r(qb), self.v_l.r(qb)
+            mn, a, b = t.r(0), t.r(1), t.r(2)
+            em.valu(f"v_max_f32 {mn}, {m}, {mx}", dst=[mn], src=[m, mx])
+            em.valu(f"v_mul_f32 {a}, s24, {m}", dst=[a], src=[m])
+            em.valu(f"v_mul_f32 {b}, s24, {mn}", dst=[b], src=[mn])
+            em.valu(f"v_sub_f32 {a}, {a}, {b}", dst=[a], src=[a, b])
             em.valu(f"v_exp_f32 {a}, {a}", dst=[a], src=[a], trans=True)
-            em.valu(f"v_cndmask_b32 {a}, 1.0, {a}, {msk}", dst=[a], src=[a])
-            em.valu(f"v_cndmask_b32 {m}, {m}, {mx}, {msk}", dst=[m], src=[m, mx])
-            em.valu(f"v_mul_f32 {self.v_l.r(qb)}, {self.v_l.r(qb)}, {a}", dst=[self.v_l.r(qb)], src=[self.v_l.r(qb), a])
-            # mc = c*m, or 0 while m = -inf
-            em.valu(f"v_mul_f32 {self.v_mc.r(qb)}, s24, {m}", dst=[self.v_mc.r(qb)], src=[m])
-            em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {m}", src=[m])
-            em.valu(f"v_cndmask_b32 {self.v_mc.r(qb)}, {self.v_mc.r(qb)}, 0, vcc",
-                    dst=[self.v_mc.r(qb)], src=[self.v_mc.r(qb)])
+            em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {mn}", src=[mn])
+            em.valu(f"v_cndmask_b32 {a}, {a}, 1.0, vcc", dst=[a], src=[a])   # alpha = 1 while all -inf
+            em.valu(f"v_mov_b32 {m}, {mn}", dst=[m], src=[mn])
+            self.emit_set_mc(qb)
+            em.valu(f"v_mul_f32 {l}, {l}, {a}", dst=[l], src=[l, a])
             for db in range(self.NDB):
                 blk = self.a_O[qb][db]
                 for i in range(16):
@@ -597,115 +695,108 @@ class Gen:
                     em.valu(f"v_accvgpr_read_b32 {tmp}, {blk.r(i)}", dst=[tmp], src=[blk.r(i)])
                     em.valu(f"v_mul_f32 {tmp}, {tmp}, {a}", dst=[tmp], src=[tmp, a])
                     em.valu(f"v_accvgpr_write_b32 {blk.r(i)}, {tmp}", dst=[blk.r(i)], src=[tmp])
+        e, s_, c = self.ops_softmax(sb, pn)
+        self.emit_all(e + s_ + c)
+        self.emit_l_update()
         em.drain()
 
-    # ------------------------------------------------------------------------
-    # one pipelined step j:
-    #   half A: P.V(j) [P buffer pb, V operands in VO] next to the row max of
-    #           sub-tile j+1 [S buffer sb], the lazy-rescale test, the
-    #           exponentials of j+1 for query block 0 and the K operand loads
-    #           for S^T(j+2) (sub-tile kb_k of the tile in the K read slot);
-    #   half B: S^T(j+2) into S[1-sb] next to the exponentials of j+1 for
-    #           query block 1 and the V operand loads for P.V(j+1) (sub-tile
-    #           kb_v of the tile addressed by v_vaddr).
-    # The slow path (some row's max rose by more than 2^8) is recorded and
-    # emitted out of line by emit_slow().
-    # ------------------------------------------------------------------------
-    def step(self, sb, pb, kb_k, kb_v, do_soft=True, do_qk=True, do_vload=True):
+    def emit_l_update(self):
         em = self.em
-        pv = self.ops_pv(pb)
-        slow = None
-        if do_soft:
-            # mask sub-tile j+1 (keys s_k0 .. s_k0+31) when it crosses the
-            # wave's diagonal or the key tail
-            l_skip = self.lab("nomask")
-            em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_k0}, 32")
-            em.salu(f"s_cmp_gt_i32 {self.s_x[0]}, {self.s_kvfull}")
-            em.salu(f"s_cbranch_scc0 {l_skip}")
-            snap = em.snapshot()
-            for qb in range(2):
-                self.emit_all(self.ops_mask(sb, qb))
-            em.label(l_skip)
-            # the masked path only resolved hazards the skip path still has
-            em.restore(snap)
-            lead = 4
-            interleave(em, pv[:lead], self.ops_max(sb) + self.ops_raise_test())
-            em.salu(f"s_or_b64 {self.s_or}, {self.s_m1}, {self.s_m2}")
-            l_slow, l_back = self.lab("slow"), self.lab("back")
-            em.salu(f"s_cbranch_scc1 {l_slow}")
-            snap = em.snapshot()
-            kl = self.ops_k_loads(kb_k) if do_qk else []
-            interleave(em, pv[lead:], kl + self.ops_exp(sb, 0, 1 - pb))
-            slow = (l_slow, l_back, snap, sb, pb, kb_k, do_qk, lead)
-            # slow path rejoins here fully drained, which is safe for what follows
-            em.label(l_back)
-        else:
-            kl = self.ops_k_loads(kb_k) if do_qk else []
-            interleave(em, pv, kl)
-        others = []
-        if do_soft:
-            others += self.ops_exp(sb, 1, 1 - pb)
-        if do_vload:
-            others += self.ops_v_loads(kb_v)
-        if do_qk:
-            interleave(em, self.ops_qk(1 - sb), others)
-        else:
-            self.emit_all(others)
-        return slow
-
-    def emit_slow(self, slow):
-        """Out-of-line slow path: finish P.V(j), rescale O and l, then the
-        exponentials of query block 0 and the K loads, and jump back."""
-        em = self.em
-        l_slow, l_back, snap, sb, pb, kb_k, do_qk, lead = slow
-        em.restore(snap)
-        em.label(l_slow)
-        self.emit_all(self.ops_pv(pb)[lead:])
-        self.rescale()
-        self.emit_all(self.ops_exp(sb, 0, 1 - pb))
-        if do_qk:
-            self.emit_all(self.ops_k_loads(kb_k))
-        em.drain()
-        em.salu(f"s_branch {l_back}")
+        for qb in range(2):
+            l, rs = self.v_l.r(qb), self.v_rs.r(qb)
+            em.valu(f"v_add_f32 {l}, {l}, {rs}", dst=[l], src=[l, rs])
 
     # ------------------------------------------------------------------------
-    debug_point = None   # debugging aid: name of a point where registers are dumped
+    # One pipeline step j (j_par = j % 2):
+    #   MFMA: P.V(j) [P[j%2], VO[j%2]] and, for kind "full", S^T(j+2) into
+    #         S[j%2] (K operands loaded in this step);
+    #   other units: the softmax numerators of sub-tile j+1 [S[(j+1)%2] ->
+    #         P[(j+1)%2]], the V operands of sub-tile j+1 [-> VO[(j+1)%2]] and
+    #         the caller's extra ops (addresses, DMA).
+    # The sub-tile is masked first when it holds keys past some row's last
+    # visible key (an out-of-line copy of the step); when a half-row sum
+    # passes the trigger an out-of-line slow path moves the reference max.
+    # ------------------------------------------------------------------------
+    def step(self, jp, kind, kb_k=0, kb_v=0, pre=(), extra=()):
+        em = self.em
+        sb = pn = vn = 1 - jp
 
-    def debug_dump(self, point, regs):
-        """At `point` (when it is the selected one), store `regs` (VGPR/AGPR
-        names) raw to the O buffer at ((w*64 + lane) * len(regs) + r) * 4 and
-        end the program."""
-        if self.debug_point != point:
+        def build():
+            mf = self.mf_pv(jp, jp)
+            if kind == "pvonly":
+                return mf, list(pre) + list(extra)
+            others = list(pre)
+            if kind == "full":
+                mf += self.mf_qk(jp)
+                others += self.ops_k_loads(kb_k)
+            e, s_, c = self.ops_softmax(sb, pn)
+            vl = self.ops_v_loads(kb_v, vn)
+            ex = list(extra)
+            # exponentials first; V operand loads and extras spread through
+            # the middle; sums, conversions and the trigger test last
+            half = len(e) // 2
+            others += e[:half] + vl[:len(vl) // 2] + ex[:len(ex) // 2] + e[half:] \
+                + vl[len(vl) // 2:] + ex[len(ex) // 2:] + s_ + self.ops_test() + c
+            return mf, others
+
+        if kind == "pvonly":
+            mf, others = build()
+            weave(em, mf, others)
             return
-        em, t = self.em, self.v_t
-        em.drain()
-        n = len(regs)
-        em.salu(f"s_lshl_b32 {self.s_x[0]}, {self.s_w}, 6")
-        em.valu(f"v_add_u32 {t.r(0)}, {self.s_x[0]}, v0", dst=[t.r(0)], src=["v0"])
-        em.valu(f"v_mul_u32_u24 {t.r(0)}, {4 * n}, {t.r(0)}", dst=[t.r(0)], src=[t.r(0)])
-        for i, r in enumerate(regs):
-            src = r
-            if r.startswith("a"):
-                em.valu(f"v_accvgpr_read_b32 {t.r(1)}, {r}", dst=[t.r(1)], src=[r])
-                src = t.r(1)
-            em.vmem(f"buffer_store_dword {src}, {t.r(0)}, {self.s_ro}, 0 offen offset:{4 * i}",
-                    src=[src, t.r(0)])
-        em.salu("s_waitcnt vmcnt(0)")
-        em.salu("s_endpgm")
+        # masked copy out of line when sub-tile j+1 reaches past kv_full
+        l_mask, l_join = self.lab("mask"), self.lab("join")
+        em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_k0}, 32")
+        em.salu(f"s_cmp_gt_i32 {self.s_x[0]}, {self.s_kvfull}")
+        em.salu(f"s_cbranch_scc1 {l_mask}")
+        snap = em.snapshot()
+        mf, others = build()
+        weave(em, mf, others)
+        em.label(l_join)
+        self.deferred.append(("mask", snap, l_mask, l_join, sb, build))
+        # trigger test -> slow path
+        l_slow, l_back = self.lab("slow"), self.lab("back")
+        em.salu(f"s_or_b64 {self.s_or}, {self.s_m1}, {self.s_m2}")
+        em.salu(f"s_cbranch_scc1 {l_slow}")
+        snap2 = em.snapshot()
+        self.emit_l_update()
+        em.label(l_back)
+        self.deferred.append(("slow", snap2, l_slow, l_back, sb, pn))
 
-    def slot_addr_update(self, vgpr_blk, off_blk, n, sgpr):
-        for i in range(n):
-            self.em.valu(f"v_add_u32 {vgpr_blk.r(i)}, {sgpr}, {off_blk.r(i)}",
-                         dst=[vgpr_blk.r(i)], src=[off_blk.r(i)])
+    def emit_deferred(self):
+        em = self.em
+        for item in self.deferred:
+            if item[0] == "mask":
+                _, snap, l_mask, l_join, sb, build = item
+                em.restore(snap)
+                em.label(l_mask)
+                self.emit_all(self.ops_mask(sb))
+                mf, others = build()
+                weave(em, mf, others)
+                em.drain()
+                em.salu(f"s_branch {l_join}")
+            else:
+                _, snap, l_slow, l_back, sb, pn = item
+                em.restore(snap)
+                em.label(l_slow)
+                self.emit_rescale(sb, pn)
+                em.salu(f"s_branch {l_back}")
 
     def epilogue(self):
         em, t = self.em, self.v_t
+        # loads still in flight (Q of an empty item, DMAs past the last tile)
+        # must land before their registers and LDS are reused (next item, or
+        # another workgroup after the end of the program)
+        em.salu("s_waitcnt vmcnt(0)")
         em.drain()
-        self.debug_dump("epi", [self.v_l.r(0), self.v_l.r(1), self.v_mc.r(0), self.v_mc.r(1),
-                                self.v_m.r(0), self.v_m.r(1)])
-        # dims 32 db + 8 i4 + 4 h .. +3 of row q: bytes qoff + 8 h + 64 db + 16 i4
+        # Lane (l, h) holds dims 32db + 8j + 4h .. +3 of row l%32 in O^T block
+        # registers 4j .. 4j+3.  For each pair j = 2jp, 2jp+1, one
+        # v_permlane32_swap per packed dword gives lanes < 32 dims 8(2jp) .. +7
+        # and lanes >= 32 dims 8(2jp+1) .. +7: 16 contiguous bytes per lane,
+        # stored at qoff + 16h + 64db + 32jp.  The E buffers are free here; four
+        # rotating output sets keep each store's data untouched after it issues.
         em.valu(f"v_lshrrev_b32 {t.r(0)}, 5, v0", dst=[t.r(0)], src=["v0"])      # h
-        em.valu(f"v_lshlrev_b32 {t.r(7)}, 3, {t.r(0)}", dst=[t.r(7)], src=[t.r(0)])  # 8h
+        em.valu(f"v_lshlrev_b32 {t.r(7)}, 4, {t.r(0)}", dst=[t.r(7)], src=[t.r(0)])  # 16h
+        E = self.v_E
         for qb in range(2):
             l = self.v_l.r(qb)
             em.valu(f"v_mov_b32 {t.r(0)}, {l}", dst=[t.r(0)], src=[l])
@@ -718,17 +809,25 @@ class Gen:
                     src=[self.v_qoff.r(qb), t.r(7)])
             for db in range(self.NDB):
                 blk = self.a_O[qb][db]
-                for i4 in range(4):
-                    for k in range(4):
-                        dst = t.r(3 + k)
-                        em.valu(f"v_accvgpr_read_b32 {dst}, {blk.r(4 * i4 + k)}", dst=[dst],
-                                src=[blk.r(4 * i4 + k)])
-                        em.valu(f"v_mul_f32 {dst}, {dst}, {t.r(1)}", dst=[dst], src=[dst, t.r(1)])
-                    em.valu(f"{self.cvt_op} {t.r(3)}, {t.r(3)}, {t.r(4)}", dst=[t.r(3)], src=[t.r(3), t.r(4)])
-                    em.valu(f"{self.cvt_op} {t.r(4)}, {t.r(5)}, {t.r(6)}", dst=[t.r(4)], src=[t.r(5), t.r(6)])
-                    off = 64 * db + 16 * i4
-                    em.vmem(f"buffer_store_dwordx2 {t.r(3, 2)}, {t.r(2)}, {self.s_ro}, 0 offen offset:{off}",
-                            src=[t.r(3, 2), t.r(2)])
+                for jp in range(2):
+                    k = 2 * db + jp
+                    F, o = E[k % 2], 8 + 4 * ((k // 2) % 2)
+                    for jj in range(2):
+                        j = 2 * jp + jj
+                        for r in range(4):
+                            dst = F.r(4 * jj + r)
+                            em.valu(f"v_accvgpr_read_b32 {dst}, {blk.r(4 * j + r)}", dst=[dst],
+                                    src=[blk.r(4 * j + r)])
+                            em.valu(f"v_mul_f32 {dst}, {dst}, {t.r(1)}", dst=[dst], src=[dst, t.r(1)])
+                        for c in range(2):
+                            a, b = F.r(4 * jj + 2 * c), F.r(4 * jj + 2 * c + 1)
+                            em.valu(f"{self.cvt_op} {F.r(o + 2 * jj + c)}, {a}, {b}",
+                                    dst=[F.r(o + 2 * jj + c)], src=[a, b])
+                    for c in range(2):
+                        x, y = F.r(o + c), F.r(o + 2 + c)
+                        em.valu(f"v_permlane32_swap_b32 {x}, {y}", dst=[x, y], src=[x, y])
+                    em.vmem(f"buffer_store_dwordx4 {F.r(o, 4)}, {t.r(2)}, {self.s_ro}, 0 offen "
+                            f"offset:{64 * db + 32 * jp}", src=[F.r(o, 4), t.r(2)])
             # LSE = ln2 * (mc + log2 l), -inf when l = 0 (vcc still holds l > 0)
             em.valu(f"v_log_f32 {t.r(3)}, {l}", dst=[t.r(3)], src=[l], trans=True)
             em.valu(f"v_add_f32 {t.r(3)}, {self.v_mc.r(qb)}, {t.r(3)}", dst=[t.r(3)], src=[self.v_mc.r(qb), t.r(3)])
@@ -737,119 +836,152 @@ class Gen:
                     src=[t.r(3), str(self.v_ninf)])
             em.vmem(f"buffer_store_dword {t.r(3)}, {self.v_lseoff.r(qb)}, {self.s_rl}, 0 offen",
                     src=[t.r(3), self.v_lseoff.r(qb)])
-        em.salu("s_endpgm")
 
     # ------------------------------------------------------------------------
     def body(self):
         em = self.em
         self.alloc()
-        self.prologue()
-        self.lane_constants()
-        self.load_q_and_init()
-        x = self.s_x
+        self.kernel_setup()
+        self.deferred = []
+        y = self.s_y
+        T, DPW = self.TILE, self.DPW
+        self.lane_dma()
+        self.lane_kv()
+        # ---- one item (batch, q-head, q-tile) per pass ----------------------------
+        l_item, l_exit = self.lab("item"), self.lab("exit")
+        em.drain()
+        em.label(l_item)
+        self.item_setup(l_exit)
+        self.lane_rows()
+        # the previous item's O stores are complete before new loads are counted
+        em.salu("s_waitcnt vmcnt(0)")
+        # Q loads first, then the first K/V tiles, so that both latencies overlap
+        # with each other and with the remaining set-up
+        self.load_q()
+        self.init_state()
         l_epi = self.lab("epilogue")
         em.salu(f"s_cmp_eq_u32 {self.s_ntiles}, 0")
         em.salu(f"s_cbranch_scc1 {l_epi}")
-        # ---- first three tiles into the rings ----------------------------------
-        for tt in range(3):
-            em.salu(f"s_mov_b32 {x[5]}, {tt}")
-            em.salu(f"s_mov_b32 {self.s_kdsl}, {self.KBASE + tt * self.TILE}")
-            em.salu(f"s_mov_b32 {self.s_vdsl}, {self.VBASE + tt * self.TILE}")
-            self.dma_tile(x[5], self.s_kdsl, self.s_vdsl)
-        self.wait_vm(2 * self.DPW)
+        # every wave is done with the previous item's LDS before it is refilled
         em.salu("s_barrier")
-        # ---- pipeline prologue: S^T(0), max(0); S^T(1) next to exp(0) -----------
-        em.salu(f"s_mov_b32 {self.s_ksl}, 0")
-        self.slot_addr_update(self.v_kaddr, self.v_koff, self.NS, self.s_ksl)
-        em.salu(f"s_mov_b32 {self.s_vsl0}, {self.VBASE}")
-        self.slot_addr_update(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl0)
-        self.debug_dump("q", [self.a_Q[q][s].r(i) for q in range(2) for s in range(self.NS) for i in range(4)])
+        # ---- tiles 0 .. PREFETCH-1 into the rings ---------------------------------
+        for tt in range(PREFETCH):
+            em.salu(f"s_mov_b32 {y[5]}, {tt}")
+            em.salu(f"s_add_u32 {self.s_kdw}, {self.s_wrow}, {self.KBASE + (tt % KSLOTS) * T}")
+            em.salu(f"s_add_u32 {self.s_vdw}, {self.s_wrow}, {self.VBASE + (tt % VSLOTS) * T}")
+            self.emit_all(self.ops_dma_desc(y[5]) + self.ops_dma_issue("k") + self.ops_dma_issue("v"))
+        # ring slots for iteration t = 0: K read tile 1, DMA tile PREFETCH; V tiles 0, 1
+        em.salu(f"s_mov_b32 {self.s_ksl}, {T}")
+        em.salu(f"s_mov_b32 {self.s_kdsl}, {(PREFETCH % KSLOTS) * T}")
+        em.salu(f"s_mov_b32 {self.s_vsl0}, 0")
+        em.salu(f"s_mov_b32 {self.s_vsl1}, {T}")
+        em.salu(f"s_mov_b32 {self.s_vdsl}, {(PREFETCH % VSLOTS) * T}")
+        em.salu(f"s_add_u32 {self.s_kdw}, {self.s_wrow}, {self.KBASE + (PREFETCH % KSLOTS) * T}")
+        em.salu(f"s_add_u32 {self.s_vdw}, {self.s_wrow}, {(PREFETCH % VSLOTS) * T}")
+        self.wait_vm((PREFETCH - 1) * 2 * DPW)                  # Q and tile 0 resident
+        em.salu("s_barrier")
+        # ---- sub-tile 0: S^T(0); its row max sets m; S^T(1) next to softmax(0) ----
+        self.emit_all(self.ops_addr(self.v_kaddr, self.v_koff, self.NS, 0))
         self.emit_all(self.ops_k_loads(0))
-        self.debug_dump("ko0", [self.v_KO[s].r(i) for s in range(self.NS) for i in range(4)])
-        self.emit_all(self.ops_qk(0))
-        self.debug_dump("s0", [self.v_S[0][q].r(i) for q in range(2) for i in range(16)])
+        self.emit_all(self.mf_qk(0))
         self.emit_all(self.ops_k_loads(1))
         em.salu(f"s_mov_b32 {self.s_k0}, 0")
         l_skip = self.lab("nomask0")
         em.salu(f"s_cmp_gt_i32 32, {self.s_kvfull}")
         em.salu(f"s_cbranch_scc0 {l_skip}")
         snap = em.snapshot()
-        for qb in range(2):
-            self.emit_all(self.ops_mask(0, qb))
+        self.emit_all(self.ops_mask(0))
         em.label(l_skip)
         em.restore(snap)
-        self.emit_all(self.ops_max(0))
         for qb in range(2):
-            m, mx, mc = self.v_m.r(qb), self.v_mx.r(qb), self.v_mc.r(qb)
+            self.emit_all(self.ops_rowmax(0, qb))
+            m, mx = self.v_m.r(qb), self.v_mx.r(qb)
             em.valu(f"v_mov_b32 {m}, {mx}", dst=[m], src=[mx])
-            em.valu(f"v_mul_f32 {mc}, s24, {m}", dst=[mc], src=[m])
-            em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {m}", src=[m])
-            em.valu(f"v_cndmask_b32 {mc}, {mc}, 0, vcc", dst=[mc], src=[mc])
-        interleave(em, self.ops_qk(1), self.ops_exp(0, 0, 0) + self.ops_exp(0, 1, 0) + self.ops_v_loads(0))
+            self.emit_set_mc(qb)
+        self.emit_all(self.ops_addr(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl0))
+        e, s_, c = self.ops_softmax(0, 0)
+        weave(em, self.mf_qk(1), e + self.ops_v_loads(0, 0) + s_ + c)
+        self.emit_l_update()
+        # ---- tile 1 resident before the loop ---------------------------------------
+        self.wait_vm((PREFETCH - 2) * 2 * DPW)
         em.salu("s_barrier")
-        # ---- main loop over tiles t = 0 .. n_tiles-2 -----------------------------
-        slows = []
-        l_last, l_loop = self.lab("last"), self.lab("loop")
+        em.salu(f"s_mov_b32 {self.s_k0}, 32")
         em.salu(f"s_mov_b32 {self.s_t}, 0")
         em.salu(f"s_sub_u32 {self.s_tlast}, {self.s_ntiles}, 1")
+        l_last, l_loop = self.lab("last"), self.lab("loop")
+        rel_pre = em.rel_state()
         em.salu(f"s_cmp_eq_u32 {self.s_tlast}, 0")
         em.salu(f"s_cbranch_scc1 {l_last}")
-        em.drain()
+        # ---- main loop over tiles t = 0 .. n_tiles-2.  The body is emitted from
+        # the merge of the entry state and its own back-edge state (re-emitted
+        # until that merge is a fixed point), so no drain is needed at the edge.
         em.label(l_loop)
-        snap_loop = em.snapshot()
-        # ring slots for tile t: K read (t+1)%3, K dma t%3, V cur t%4, V next (t+1)%4, V dma (t+3)%4
-        self.emit_slot_sgprs()
-        em.salu(f"s_add_u32 {x[5]}, {self.s_t}, 3")
-        self.dma_tile(x[5], self.s_kdsl, self.s_vdsl)
-        self.slot_addr_update(self.v_kaddr, self.v_koff, self.NS, self.s_ksl)
-        em.salu(f"s_lshl_b32 {self.s_k0}, {self.s_t}, 6")
-        em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
-        slows.append(self.step(sb=1, pb=0, kb_k=0, kb_v=1))
-        self.slot_addr_update(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl1)
-        em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
-        slows.append(self.step(sb=0, pb=1, kb_k=1, kb_v=0))
-        self.wait_vm(2 * self.DPW)
-        em.salu("s_barrier")
-        em.salu(f"s_add_u32 {self.s_t}, {self.s_t}, 1")
-        em.salu(f"s_cmp_lt_u32 {self.s_t}, {self.s_tlast}")
-        em.drain()
+        mark = (len(em.lines), self._lab, len(self.deferred))
+        rel_in = rel_pre
+        for _ in range(4):
+            em.apply_rel(rel_in)
+            self.emit_iteration()
+            merged = Emitter.merge_rel(rel_pre, em.rel_state())
+            if merged == rel_in:
+                break
+            del em.lines[mark[0]:]
+            self._lab = mark[1]
+            del self.deferred[mark[2]:]
+            rel_in = merged
+        else:
+            raise RuntimeError("loop hazard state did not converge")
         em.salu(f"s_cbranch_scc1 {l_loop}")
-        # ---- last tile: P.V(2t) next to softmax(2t+1), then P.V(2t+1) -------------
+        rel_exit = em.rel_state()
+        # ---- last tile: P.V(2n-2) next to softmax(2n-1), then P.V(2n-1) ------------
         em.label(l_last)
-        em.drain()
-        em.salu(f"s_lshl_b32 {self.s_k0}, {self.s_t}, 6")
-        em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
-        slows.append(self.step(sb=1, pb=0, kb_k=0, kb_v=1, do_qk=False))
-        self.step(sb=0, pb=1, kb_k=1, kb_v=0, do_soft=False, do_qk=False, do_vload=False)
+        em.apply_rel(Emitter.merge_rel(rel_exit, rel_pre))
+        self.step(0, "noqk", kb_v=1, pre=self.ops_addr(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl0))
+        self.step(1, "pvonly")
         em.label(l_epi)
         self.epilogue()
-        # ---- out-of-line slow paths --------------------------------------------------
-        for sl in slows:
-            if sl is not None:
-                self.emit_slow(sl)
+        em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        em.drain()
+        em.salu(f"s_branch {l_item}")
+        em.label(l_exit)
+        em.salu("s_waitcnt vmcnt(0)")
+        em.salu("s_endpgm")
+        self.emit_deferred()
 
-    def emit_slot_sgprs(self):
-        """Slot byte addresses for tile s_t (s_t % 3 and s_t % 4 from scratch)."""
-        em, x = self.em, self.s_x
-        # t % 3 via (t * 0xAAAB) >> 17 for t < 2^16 -> quotient; remainder = t - 3q
-        em.salu(f"s_mul_i32 {x[0]}, {self.s_t}, 0xAAAB")
-        em.salu(f"s_lshr_b32 {x[0]}, {x[0]}, 17")
-        em.salu(f"s_mul_i32 {x[0]}, {x[0]}, 3")
-        em.salu(f"s_sub_u32 {x[0]}, {self.s_t}, {x[0]}")            # t % 3
-        em.salu(f"s_mul_i32 {self.s_kdsl}, {x[0]}, {self.TILE}")
-        em.salu(f"s_add_u32 {self.s_kdsl}, {self.s_kdsl}, {self.KBASE}")   # K dma slot (t+3)%3 = t%3
-        em.salu(f"s_add_u32 {x[1]}, {x[0]}, 1")
-        em.salu(f"s_cmp_eq_u32 {x[1]}, 3")
-        em.salu(f"s_cselect_b32 {x[1]}, 0, {x[1]}")
-        em.salu(f"s_mul_i32 {self.s_ksl}, {x[1]}, {self.TILE}")           # K read slot (t+1)%3
-        em.salu(f"s_and_b32 {x[0]}, {self.s_t}, 3")
-        em.salu(f"s_mul_i32 {self.s_vsl0}, {x[0]}, {self.TILE}")           # V(t)
-        em.salu(f"s_add_u32 {x[1]}, {x[0]}, 1")
-        em.salu(f"s_and_b32 {x[1]}, {x[1]}, 3")
-        em.salu(f"s_mul_i32 {self.s_vsl1}, {x[1]}, {self.TILE}")           # V(t+1)
-        em.salu(f"s_add_u32 {x[1]}, {x[0]}, 3")
-        em.salu(f"s_and_b32 {x[1]}, {x[1]}, 3")
-        em.salu(f"s_mul_i32 {self.s_vdsl}, {x[1]}, {self.TILE}")           # V(t+3)
+    def emit_iteration(self):
+        """Tile t: steps j = 2t and 2t+1, then the ring hand-over."""
+        em, x, y = self.em, self.s_x, self.s_y
+        T, DPW = self.TILE, self.DPW
+        # step 2t: K operands of tile t+1 (sub-tile 0), V operands of tile t
+        # (sub-tile 1); DMA of tile t+PREFETCH: its descriptors and K rows
+        pre = (self.ops_addr(self.v_kaddr, self.v_koff, self.NS, self.s_ksl)
+               + self.ops_addr(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl0))
+        dma_k = ([self._salu_op(f"s_add_u32 {y[5]}, {self.s_t}, {PREFETCH}")]
+                 + self.ops_dma_desc(y[5]) + self.ops_dma_issue("k"))
+        self.step(0, "full", kb_k=0, kb_v=1, pre=pre, extra=dma_k)
+        em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
+        # step 2t+1: K operands of tile t+1 (sub-tile 1), V operands of tile t+1
+        # (sub-tile 0); V rows of tile t+PREFETCH
+        self.step(1, "full", kb_k=1, kb_v=0,
+                  pre=self.ops_addr(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl1),
+                  extra=self.ops_dma_issue("v"))
+        em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
+        # tile t+2 resident for the next tile; the slots read here become free
+        self.wait_vm(2 * 2 * DPW)
+        em.salu("s_barrier")
+        em.salu(f"s_add_u32 {self.s_ksl}, {self.s_ksl}, {T}")
+        em.salu(f"s_and_b32 {self.s_ksl}, {self.s_ksl}, {KSLOTS * T - 1}")
+        em.salu(f"s_add_u32 {self.s_kdsl}, {self.s_kdsl}, {T}")
+        em.salu(f"s_and_b32 {self.s_kdsl}, {self.s_kdsl}, {KSLOTS * T - 1}")
+        em.salu(f"s_mov_b32 {self.s_vsl0}, {self.s_vsl1}")
+        for r in (self.s_vsl1, self.s_vdsl):
+            em.salu(f"s_add_u32 {r}, {r}, {T}")
+            em.salu(f"s_sub_u32 {x[1]}, {r}, {VSLOTS * T}")
+            em.salu(f"s_cselect_b32 {r}, {r}, {x[1]}")
+        em.salu(f"s_add_u32 {self.s_kdw}, {self.s_kdsl}, {self.s_wrow}")
+        em.salu(f"s_add_u32 {self.s_kdw}, {self.s_kdw}, {self.KBASE}")
+        em.salu(f"s_add_u32 {self.s_vdw}, {self.s_vdsl}, {self.s_wrow}")
+        em.salu(f"s_add_u32 {self.s_t}, {self.s_t}, 1")
+        em.salu(f"s_cmp_lt_u32 {self.s_t}, {self.s_tlast}")
 
     # ------------------------------------------------------------------------
     def assemble_text(self) -> str:

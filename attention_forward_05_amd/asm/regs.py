@@ -104,6 +104,39 @@ class Emitter:
         self.mfma_w, self.valu_w, self.trans_w = dict(self.mfma_w), dict(self.valu_w), dict(self.trans_w)
         self.lds_pending = [set(x) for x in pend]
 
+    # ---- relative states, for control-flow joins ----------------------------
+    def rel_state(self):
+        """The hazard state as ages (wait states since each write) plus the
+        in-flight LDS reads, independent of the absolute clock."""
+        ages = tuple({r: self.idx - w for r, w in t.items()}
+                     for t in (self.mfma_w, self.valu_w, self.trans_w))
+        return ages, [set(x) for x in self.lds_pending]
+
+    @staticmethod
+    def merge_rel(a, b):
+        """Conservative merge of two relative states: the most recent write of
+        each register, and in-flight LDS reads aligned at the newest one."""
+        ages = []
+        for ta, tb in zip(a[0], b[0]):
+            m = dict(ta)
+            for r, v in tb.items():
+                m[r] = min(m.get(r, v), v)
+            ages.append(m)
+        pa, pb = a[1], b[1]
+        n = max(len(pa), len(pb))
+        pend = []
+        for i in range(n):
+            sa = pa[len(pa) - n + i] if len(pa) - n + i >= 0 else set()
+            sb = pb[len(pb) - n + i] if len(pb) - n + i >= 0 else set()
+            pend.append(set(sa) | set(sb))
+        return tuple(ages), pend
+
+    def apply_rel(self, rel):
+        ages, pend = rel
+        self.mfma_w, self.valu_w, self.trans_w = (
+            {r: self.idx - a for r, a in t.items()} for t in ages)
+        self.lds_pending = [set(x) for x in pend][-MAX_LGKM:]
+
     def drain(self):
         """Make every earlier result safe to use (used at control-flow joins)."""
         if self.lds_pending:
@@ -261,6 +294,44 @@ def interleave(em: Emitter, mfmas, others, lead: int = 0):
         take = (len(ot) - i + remaining_m - 1) // remaining_m
         for _ in range(take):
             ot[i]()
+            i += 1
+    while i < len(ot):
+        ot[i]()
+        i += 1
+
+
+class Op:
+    """One schedulable instruction (or an indivisible group) with an issue
+    cost in VALU-instruction units."""
+
+    def __init__(self, fn, cost=1.0):
+        self.fn, self.cost = fn, cost
+
+    def __call__(self):
+        self.fn()
+
+
+def weave(em: Emitter, mfmas, others, tail: float = 0.0):
+    """Spread `others` (Op objects, emitted in list order) over the gaps after
+    each MFMA so that every gap carries about the same issue cost.  `tail`
+    extra cost units are assumed to follow the last MFMA (work emitted after
+    the call), so the last gaps are left lighter."""
+    mf = list(mfmas)
+    ot = list(others)
+    total = sum(o.cost for o in ot) + tail
+    n = len(mf)
+    if n == 0:
+        for o in ot:
+            o()
+        return
+    per = total / n
+    i, done = 0, 0.0
+    for k, f in enumerate(mf):
+        f()
+        target = per * (k + 1)
+        while i < len(ot) and done + ot[i].cost * 0.5 <= target:
+            ot[i]()
+            done += ot[i].cost
             i += 1
     while i < len(ot):
         ot[i]()

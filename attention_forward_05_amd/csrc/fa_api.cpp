@@ -63,10 +63,11 @@ int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o,
 
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
-  // Size limits of the kernel's 32-bit address arithmetic and launch grid:
-  // grid y (query tiles) and z (batch) at most 65535; one batch slice of q/o
-  // below 2 GiB; key tiles below 65536; B*Sq*Hq and B*Skv below 2^31.
-  if (fa::query_tiles(Sq) > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  // Size limits of the kernel's 32-bit address arithmetic and item decoding:
+  // query tiles at most 65535; fewer than 2^24 (batch, q-head, query tile)
+  // items; one batch slice of q/o below 2 GiB; key tiles below 65536; B*Sq*Hq
+  // and B*Skv below 2^31.
+  if (fa::query_tiles(Sq) > 65535 || fa::work_items(B, Sq, Hq) >= (1ll << 24)) return FA_ERR_UNSUPPORTED;
   if ((uint64_t)Sq * (uint64_t)Hq * (uint64_t)D * 2u >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
   if ((uint64_t)B * (uint64_t)Sq * (uint64_t)Hq >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
   if ((uint64_t)B * (uint64_t)Skv >= (1ull << 31)) return FA_ERR_UNSUPPORTED;

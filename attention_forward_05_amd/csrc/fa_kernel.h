@@ -20,8 +20,9 @@ struct LaunchArgs {
   hipStream_t stream;
 };
 
-// Workgroups launched for these sizes.
-int64_t grid_blocks(int B, int Sq, int Hq);
+// (batch, q-head, 256-row query tile) items of these sizes; the persistent
+// kernel runs min(items, compute units) workgroups over them.
+int64_t work_items(int B, int Sq, int Hq);
 // Query tiles of 256 rows and key tiles of 64 keys.
 int query_tiles(int Sq);
 int key_tiles(int Skv);

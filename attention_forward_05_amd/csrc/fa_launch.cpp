@@ -2,11 +2,14 @@
 // generator in attention_forward_05_amd/asm and embedded in this library as a
 // code object) and launches them.
 //
-// Grid: x = q-head slot (Hq), y = query tile of 256 rows (nq), z = batch.
-// Workgroups are handed to the 8 XCDs round-robin by linear id, whose
-// residue mod 8 is x mod 8 when Hq % 8 == 0; the kernel then maps slot x to
-// head (x % 8) * (Hq / 8) + x / 8 so each XCD serves a contiguous run of
-// heads (whole GQA groups), whose K/V its L2 keeps.
+// The kernels are persistent: the grid has G = min(items, compute units)
+// workgroups, one per CU, and workgroup g takes item r*G + (g or G-1-g,
+// alternating by round r) of the (batch, q-head, 256-row query tile) items,
+// which the kernel orders longest first.  Workgroups are handed to the 8
+// XCDs round-robin by id, so within a round each XCD sees one residue of the
+// head slot mod 8; the kernel maps slot s to head (s % 8) * (Hq / 8) + s / 8
+// when Hq % 8 == 0, so each XCD serves a contiguous run of heads (whole GQA
+// groups) whose K/V its L2 keeps.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,7 +37,7 @@ struct alignas(8) KernArgs {
   float* lse;
   int32_t B, Sq, Skv, Hq, Hkv, causal;
   float c;
-  int32_t nq;
+  uint32_t nq_grid;  // query tiles | workgroups << 16
   uint32_t gmagic;  // hk = (hq * gmagic) >> 20
   uint32_t hq_xcd;  // Hq / 8 when Hq % 8 == 0, else 0
 };
@@ -47,6 +50,7 @@ struct DeviceKernels {
   bool loaded = false;
   hipModule_t mod = nullptr;
   hipFunction_t fn[4] = {};
+  int cus = 0;  // compute units of the device
 };
 
 std::mutex g_mu;
@@ -66,6 +70,9 @@ hipError_t kernels_for_current_device(DeviceKernels** out) {
       e = hipModuleGetFunction(&d.fn[i], d.mod, kNames[i]);
       if (e != hipSuccess) return e;
     }
+    e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (d.cus < 1) d.cus = 1;
     d.loaded = true;
   }
   *out = &d;
@@ -86,7 +93,7 @@ bool group_magic(int Hq, int Hkv, uint32_t* magic) {
   return true;
 }
 
-int64_t grid_blocks(int B, int Sq, int Hq) {
+int64_t work_items(int B, int Sq, int Hq) {
   return (int64_t)((Sq + kBM - 1) / kBM) * B * Hq;
 }
 
@@ -112,14 +119,17 @@ hipError_t launch(const LaunchArgs& a) {
   ka.Hkv = a.Hkv;
   ka.causal = a.causal;
   ka.c = a.c;
-  ka.nq = query_tiles(a.Sq);
+  const int64_t nq = query_tiles(a.Sq);
+  const int64_t items = nq * a.B * a.Hq;
+  const int64_t grid = items < dk->cus ? items : dk->cus;
+  ka.nq_grid = (uint32_t)nq | ((uint32_t)grid << 16);
   if (!group_magic(a.Hq, a.Hkv, &ka.gmagic)) return hipErrorInvalidValue;
   ka.hq_xcd = (a.Hq % 8 == 0) ? (uint32_t)(a.Hq / 8) : 0u;
   size_t size = sizeof(ka);
   void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &ka, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
                     HIP_LAUNCH_PARAM_END};
-  e = hipModuleLaunchKernel(dk->fn[variant], (unsigned)a.Hq, (unsigned)ka.nq, (unsigned)a.B, 256,
-                            1, 1, 0, a.stream, nullptr, config);
+  e = hipModuleLaunchKernel(dk->fn[variant], (unsigned)grid, 1, 1, 256, 1, 1, 0, a.stream,
+                            nullptr, config);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

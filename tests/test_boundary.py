@@ -85,7 +85,13 @@ def test_invalid_arguments(lib, entry, over):
 
 
 UNSUPPORTED = [dict(D=96), dict(D=256), dict(D=32), dict(D=16), dict(scale=-0.1),
-               dict(scale=3e38)]
+               dict(scale=3e38),
+               # 2^24 (batch, q-head, query tile) items: beyond the item decoding
+               dict(B=16384, Sq=1, Skv=1, Hq=1024, Hkv=1),
+               # 65536 key tiles of 64 keys
+               dict(Skv=65536 * 64),
+               # 65536 query tiles of 256 rows (and a 2 GiB q slice)
+               dict(Sq=65536 * 256, Hq=1, Hkv=1, D=64)]
 
 
 @pytest.mark.parametrize("over", UNSUPPORTED, ids=[str(x) for x in UNSUPPORTED])
