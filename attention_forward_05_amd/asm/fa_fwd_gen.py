@@ -228,7 +228,7 @@ class Gen:
         em.valu(f"v_cndmask_b32 {t.r(7)}, 0, {dv}, vcc", dst=[t.r(7)], src=[dv])
         em.valu(f"v_sub_u32 {rem}, {rem}, {t.r(7)}", dst=[rem], src=[rem, t.r(7)])
 
-    def item_setup(self, l_exit):
+    def item_setup_a(self, l_exit):
         """Decode this round's item; set the block's rows, key range and
         buffer resources.  Jumps to l_exit when the workgroup has no item left."""
         em, D = self.em, self.D
@@ -302,7 +302,12 @@ class Gen:
         em.salu(f"s_addc_u32 {self.s_kb.r(1)}, s11, {x[3]}")
         em.salu(f"s_add_u32 {self.s_vb.r(0)}, s12, {x[2]}")
         em.salu(f"s_addc_u32 {self.s_vb.r(1)}, s13, {x[3]}")
-        # Q / O descriptors: base = batch + head, records = (Sq*Hq - hq)*D*2
+        self.emit_qo_desc(self.s_rq, 8)
+
+    def emit_qo_desc(self, rs, base):
+        """Q (base s8) or O (base s14) buffer resource of the item:
+        base = batch + head, records = (Sq*Hq - hq)*D*2."""
+        em, D, x = self.em, self.D, self.s_x
         em.salu(f"s_mul_i32 {x[0]}, s19, s21")                     # Sq*Hq
         em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, {x[0]}")           # b*Sq*Hq
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
@@ -310,12 +315,18 @@ class Gen:
         em.salu(f"s_mul_hi_u32 {x[3]}, {x[4]}, {D * 2}")
         em.salu(f"s_sub_u32 {x[5]}, {x[0]}, {self.s_hq}")
         em.salu(f"s_mul_i32 {x[5]}, {x[5]}, {D * 2}")
-        for rs, base in ((self.s_rq, 8), (self.s_ro, 14)):
-            em.salu(f"s_add_u32 {rs.r(0)}, s{base}, {x[2]}")
-            em.salu(f"s_addc_u32 {rs.r(1)}, s{base + 1}, {x[3]}")
-            em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
-            em.salu(f"s_mov_b32 {rs.r(2)}, {x[5]}")
-            em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
+        em.salu(f"s_add_u32 {rs.r(0)}, s{base}, {x[2]}")
+        em.salu(f"s_addc_u32 {rs.r(1)}, s{base + 1}, {x[3]}")
+        em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
+        em.salu(f"s_mov_b32 {rs.r(2)}, {x[5]}")
+        em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
+
+    def item_setup_b(self):
+        """The parts of an item's set-up that the previous item's epilogue
+        must not see overwritten: the O and LSE buffer resources and the
+        per-lane row offsets."""
+        em, x = self.em, self.s_x
+        self.emit_qo_desc(self.s_ro, 14)
         # LSE descriptor: base = lse + ((b*Hq + hq)*Sq)*4, records = Sq*4 (0 if no lse)
         em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, s21")
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
@@ -330,6 +341,7 @@ class Gen:
         em.salu(f"s_or_b32 {x[0]}, s16, s17")
         em.salu(f"s_cmp_eq_u32 {x[0]}, 0")
         em.salu(f"s_cselect_b32 {self.s_rl.r(2)}, 0, {self.s_rl.r(2)}")
+        self.lane_rows()
 
     def lane_rows(self):
         """Per-lane query rows: Q/O and LSE byte offsets, last visible key."""
@@ -445,11 +457,18 @@ class Gen:
         """Issue the loads of the wave's 64 Q rows straight into the Q AGPRs
         (lanes of the upper half take dims 8..15 of each 16-dim step)."""
         em, t = self.em, self.v_t
+        # row q = qw0 + 32 qb + l32; address q*Hq*D*2 + 16h
+        em.valu(f"v_and_b32 {t.r(0)}, 31, v0", dst=[t.r(0)], src=["v0"])
+        em.valu(f"v_add_u32 {t.r(0)}, {self.s_qw0}, {t.r(0)}", dst=[t.r(0)], src=[t.r(0)])
+        em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {self.D * 2}")
         em.valu(f"v_lshrrev_b32 {t.r(4)}, 5, v0", dst=[t.r(4)], src=["v0"])
         em.valu(f"v_lshlrev_b32 {t.r(4)}, 4, {t.r(4)}", dst=[t.r(4)], src=[t.r(4)])
         for qb in range(2):
-            em.valu(f"v_add_u32 {t.r(5 + qb)}, {self.v_qoff.r(qb)}, {t.r(4)}",
-                    dst=[t.r(5 + qb)], src=[self.v_qoff.r(qb), t.r(4)])
+            if qb:
+                em.valu(f"v_add_u32 {t.r(0)}, 32, {t.r(0)}", dst=[t.r(0)], src=[t.r(0)])
+            em.valu(f"v_mul_lo_u32 {t.r(5 + qb)}, {t.r(0)}, {self.s_x[0]}", dst=[t.r(5 + qb)], src=[t.r(0)])
+            em.valu(f"v_add_u32 {t.r(5 + qb)}, {t.r(5 + qb)}, {t.r(4)}",
+                    dst=[t.r(5 + qb)], src=[t.r(5 + qb), t.r(4)])
         for qb in range(2):
             for s in range(self.NS):
                 dst = str(self.a_Q[qb][s])
@@ -783,10 +802,8 @@ class Gen:
 
     def epilogue(self):
         em, t = self.em, self.v_t
-        # loads still in flight (Q of an empty item, DMAs past the last tile)
-        # must land before their registers and LDS are reused (next item, or
-        # another workgroup after the end of the program)
-        em.salu("s_waitcnt vmcnt(0)")
+        # (the next item's Q and K/V loads may be in flight: the epilogue reads
+        # none of the registers or LDS they write)
         em.drain()
         # Lane (l, h) holds dims 32db + 8j + 4h .. +3 of row l%32 in O^T block
         # registers 4j .. 4j+3.  For each pair j = 2jp, 2jp+1, one
@@ -847,39 +864,22 @@ class Gen:
         T, DPW = self.TILE, self.DPW
         self.lane_dma()
         self.lane_kv()
-        # ---- one item (batch, q-head, q-tile) per pass ----------------------------
-        l_item, l_exit = self.lab("item"), self.lab("exit")
+        # ---- items (batch, q-head, q-tile), one per pass.  The next item's Q and
+        # first K/V tiles are requested before the current item's epilogue, so
+        # their latency is spent storing O.
+        l_exit, l_body, l_final = self.lab("exit"), self.lab("body"), self.lab("final")
         em.drain()
-        em.label(l_item)
-        self.item_setup(l_exit)
-        self.lane_rows()
-        # the previous item's O stores are complete before new loads are counted
-        em.salu("s_waitcnt vmcnt(0)")
-        # Q loads first, then the first K/V tiles, so that both latencies overlap
-        # with each other and with the remaining set-up
-        self.load_q()
+        self.item_setup_a(l_exit)
+        self.issue_item_loads()
+        em.drain()
+        em.label(l_body)
+        self.item_setup_b()
         self.init_state()
-        l_epi = self.lab("epilogue")
+        em.salu("s_waitcnt vmcnt(0)")      # Q, the first tiles, the previous item's stores
+        em.salu("s_barrier")
+        l_empty = self.lab("empty")
         em.salu(f"s_cmp_eq_u32 {self.s_ntiles}, 0")
-        em.salu(f"s_cbranch_scc1 {l_epi}")
-        # every wave is done with the previous item's LDS before it is refilled
-        em.salu("s_barrier")
-        # ---- tiles 0 .. PREFETCH-1 into the rings ---------------------------------
-        for tt in range(PREFETCH):
-            em.salu(f"s_mov_b32 {y[5]}, {tt}")
-            em.salu(f"s_add_u32 {self.s_kdw}, {self.s_wrow}, {self.KBASE + (tt % KSLOTS) * T}")
-            em.salu(f"s_add_u32 {self.s_vdw}, {self.s_wrow}, {self.VBASE + (tt % VSLOTS) * T}")
-            self.emit_all(self.ops_dma_desc(y[5]) + self.ops_dma_issue("k") + self.ops_dma_issue("v"))
-        # ring slots for iteration t = 0: K read tile 1, DMA tile PREFETCH; V tiles 0, 1
-        em.salu(f"s_mov_b32 {self.s_ksl}, {T}")
-        em.salu(f"s_mov_b32 {self.s_kdsl}, {(PREFETCH % KSLOTS) * T}")
-        em.salu(f"s_mov_b32 {self.s_vsl0}, 0")
-        em.salu(f"s_mov_b32 {self.s_vsl1}, {T}")
-        em.salu(f"s_mov_b32 {self.s_vdsl}, {(PREFETCH % VSLOTS) * T}")
-        em.salu(f"s_add_u32 {self.s_kdw}, {self.s_wrow}, {self.KBASE + (PREFETCH % KSLOTS) * T}")
-        em.salu(f"s_add_u32 {self.s_vdw}, {self.s_wrow}, {(PREFETCH % VSLOTS) * T}")
-        self.wait_vm((PREFETCH - 1) * 2 * DPW)                  # Q and tile 0 resident
-        em.salu("s_barrier")
+        em.salu(f"s_cbranch_scc1 {l_empty}")
         # ---- sub-tile 0: S^T(0); its row max sets m; S^T(1) next to softmax(0) ----
         self.emit_all(self.ops_addr(self.v_kaddr, self.v_koff, self.NS, 0))
         self.emit_all(self.ops_k_loads(0))
@@ -902,9 +902,7 @@ class Gen:
         e, s_, c = self.ops_softmax(0, 0)
         weave(em, self.mf_qk(1), e + self.ops_v_loads(0, 0) + s_ + c)
         self.emit_l_update()
-        # ---- tile 1 resident before the loop ---------------------------------------
-        self.wait_vm((PREFETCH - 2) * 2 * DPW)
-        em.salu("s_barrier")
+        # (tiles 0 .. PREFETCH-1 are resident: waited for at the item start)
         em.salu(f"s_mov_b32 {self.s_k0}, 32")
         em.salu(f"s_mov_b32 {self.s_t}, 0")
         em.salu(f"s_sub_u32 {self.s_tlast}, {self.s_ntiles}, 1")
@@ -937,15 +935,44 @@ class Gen:
         em.apply_rel(Emitter.merge_rel(rel_exit, rel_pre))
         self.step(0, "noqk", kb_v=1, pre=self.ops_addr(self.v_vaddr, self.v_voff, self.NDB, self.s_vsl0))
         self.step(1, "pvonly")
-        em.label(l_epi)
-        self.epilogue()
-        em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        em.label(l_empty)
         em.drain()
-        em.salu(f"s_branch {l_item}")
+        # every wave is done with this item's LDS before the next item fills it
+        em.salu("s_barrier")
+        em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        self.item_setup_a(l_final)
+        self.issue_item_loads()
+        self.epilogue()                     # the finished item's O and LSE
+        em.drain()
+        em.salu(f"s_branch {l_body}")
+        em.label(l_final)
+        self.epilogue()
         em.label(l_exit)
+        # nothing may be in flight when the wave ends and its registers and
+        # LDS are reused by another workgroup
         em.salu("s_waitcnt vmcnt(0)")
         em.salu("s_endpgm")
         self.emit_deferred()
+
+    def issue_item_loads(self):
+        """Q of the item (into the Q AGPRs) and its first PREFETCH K/V tiles,
+        with the ring slots set for the first tile iteration."""
+        em, y = self.em, self.s_y
+        T = self.TILE
+        self.load_q()
+        for tt in range(PREFETCH):
+            em.salu(f"s_mov_b32 {y[5]}, {tt}")
+            em.salu(f"s_add_u32 {self.s_kdw}, {self.s_wrow}, {self.KBASE + (tt % KSLOTS) * T}")
+            em.salu(f"s_add_u32 {self.s_vdw}, {self.s_wrow}, {self.VBASE + (tt % VSLOTS) * T}")
+            self.emit_all(self.ops_dma_desc(y[5]) + self.ops_dma_issue("k") + self.ops_dma_issue("v"))
+        # ring slots for iteration t = 0: K read tile 1, DMA tile PREFETCH; V tiles 0, 1
+        em.salu(f"s_mov_b32 {self.s_ksl}, {T}")
+        em.salu(f"s_mov_b32 {self.s_kdsl}, {(PREFETCH % KSLOTS) * T}")
+        em.salu(f"s_mov_b32 {self.s_vsl0}, 0")
+        em.salu(f"s_mov_b32 {self.s_vsl1}, {T}")
+        em.salu(f"s_mov_b32 {self.s_vdsl}, {(PREFETCH % VSLOTS) * T}")
+        em.salu(f"s_add_u32 {self.s_kdw}, {self.s_wrow}, {self.KBASE + (PREFETCH % KSLOTS) * T}")
+        em.salu(f"s_add_u32 {self.s_vdw}, {self.s_wrow}, {(PREFETCH % VSLOTS) * T}")
 
     def emit_iteration(self):
         """Tile t: steps j = 2t and 2t+1, then the ring hand-over."""
