@@ -1067,7 +1067,7 @@ def metadata(kernels) -> str:
             f"    .group_segment_fixed_size: {k['lds']}",
             "    .kernarg_segment_align: 8",
             f"    .kernarg_segment_size: {KERNARG_BYTES}",
-            "    .max_flat_workgroup_size: 256",
+            f"    .max_flat_workgroup_size: {k.get('wg', 256)}",
             f"    .name: {k['name']}",
             "    .private_segment_fixed_size: 0",
             f"    .sgpr_count: {k['ns']}",
@@ -1088,10 +1088,17 @@ VARIANTS = [("bf16", 128), ("bf16", 64), ("f16", 128), ("f16", 64)]
 
 
 def generate_all() -> str:
+    """Every kernel of the library: the four-wave variants, then the
+    eight-wave D = 128 variants (fa_fwd_x8)."""
+    from .fa_fwd_x8 import Gen8
     texts, metas = [], []
     for dt, D in VARIANTS:
         g = Gen(dt, D)
         txt, info = g.assemble_text()
+        texts.append(txt)
+        metas.append(info)
+    for dt in ("bf16", "f16"):
+        txt, info = Gen8(dt).assemble_text()
         texts.append(txt)
         metas.append(info)
     return "".join(texts) + metadata(metas)

@@ -1,0 +1,874 @@
+"""Generator of the eight-wave gfx950 (MI355X) attention forward kernel, D = 128.
+
+Same operation as the four-wave kernel (fa_fwd_gen.py): the tiled
+online-softmax forward pass of the JAX Pallas FlashAttention3 page
+(`kv_loop`: running max m, running sum l, rescaled accumulator) in the exp2
+form of the Croqtile `flash_atten` page, with a lazy reference max:
+
+    P = 2^(c*S - mc),  l += rowsum(P),  O += P.V          (mc = c*m)
+
+and, only when some p of a sub-tile would exceed the trigger, a slow path
+that moves m to the row max, rescales O and l by 2^(mc_old - mc_new) and
+redoes the sub-tile.  At the end O / l and LSE = ln2*(mc + log2 l).
+
+Organisation (per workgroup: 512 query rows of one (batch, q-head) against
+the visible keys of its kv-head, in tiles of 64 keys):
+
+* Eight waves, two per SIMD (waves w and w+4 share one).  Wave w owns the
+  32-row query blocks w and 15-w of the 512-row tile (a causal diagonal then
+  costs every wave about the same), 64 rows in all: O^T (128 AGPRs) and Q
+  (64 AGPRs) stay in registers, 64 VGPRs hold S/P (32), a ring of three MFMA
+  operand buffers (12) and the rest.
+* Each wave alternates an MFMA phase (P.V of sub-tile j-1 then S^T = K.Q^T
+  of sub-tile j: 32 MFMAs, operands streamed from LDS through the ring) and
+  a softmax phase (exponentials, row sums, conversion of P, in place).
+  Waves 4-7 run one phase behind waves 0-3, with one s_barrier per phase,
+  so on every SIMD one wave's MFMAs overlap the other wave's softmax.
+* K and V tiles go HBM -> LDS by buffer_load ... lds, three tiles ahead,
+  through four K slots and four V slots (128 KB); each wave moves 8 rows of
+  each tile.  Tile u is needed from global phase 4u and freed after phase
+  4u+5; its loads are issued in phase 4u-9 (4u-8 for waves 4-7).
+* S and P share registers: P (the input dtype) is converted over the first
+  half of S, and the next S^T overwrites it only after the P.V MFMAs that
+  read it have issued.  The slow path therefore recomputes S^T from the K
+  tile, which is still resident.
+* Persistent schedule as in the four-wave kernel: workgroup g takes items
+  r*G + (g or G-1-g) of the longest-first (batch, q-head, q-tile) list.
+"""
+from __future__ import annotations
+
+import math
+
+from .regs import Alloc, Emitter
+from .fa_fwd_gen import LN2, f32_hex
+
+BM = 512          # query rows per workgroup
+BN = 64           # keys per tile
+WAVES = 8
+SLOTS = 4         # K (and V) tiles held in LDS
+AHEAD = 3         # tiles whose loads are in flight ahead of the tile in use
+THRESH = 32768.0  # slow-path trigger: a lane's 16-key partial row sum above 2^15
+
+
+def kernel_name(dtype: str) -> str:
+    return f"fa_fwd_{dtype}_d128_x8_gfx950"
+
+
+class Gen8:
+    D = 128
+
+    def __init__(self, dtype: str):
+        assert dtype in ("bf16", "f16")
+        self.dtype = dtype
+        self.name = kernel_name(dtype)
+        self.mfma_op = "v_mfma_f32_32x32x16_bf16" if dtype == "bf16" else "v_mfma_f32_32x32x16_f16"
+        self.cvt_op = "v_cvt_pk_bf16_f32" if dtype == "bf16" else "v_cvt_pk_f16_f32"
+        D = self.D
+        self.NS = D // 16             # k-steps of S^T
+        self.NDB = D // 32            # 32-dim blocks of O^T
+        self.ROW = D * 2              # bytes per K/V row in LDS
+        self.TILE = BN * self.ROW     # bytes per K or V tile (16 KB)
+        self.CH = D // 8              # 16-byte chunks per row
+        self.RPD = 64 // self.CH      # rows per 64-lane DMA instruction
+        self.DPW = (BN // WAVES) // self.RPD  # DMA instructions per wave per K (or V) tile
+        self.KREG = 0
+        self.VREG = SLOTS * self.TILE
+        self.LDS = 2 * SLOTS * self.TILE
+        assert self.VREG == 65536 and self.DPW == 2
+        self.em = Emitter()
+        self._lab = 0
+        self.deferred = []
+
+    def lab(self, tag):
+        self._lab += 1
+        return f".L{self.dtype}x8_{tag}_{self._lab}"
+
+    # ------------------------------------------------------------------------
+    def alloc(self):
+        V = Alloc("v", 0, 64)
+        A = Alloc("a", 0, 192)
+        S = Alloc("s", 28, 102)
+        r = self.__dict__
+        r["v_lane"] = V.take("lane", 1)        # v0: lane id (after kernel_setup)
+        r["v_klane"] = V.take("klane", 1)      # K operand address of k-step 0, slot 0
+        r["v_vlane"] = V.take("vlane", 1)      # V operand address of d-block 0, slot 0
+        r["v_kb"] = V.take("kb", 1)            # K operand base of the tile in S^T
+        r["v_S"] = [V.take(f"S{q}", 16, 4) for q in range(2)]
+        r["v_R"] = [V.take(f"R{i}", 4, 4) for i in range(3)]
+        r["v_vb"] = V.take("vb", 1)            # V operand base of the tile in P.V
+        r["v_kdma"] = V.take("kdma", self.DPW)
+        r["v_vdma"] = V.take("vdma", self.DPW)
+        r["v_mc"] = V.take("mc", 2)            # c * m per query block (0 while m = -inf)
+        r["v_l"] = V.take("l", 2)              # per-lane partial row sums
+        r["v_rs"] = V.take("rs", 2)            # partial row sums of the current sub-tile
+        r["v_t"] = V.take("tmp", 5)
+        self.nvgpr = 64
+        assert V.next <= 64, V.next
+        r["a_O"] = [[A.take(f"O{q}{d}", 16, 4) for d in range(self.NDB)] for q in range(2)]
+        r["a_Q"] = [[A.take(f"Q{q}{s}", 4, 4) for s in range(self.NS)] for q in range(2)]
+        self.nagpr = 192
+        assert A.next == 192
+        t = S.take
+        r["s_hq"], r["s_qt"], r["s_b"], r["s_hk"] = t("hq", 1), t("qt", 1), t("b", 1), t("hk", 1)
+        r["s_w"], r["s_q0"], r["s_off"], r["s_ntiles"] = t("w", 1), t("q0", 1), t("off", 1), t("nt", 1)
+        r["s_kvfull"], r["s_rowlim"], r["s_rowb"], r["s_u"] = t("kvf", 1), t("rowlim", 1), t("rowb", 1), t("u", 1)
+        r["s_rb"] = [t("rb0", 1), t("rb1", 1)]
+        r["s_ro"] = t("ro", 4, 4)
+        r["s_rl"] = t("rl", 4, 4)
+        r["s_rk"] = t("rk", 4, 4)
+        r["s_rq"] = r["s_rk"]                  # Q loads are issued before the first K descriptor
+        r["s_rv"] = t("rv", 4, 4)
+        r["s_g"], r["s_r"] = t("wg", 1), t("round", 1)
+        r["s_nitems"], r["s_P"] = t("nitems", 1), t("pairs", 1)
+        r["s_kbase"] = t("kbase", 2, 2)
+        r["s_vbase"] = t("vbase", 2, 2)
+        r["s_k0"] = t("k0", 1)                 # first key of the current softmax sub-tile
+        r["s_kdw"], r["s_vdw"], r["s_wrow"] = t("kdw", 1), t("vdw", 1), t("wrow", 1)
+        r["s_x"] = [t(f"x{i}", 1) for i in range(6)]
+        r["s_y"] = [t(f"y{i}", 1) for i in range(6)]
+        r["s_m1"], r["s_m2"] = t("msk1", 2, 2), t("msk2", 2, 2)
+        r["s_or"] = t("orpair", 2, 2)
+        r["s_neg"] = t("neginf", 1)
+        r["s_thr"] = t("thr", 1)
+        r["s_row"] = t("row", 1)
+        self.nsgpr = S.next
+
+    # ------------------------------------------------------------------------
+    # set-up
+    # ------------------------------------------------------------------------
+    def kernel_setup(self):
+        em, D = self.em, self.D
+        em.salu("s_load_dwordx16 s[8:23], s[0:1], 0x0")
+        em.salu("s_load_dwordx4 s[24:27], s[0:1], 0x40")
+        em.valu(f"v_readfirstlane_b32 {self.s_w}, v0", src=["v0"])
+        em.salu(f"s_lshr_b32 {self.s_w}, {self.s_w}, 6")
+        em.valu("v_and_b32 v0, 63, v0", dst=["v0"], src=["v0"])
+        em.salu(f"s_mov_b32 {self.s_g}, s2")
+        em.salu(f"s_mov_b32 {self.s_r}, 0")
+        em.salu("s_waitcnt lgkmcnt(0)")
+        em.salu(f"s_mov_b32 {self.s_neg}, 0xff800000")
+        em.salu(f"s_mov_b32 {self.s_thr}, {f32_hex(THRESH)}")
+        em.salu(f"s_mov_b32 {self.s_row}, {self.ROW}")
+        em.salu(f"s_mul_i32 {self.s_rowb}, s22, {D * 2}")          # K/V row stride
+        em.salu(f"s_mul_i32 {self.s_P}, s18, s21")                 # (batch, head) pairs
+        em.salu(f"s_and_b32 {self.s_x[0]}, s25, 0xffff")           # query tiles
+        em.salu(f"s_mul_i32 {self.s_nitems}, {self.s_P}, {self.s_x[0]}")
+        em.salu(f"s_mul_i32 {self.s_wrow}, {self.s_w}, {(BN // WAVES) * self.ROW}")
+
+    def tmps(self):
+        """Scratch VGPRs for set-up code (the S registers are free then)."""
+        return [self.v_S[i // 16].r(i % 16) for i in range(32)]
+
+    def emit_div(self, num, den, q, rem, t):
+        """q = num / den, rem = num - q*den for num, den < 2^24 (VGPR num,
+        SGPR den): float reciprocal estimate, then one correction each way."""
+        em = self.em
+        dv, z = t[0], t[1]
+        em.valu(f"v_mov_b32 {dv}, {den}", dst=[dv])
+        em.valu(f"v_cvt_f32_u32 {q}, {num}", dst=[q], src=[num])
+        em.valu(f"v_cvt_f32_u32 {rem}, {dv}", dst=[rem], src=[dv])
+        em.valu(f"v_rcp_f32 {rem}, {rem}", dst=[rem], src=[rem], trans=True)
+        em.valu(f"v_mul_f32 {q}, {q}, {rem}", dst=[q], src=[q, rem])
+        em.valu(f"v_cvt_u32_f32 {q}, {q}", dst=[q], src=[q])
+        em.valu(f"v_mul_lo_u32 {rem}, {q}, {dv}", dst=[rem], src=[q, dv])
+        em.valu(f"v_sub_u32 {rem}, {num}, {rem}", dst=[rem], src=[num, rem])
+        em.valu(f"v_cmp_gt_i32 vcc, 0, {rem}", src=[rem])
+        em.valu(f"v_cndmask_b32 {z}, 0, -1, vcc", dst=[z])
+        em.valu(f"v_add_u32 {q}, {q}, {z}", dst=[q], src=[q, z])
+        em.valu(f"v_cndmask_b32 {z}, 0, {dv}, vcc", dst=[z], src=[dv])
+        em.valu(f"v_add_u32 {rem}, {rem}, {z}", dst=[rem], src=[rem, z])
+        em.valu(f"v_cmp_le_u32 vcc, {dv}, {rem}", src=[rem, dv])
+        em.valu(f"v_cndmask_b32 {z}, 0, 1, vcc", dst=[z])
+        em.valu(f"v_add_u32 {q}, {q}, {z}", dst=[q], src=[q, z])
+        em.valu(f"v_cndmask_b32 {z}, 0, {dv}, vcc", dst=[z], src=[dv])
+        em.valu(f"v_sub_u32 {rem}, {rem}, {z}", dst=[rem], src=[rem, z])
+
+    def lane_consts(self):
+        """Per-lane DMA source offsets and LDS operand addresses."""
+        em, D = self.em, self.D
+        t = self.tmps()
+        lane = "v0"
+        l32, h = t[0], t[1]
+        em.valu(f"v_and_b32 {l32}, 31, {lane}", dst=[l32], src=[lane])
+        em.valu(f"v_lshrrev_b32 {h}, 5, {lane}", dst=[h], src=[lane])
+        # DMA: row r = 8w + RPD*i + lane/CH of the tile, LDS chunk p = lane % CH
+        # holds row chunk p ^ swz(r) (K: r & 15, V: 4*(r & 3))
+        CH = self.CH
+        em.valu(f"v_lshrrev_b32 {t[2]}, {int(math.log2(CH))}, {lane}", dst=[t[2]], src=[lane])
+        em.valu(f"v_and_b32 {t[3]}, {CH - 1}, {lane}", dst=[t[3]], src=[lane])
+        em.salu(f"s_lshl_b32 {self.s_x[0]}, {self.s_w}, 3")
+        em.valu(f"v_add_u32 {t[2]}, {self.s_x[0]}, {t[2]}", dst=[t[2]], src=[t[2]])
+        for i in range(self.DPW):
+            r_, off, sw = t[4], t[5], t[6]
+            em.valu(f"v_add_u32 {r_}, {self.RPD * i}, {t[2]}", dst=[r_], src=[t[2]])
+            em.valu(f"v_mul_lo_u32 {off}, {r_}, {self.s_rowb}", dst=[off], src=[r_])
+            em.valu(f"v_and_b32 {sw}, 15, {r_}", dst=[sw], src=[r_])
+            em.valu(f"v_xor_b32 {sw}, {sw}, {t[3]}", dst=[sw], src=[sw, t[3]])
+            em.valu(f"v_lshl_add_u32 {self.v_kdma.r(i)}, {sw}, 4, {off}", dst=[self.v_kdma.r(i)], src=[sw, off])
+            em.valu(f"v_and_b32 {sw}, 3, {r_}", dst=[sw], src=[r_])
+            em.valu(f"v_lshlrev_b32 {sw}, 2, {sw}", dst=[sw], src=[sw])
+            em.valu(f"v_xor_b32 {sw}, {sw}, {t[3]}", dst=[sw], src=[sw, t[3]])
+            em.valu(f"v_lshl_add_u32 {self.v_vdma.r(i)}, {sw}, 4, {off}", dst=[self.v_vdma.r(i)], src=[sw, off])
+        # K operand of k-step s: l32*ROW + 16*((2s + h) ^ (l32 & 15)) = klane ^ (s << 5)
+        em.valu(f"v_and_b32 {t[2]}, 15, {l32}", dst=[t[2]], src=[l32])
+        em.valu(f"v_xor_b32 {t[2]}, {t[2]}, {h}", dst=[t[2]], src=[t[2], h])
+        em.valu(f"v_mul_u32_u24 {t[3]}, {self.ROW}, {l32}", dst=[t[3]], src=[l32])
+        em.valu(f"v_lshl_add_u32 {self.v_klane}, {t[2]}, 4, {t[3]}", dst=[str(self.v_klane)], src=[t[2], t[3]])
+        # V operand of d-block db (transposing reads): tr_i = lane & 15,
+        # tr_row = 4h + (tr_i >> 2), chunk (4db + 2*((lane >> 4) & 1) + ((lane >> 1) & 1))
+        # ^ 4*(tr_row & 3), byte 8*(lane & 1):  vlane ^ (db << 6)
+        em.valu(f"v_bfe_u32 {t[2]}, {lane}, 2, 2", dst=[t[2]], src=[lane])
+        em.valu(f"v_lshl_add_u32 {t[2]}, {h}, 2, {t[2]}", dst=[t[2]], src=[h, t[2]])       # tr_row
+        em.valu(f"v_and_b32 {t[3]}, 3, {t[2]}", dst=[t[3]], src=[t[2]])
+        em.valu(f"v_lshlrev_b32 {t[3]}, 2, {t[3]}", dst=[t[3]], src=[t[3]])                # sw
+        em.valu(f"v_bfe_u32 {t[4]}, {lane}, 4, 1", dst=[t[4]], src=[lane])
+        em.valu(f"v_bfe_u32 {t[5]}, {lane}, 1, 1", dst=[t[5]], src=[lane])
+        em.valu(f"v_lshl_add_u32 {t[4]}, {t[4]}, 1, {t[5]}", dst=[t[4]], src=[t[4], t[5]])
+        em.valu(f"v_xor_b32 {t[4]}, {t[4]}, {t[3]}", dst=[t[4]], src=[t[4], t[3]])
+        em.valu(f"v_and_b32 {t[5]}, 1, {lane}", dst=[t[5]], src=[lane])
+        em.valu(f"v_lshlrev_b32 {t[5]}, 3, {t[5]}", dst=[t[5]], src=[t[5]])
+        em.valu(f"v_mad_u32_u24 {t[5]}, {t[2]}, {self.s_row}, {t[5]}", dst=[t[5]], src=[t[2], t[5]])
+        em.valu(f"v_lshl_add_u32 {t[5]}, {t[4]}, 4, {t[5]}", dst=[t[5]], src=[t[4], t[5]])
+        em.valu(f"v_add_u32 {self.v_vlane}, {self.VREG}, {t[5]}", dst=[str(self.v_vlane)], src=[t[5]])
+
+    def item_setup(self, l_exit):
+        """Decode this round's item; rows, key range, thresholds, resources."""
+        em, D = self.em, self.D
+        x = self.s_x
+        t = self.tmps()
+        em.salu(f"s_lshr_b32 {x[1]}, s25, 16")                     # G
+        em.salu(f"s_mul_i32 {x[0]}, {self.s_r}, {x[1]}")
+        em.salu(f"s_sub_u32 {x[2]}, {x[1]}, 1")
+        em.salu(f"s_sub_u32 {x[2]}, {x[2]}, {self.s_g}")
+        em.salu(f"s_bitcmp1_b32 {self.s_r}, 0")
+        em.salu(f"s_cselect_b32 {x[2]}, {x[2]}, {self.s_g}")
+        em.salu(f"s_add_u32 {x[0]}, {x[0]}, {x[2]}")                # idx
+        em.salu(f"s_cmp_ge_u32 {x[0]}, {self.s_nitems}")
+        em.salu(f"s_cbranch_scc1 {l_exit}")
+        em.valu(f"v_mov_b32 {t[2]}, {x[0]}", dst=[t[2]])
+        self.emit_div(t[2], self.s_P, t[3], t[4], t[8:10])
+        self.emit_div(t[4], "s21", t[5], t[6], t[8:10])
+        em.valu(f"v_readfirstlane_b32 {x[3]}, {t[3]}", src=[t[3]])       # level
+        em.valu(f"v_readfirstlane_b32 {self.s_b}, {t[5]}", src=[t[5]])   # b
+        em.valu(f"v_readfirstlane_b32 {x[4]}, {t[6]}", src=[t[6]])       # head slot
+        # hq: contiguous head groups over the 8 XCDs
+        em.salu("s_cmp_eq_u32 s27, 0")
+        em.salu(f"s_cselect_b32 {x[5]}, 0, 7")
+        em.salu(f"s_and_b32 {self.s_hq}, {x[4]}, {x[5]}")
+        em.salu(f"s_mul_i32 {self.s_hq}, {self.s_hq}, s27")
+        em.salu("s_cmp_eq_u32 s27, 0")
+        em.salu(f"s_cselect_b32 {x[5]}, 0, 3")
+        em.salu(f"s_lshr_b32 {x[5]}, {x[4]}, {x[5]}")
+        em.salu(f"s_add_u32 {self.s_hq}, {self.s_hq}, {x[5]}")
+        # query tile: longest causal tiles first
+        em.salu(f"s_and_b32 {x[5]}, s25, 0xffff")
+        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, 1")
+        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, {x[3]}")
+        em.salu("s_cmp_eq_u32 s23, 0")
+        em.salu(f"s_cselect_b32 {self.s_qt}, {x[3]}, {x[5]}")
+        em.salu(f"s_mul_i32 {self.s_hk}, {self.s_hq}, s26")
+        em.salu(f"s_lshr_b32 {self.s_hk}, {self.s_hk}, 20")
+        # rows: q0 = 512 qt; blocks w and 15-w of 32 rows
+        em.salu(f"s_lshl_b32 {self.s_q0}, {self.s_qt}, 9")
+        em.salu(f"s_lshl_b32 {x[0]}, {self.s_w}, 5")
+        em.salu(f"s_add_u32 {self.s_rb[0]}, {self.s_q0}, {x[0]}")
+        em.salu(f"s_sub_u32 {self.s_rb[1]}, {self.s_q0}, {x[0]}")
+        em.salu(f"s_add_u32 {self.s_rb[1]}, {self.s_rb[1]}, {32 * 15}")
+        em.salu(f"s_sub_i32 {self.s_off}, s20, s19")              # Skv - Sq
+        # key tiles: kv_end = causal ? min(Skv, min(q0 + 512, Sq) + off) : Skv
+        em.salu(f"s_add_u32 {x[0]}, {self.s_q0}, {BM}")
+        em.salu(f"s_min_i32 {x[0]}, {x[0]}, s19")
+        em.salu(f"s_add_i32 {x[0]}, {x[0]}, {self.s_off}")
+        em.salu(f"s_min_i32 {x[0]}, {x[0]}, s20")
+        em.salu("s_cmp_eq_u32 s23, 0")
+        em.salu(f"s_cselect_b32 {x[0]}, s20, {x[0]}")
+        em.salu(f"s_max_i32 {x[0]}, {x[0]}, 0")
+        em.salu(f"s_add_u32 {x[0]}, {x[0]}, {BN - 1}")
+        em.salu(f"s_lshr_b32 {self.s_ntiles}, {x[0]}, 6")
+        em.salu(f"s_lshl_b32 {x[0]}, {self.s_ntiles}, 6")
+        em.salu(f"s_min_u32 {self.s_rowlim}, {x[0]}, s20")
+        # keys below kv_full are visible to every row of the wave (its lowest
+        # row is the first of block 0)
+        em.salu(f"s_add_i32 {x[0]}, {self.s_rb[0]}, {self.s_off}")
+        em.salu(f"s_add_i32 {x[0]}, {x[0]}, 1")
+        em.salu(f"s_min_i32 {x[0]}, {x[0]}, s20")
+        em.salu("s_cmp_eq_u32 s23, 0")
+        em.salu(f"s_cselect_b32 {self.s_kvfull}, s20, {x[0]}")
+        # K/V batch/head bases (bytes)
+        em.salu(f"s_mul_i32 {x[0]}, {self.s_b}, s20")
+        em.salu(f"s_mul_i32 {x[2]}, {x[0]}, {self.s_rowb}")
+        em.salu(f"s_mul_hi_u32 {x[3]}, {x[0]}, {self.s_rowb}")
+        em.salu(f"s_mul_i32 {x[4]}, {self.s_hk}, {D * 2}")
+        em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[4]}")
+        em.salu(f"s_addc_u32 {x[3]}, {x[3]}, 0")
+        em.salu(f"s_add_u32 {self.s_kbase.r(0)}, s10, {x[2]}")
+        em.salu(f"s_addc_u32 {self.s_kbase.r(1)}, s11, {x[3]}")
+        em.salu(f"s_add_u32 {self.s_vbase.r(0)}, s12, {x[2]}")
+        em.salu(f"s_addc_u32 {self.s_vbase.r(1)}, s13, {x[3]}")
+        self.emit_qo_desc(self.s_rq, 8)
+
+    def emit_qo_desc(self, rs, base):
+        """Q (base s8) or O (base s14) buffer resource of the item."""
+        em, D, x = self.em, self.D, self.s_x
+        em.salu(f"s_mul_i32 {x[0]}, s19, s21")
+        em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, {x[0]}")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
+        em.salu(f"s_mul_i32 {x[2]}, {x[4]}, {D * 2}")
+        em.salu(f"s_mul_hi_u32 {x[3]}, {x[4]}, {D * 2}")
+        em.salu(f"s_sub_u32 {x[5]}, {x[0]}, {self.s_hq}")
+        em.salu(f"s_mul_i32 {x[5]}, {x[5]}, {D * 2}")
+        em.salu(f"s_add_u32 {rs.r(0)}, s{base}, {x[2]}")
+        em.salu(f"s_addc_u32 {rs.r(1)}, s{base + 1}, {x[3]}")
+        em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
+        em.salu(f"s_mov_b32 {rs.r(2)}, {x[5]}")
+        em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
+
+    def out_desc(self):
+        """O and LSE buffer resources of the item."""
+        em, x = self.em, self.s_x
+        self.emit_qo_desc(self.s_ro, 14)
+        em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, s21")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
+        em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s19")
+        em.salu(f"s_mul_i32 {x[2]}, {x[4]}, 4")
+        em.salu(f"s_mul_hi_u32 {x[3]}, {x[4]}, 4")
+        em.salu(f"s_add_u32 {self.s_rl.r(0)}, s16, {x[2]}")
+        em.salu(f"s_addc_u32 {self.s_rl.r(1)}, s17, {x[3]}")
+        em.salu(f"s_and_b32 {self.s_rl.r(1)}, {self.s_rl.r(1)}, 0xffff")
+        em.salu(f"s_lshl_b32 {self.s_rl.r(2)}, s19, 2")
+        em.salu(f"s_mov_b32 {self.s_rl.r(3)}, 0x20000")
+        em.salu(f"s_or_b32 {x[0]}, s16, s17")
+        em.salu(f"s_cmp_eq_u32 {x[0]}, 0")
+        em.salu(f"s_cselect_b32 {self.s_rl.r(2)}, 0, {self.s_rl.r(2)}")
+
+    def row_of_block(self, qb, dst):
+        """dst = query row of this lane in block qb (rb + lane % 32)."""
+        em = self.em
+        em.valu(f"v_and_b32 {dst}, 31, v0", dst=[dst], src=["v0"])
+        em.valu(f"v_add_u32 {dst}, {self.s_rb[qb]}, {dst}", dst=[dst], src=[dst])
+
+    def load_q(self):
+        """The wave's 64 Q rows straight into the Q AGPRs."""
+        em = self.em
+        t = self.tmps()
+        em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {self.D * 2}")
+        em.valu(f"v_lshrrev_b32 {t[4]}, 5, v0", dst=[t[4]], src=["v0"])
+        em.valu(f"v_lshlrev_b32 {t[4]}, 4, {t[4]}", dst=[t[4]], src=[t[4]])
+        for qb in range(2):
+            self.row_of_block(qb, t[0])
+            em.valu(f"v_mul_lo_u32 {t[5 + qb]}, {t[0]}, {self.s_x[0]}", dst=[t[5 + qb]], src=[t[0]])
+            em.valu(f"v_add_u32 {t[5 + qb]}, {t[5 + qb]}, {t[4]}", dst=[t[5 + qb]], src=[t[5 + qb], t[4]])
+        for qb in range(2):
+            for s in range(self.NS):
+                dst = str(self.a_Q[qb][s])
+                em.vmem_load_to(f"buffer_load_dwordx4 {dst}, {t[5 + qb]}, {self.s_rq}, 0 offen offset:{32 * s}",
+                                dst, src=[t[5 + qb]])
+
+    # ------------------------------------------------------------------------
+    # K/V DMA
+    # ------------------------------------------------------------------------
+    def emit_dma_desc(self, tile):
+        """Buffer resources s_rk / s_rv of the tile index in sgpr `tile`:
+        base = head base + 64*tile*rowb, size = the bytes up to row_lim."""
+        em, y, rb = self.em, self.s_y, self.s_rowb
+        em.salu(f"s_lshl_b32 {y[0]}, {tile}, 6")
+        em.salu(f"s_sub_i32 {y[1]}, {self.s_rowlim}, {y[0]}")
+        em.salu(f"s_max_i32 {y[1]}, {y[1]}, 0")
+        em.salu(f"s_mul_i32 {y[2]}, {y[1]}, {rb}")
+        em.salu(f"s_mul_hi_u32 {y[3]}, {y[1]}, {rb}")
+        em.salu(f"s_cmp_eq_u32 {y[3]}, 0")
+        em.salu(f"s_cselect_b32 {y[2]}, {y[2]}, 0x7fffffff")
+        em.salu(f"s_min_u32 {y[2]}, {y[2]}, 0x7fffffff")
+        em.salu(f"s_mul_i32 {y[3]}, {y[0]}, {rb}")
+        em.salu(f"s_mul_hi_u32 {y[4]}, {y[0]}, {rb}")
+        for rs, bb in ((self.s_rk, self.s_kbase), (self.s_rv, self.s_vbase)):
+            em.salu(f"s_add_u32 {rs.r(0)}, {bb.r(0)}, {y[3]}")
+            em.salu(f"s_addc_u32 {rs.r(1)}, {bb.r(1)}, {y[4]}")
+            em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
+            em.salu(f"s_mov_b32 {rs.r(2)}, {y[2]}")
+            em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
+
+    def emit_dma(self, tile):
+        """Issue the wave's 2 K and 2 V row loads of tile index `tile` (sgpr)
+        into LDS slot tile % SLOTS."""
+        em, y = self.em, self.s_y
+        self.emit_dma_desc(tile)
+        em.salu(f"s_and_b32 {y[5]}, {tile}, {SLOTS - 1}")
+        em.salu(f"s_mul_i32 {y[5]}, {y[5]}, {self.TILE}")
+        em.salu(f"s_add_u32 {self.s_kdw}, {y[5]}, {self.s_wrow}")
+        em.salu(f"s_add_u32 {self.s_vdw}, {self.s_kdw}, {self.VREG}")
+        for desc, slot, voff in ((self.s_rk, self.s_kdw, self.v_kdma), (self.s_rv, self.s_vdw, self.v_vdma)):
+            for i in range(self.DPW):
+                em.salu(f"s_add_u32 m0, {slot}, {self.RPD * i * self.ROW}")
+                em.vmem(f"buffer_load_dwordx4 {voff.r(i)}, {desc}, 0 offen lds", src=[voff.r(i)])
+
+    # ------------------------------------------------------------------------
+    # operand fragments and the MFMA phase
+    # ------------------------------------------------------------------------
+    def frag_v(self, kb, db, th):
+        """V^T fragment (dims 32db.., keys 16th.. of sub-tile kb of the V tile
+        at v_vb): two transposing reads.  Returns (reads(buf, tmp), mfmas(buf))."""
+        em = self.em
+
+        def reads(buf, tmp):
+            R = self.v_R[buf]
+            em.valu(f"v_xor_b32 {tmp}, {db << 6}, {self.v_vb}", dst=[tmp], src=[str(self.v_vb)])
+            for e in range(2):
+                off = (32 * kb + 16 * th + 8 * e) * self.ROW
+                em.ds_read(f"ds_read_b64_tr_b16 {R.r(2 * e, 2)}, {tmp} offset:{off}", R.r(2 * e, 2), tmp)
+        return reads, ("v", db, th)
+
+    def frag_k(self, kb, s):
+        """K fragment (keys of sub-tile kb of the K tile at v_kb, dims 16s..)."""
+        em = self.em
+
+        def reads(buf, tmp):
+            R = self.v_R[buf]
+            em.valu(f"v_xor_b32 {tmp}, {s << 5}, {self.v_kb}", dst=[tmp], src=[str(self.v_kb)])
+            em.ds_read(f"ds_read_b128 {R}, {tmp} offset:{kb * 32 * self.ROW}", str(R), tmp)
+        return reads, ("k", s)
+
+    def frag_mfma(self, tag, buf, qb, first_pv=False):
+        em = self.em
+        R = str(self.v_R[buf])
+        if tag[0] == "v":
+            _, db, th = tag
+            o = str(self.a_O[qb][db])
+            c = "0" if (first_pv and th == 0) else o
+            em.mfma(self.mfma_op, o, R, self.v_S[qb].r(4 * th, 4), c)
+        else:
+            _, s = tag
+            d = str(self.v_S[qb])
+            em.mfma(self.mfma_op, d, R, str(self.a_Q[qb][s]), "0" if s == 0 else d)
+
+    def pv_frags(self, kb):
+        return [self.frag_v(kb, db, th) for db in range(self.NDB) for th in range(2)]
+
+    def qk_frags(self, kb):
+        return [self.frag_k(kb, s) for s in range(self.NS)]
+
+    def prefetch(self, frags):
+        """Reads of the first two fragments of the next MFMA phase (buffers 0, 1)."""
+        t = self.v_t
+        for i in range(min(2, len(frags))):
+            frags[i][0](i, t.r(i))
+
+    def m_phase(self, frags, first_pv=False):
+        """MFMAs of the fragments in order, both query blocks per fragment;
+        fragments 0 and 1 are already in flight; fragment i+2 is read into
+        the buffer of fragment i-1 after the first MFMA of fragment i."""
+        t = self.v_t
+        n = len(frags)
+        for i, (reads, tag) in enumerate(frags):
+            buf = i % 3
+            self.frag_mfma(tag, buf, 0, first_pv)
+            if i + 2 < n:
+                frags[i + 2][0]((i + 2) % 3, t.r((i + 2) % 2))
+            self.frag_mfma(tag, buf, 1, first_pv)
+
+    # ------------------------------------------------------------------------
+    # softmax phase
+    # ------------------------------------------------------------------------
+    def emit_mask(self):
+        """S entries of keys past each row's last visible key -> -inf.
+        Register i of a block holds key k0 + 8*(i >> 2) + 4h + (i & 3); the
+        last visible key is min(row + off, Skv - 1) (causal) or Skv - 1."""
+        em = self.em
+        t = self.v_t
+        d, h4, ninf = t.r(0), t.r(1), t.r(2)
+        x = self.s_x
+        em.valu(f"v_lshrrev_b32 {h4}, 5, v0", dst=[h4], src=["v0"])
+        em.valu(f"v_lshlrev_b32 {h4}, 2, {h4}", dst=[h4], src=[h4])          # 4h
+        em.salu(f"s_sub_i32 {x[1]}, s20, 1")                                  # Skv - 1
+        em.salu("s_cmp_eq_u32 s23, 0")
+        em.salu(f"s_cselect_b32 {x[2]}, s20, {self.s_off}")                  # row offset of the limit
+        em.valu(f"v_mov_b32 {ninf}, {self.s_neg}", dst=[ninf])
+        for qb in range(2):
+            S = self.v_S[qb]
+            self.row_of_block(qb, d)
+            em.valu(f"v_add_u32 {d}, {x[2]}, {d}", dst=[d], src=[d])
+            em.valu(f"v_min_i32 {d}, {x[1]}, {d}", dst=[d], src=[d])
+            em.valu(f"v_sub_u32 {d}, {d}, {h4}", dst=[d], src=[d, h4])
+            em.valu(f"v_subrev_u32 {d}, {self.s_k0}, {d}", dst=[d], src=[d])
+            for i in range(16):
+                ci = 8 * (i >> 2) + (i & 3)
+                em.valu(f"v_cmp_lt_i32 vcc, {d}, {ci}", src=[d])
+                em.valu(f"v_cndmask_b32 {S.r(i)}, {S.r(i)}, {ninf}, vcc", dst=[S.r(i)], src=[S.r(i), ninf])
+
+    def emit_rowmax_init(self):
+        """First sub-tile: mc = c * rowmax (0 for rows with every key masked)."""
+        em = self.em
+        t = self.v_t
+        for qb in range(2):
+            S, mx, tmp = self.v_S[qb], t.r(0), t.r(1)
+            em.valu(f"v_max3_f32 {mx}, {S.r(0)}, {S.r(1)}, {S.r(2)}", dst=[mx], src=[S.r(0), S.r(1), S.r(2)])
+            for i in range(3, 15, 2):
+                em.valu(f"v_max3_f32 {mx}, {mx}, {S.r(i)}, {S.r(i + 1)}", dst=[mx], src=[mx, S.r(i), S.r(i + 1)])
+            em.valu(f"v_max_f32 {mx}, {mx}, {S.r(15)}", dst=[mx], src=[mx, S.r(15)])
+            em.valu(f"v_mov_b32 {tmp}, {mx}", dst=[tmp], src=[mx])
+            em.valu(f"v_permlane32_swap_b32 {mx}, {tmp}", dst=[mx, tmp], src=[mx, tmp])
+            em.valu(f"v_max_f32 {mx}, {mx}, {tmp}", dst=[mx], src=[mx, tmp])
+            mc = self.v_mc.r(qb)
+            em.valu(f"v_mul_f32 {mc}, s24, {mx}", dst=[mc], src=[mx])
+            em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {mx}", src=[mx])
+            em.valu(f"v_cndmask_b32 {mc}, {mc}, 0, vcc", dst=[mc], src=[mc])
+
+    def softmax_ops(self):
+        """In place: S = 2^(c*S - mc); rs = lane sums per block; P = S rounded
+        (over the first 8 registers of each block); the trigger masks."""
+        em = self.em
+        out = []
+        E = []
+        for qb in range(2):
+            S, mc = self.v_S[qb], self.v_mc.r(qb)
+            e = []
+            for c4 in range(4):
+                for i in range(4 * c4, 4 * c4 + 4):
+                    e.append(lambda S=S, mc=mc, i=i: em.valu(
+                        f"v_fma_f32 {S.r(i)}, {S.r(i)}, s24, -{mc}", dst=[S.r(i)], src=[S.r(i), mc]))
+                for i in range(4 * c4, 4 * c4 + 4):
+                    e.append(lambda S=S, i=i: em.valu(
+                        f"v_exp_f32 {S.r(i)}, {S.r(i)}", dst=[S.r(i)], src=[S.r(i)], trans=True))
+            E.append(e)
+        # sums: two chains per block (rs and a temp), folded at the end
+        Ssum = []
+        for qb in range(2):
+            S, ra, rb = self.v_S[qb], self.v_rs.r(qb), self.v_t.r(qb)
+            s = [lambda S=S, ra=ra: em.valu(f"v_add_f32 {ra}, {S.r(0)}, {S.r(1)}", dst=[ra], src=[S.r(0), S.r(1)]),
+                 lambda S=S, rb=rb: em.valu(f"v_add_f32 {rb}, {S.r(2)}, {S.r(3)}", dst=[rb], src=[S.r(2), S.r(3)])]
+            for i in range(4, 16):
+                acc = ra if i % 2 == 0 else rb
+                s.append(lambda S=S, acc=acc, i=i: em.valu(
+                    f"v_add_f32 {acc}, {acc}, {S.r(i)}", dst=[acc], src=[acc, S.r(i)]))
+            s.append(lambda ra=ra, rb=rb: em.valu(f"v_add_f32 {ra}, {ra}, {rb}", dst=[ra], src=[ra, rb]))
+            Ssum.append(s)
+        # order: exponentials of both blocks chunk by chunk, the sums of a
+        # chunk one chunk later
+        for c4 in range(4):
+            for qb in range(2):
+                out += E[qb][8 * c4:8 * c4 + 8]
+            if c4 >= 1:
+                for qb in range(2):
+                    out += Ssum[qb][4 * (c4 - 1):4 * c4]
+        for qb in range(2):
+            out += Ssum[qb][12:]
+        for qb, msk in ((0, self.s_m1), (1, self.s_m2)):
+            out.append(lambda qb=qb, msk=msk: em.valu(
+                f"v_cmp_lt_f32 {msk}, {self.s_thr}, {self.v_rs.r(qb)}", src=[self.v_rs.r(qb)]))
+        for qb in range(2):
+            S = self.v_S[qb]
+            for k in range(8):
+                lo, hi = S.r(2 * k), S.r(2 * k + 1)
+                out.append(lambda S=S, k=k, lo=lo, hi=hi: em.valu(
+                    f"{self.cvt_op} {S.r(k)}, {lo}, {hi}", dst=[S.r(k)], src=[lo, hi]))
+        return out
+
+    def emit_softmax(self):
+        for f in self.softmax_ops():
+            f()
+
+    def emit_l(self, first=False):
+        em = self.em
+        for qb in range(2):
+            l, rs = self.v_l.r(qb), self.v_rs.r(qb)
+            if first:
+                em.valu(f"v_mov_b32 {l}, {rs}", dst=[l], src=[rs])
+            else:
+                em.valu(f"v_add_f32 {l}, {l}, {rs}", dst=[l], src=[l, rs])
+
+    def emit_masked_branch(self, body, tag):
+        """Emit `body(masked)` with the masked copy out of line, chosen when
+        the sub-tile at k0 reaches past kv_full."""
+        em = self.em
+        l_mask, l_join = self.lab(f"mask{tag}"), self.lab(f"join{tag}")
+        em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_k0}, 32")
+        em.salu(f"s_cmp_gt_i32 {self.s_x[0]}, {self.s_kvfull}")
+        em.salu(f"s_cbranch_scc1 {l_mask}")
+        snap = em.snapshot()
+        body(False)
+        em.label(l_join)
+        self.deferred.append((snap, l_mask, l_join, lambda: body(True)))
+
+    def emit_slow(self, kb):
+        """Out-of-line slow path of the softmax of sub-tile kb of the K tile at
+        v_kb: recompute S^T, move mc to c * max(m, rowmax), rescale O and l,
+        redo the exponentials."""
+        em = self.em
+        t = self.v_t
+        l_slow, l_back = self.lab("slow"), self.lab("back")
+        em.salu(f"s_or_b64 {self.s_or}, {self.s_m1}, {self.s_m2}")
+        em.salu(f"s_cbranch_scc1 {l_slow}")
+        snap = em.snapshot()
+
+        def body():
+            em.drain()
+            frags = self.qk_frags(kb)
+            for i, (reads, tag) in enumerate(frags):
+                reads(i % 3, t.r(0))
+                for qb in range(2):
+                    self.frag_mfma(tag, i % 3, qb)
+            em.drain()
+            l_nm = self.lab("slownm")
+            em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_k0}, 32")
+            em.salu(f"s_cmp_gt_i32 {self.s_x[0]}, {self.s_kvfull}")
+            em.salu(f"s_cbranch_scc0 {l_nm}")
+            self.emit_mask()
+            em.drain()
+            em.label(l_nm)
+            for qb in range(2):
+                S, mx, tmp, a = self.v_S[qb], t.r(0), t.r(1), t.r(2)
+                em.valu(f"v_max3_f32 {mx}, {S.r(0)}, {S.r(1)}, {S.r(2)}", dst=[mx], src=[S.r(0), S.r(1), S.r(2)])
+                for i in range(3, 15, 2):
+                    em.valu(f"v_max3_f32 {mx}, {mx}, {S.r(i)}, {S.r(i + 1)}", dst=[mx], src=[mx, S.r(i), S.r(i + 1)])
+                em.valu(f"v_max_f32 {mx}, {mx}, {S.r(15)}", dst=[mx], src=[mx, S.r(15)])
+                em.valu(f"v_mov_b32 {tmp}, {mx}", dst=[tmp], src=[mx])
+                em.valu(f"v_permlane32_swap_b32 {mx}, {tmp}", dst=[mx, tmp], src=[mx, tmp])
+                em.valu(f"v_max_f32 {mx}, {mx}, {tmp}", dst=[mx], src=[mx, tmp])
+                mc, l = self.v_mc.r(qb), self.v_l.r(qb)
+                # new mc = max(mc, c*mx) (rows without a visible key keep 0)
+                em.valu(f"v_mul_f32 {mx}, s24, {mx}", dst=[mx], src=[mx])
+                em.valu(f"v_max_f32 {mx}, {mc}, {mx}", dst=[mx], src=[mc, mx])
+                em.valu(f"v_sub_f32 {a}, {mc}, {mx}", dst=[a], src=[mc, mx])
+                em.valu(f"v_exp_f32 {a}, {a}", dst=[a], src=[a], trans=True)
+                em.valu(f"v_mov_b32 {mc}, {mx}", dst=[mc], src=[mx])
+                em.valu(f"v_mul_f32 {l}, {l}, {a}", dst=[l], src=[l, a])
+                for db in range(self.NDB):
+                    blk = self.a_O[qb][db]
+                    for i in range(16):
+                        tr = self.v_R[0].r(i & 3)
+                        em.valu(f"v_accvgpr_read_b32 {tr}, {blk.r(i)}", dst=[tr], src=[blk.r(i)])
+                        em.valu(f"v_mul_f32 {tr}, {tr}, {a}", dst=[tr], src=[tr, a])
+                        em.valu(f"v_accvgpr_write_b32 {blk.r(i)}, {tr}", dst=[blk.r(i)], src=[tr])
+            self.emit_softmax()
+            self.emit_l()
+            em.drain()
+            em.salu(f"s_branch {l_back}")
+
+        self.deferred.append((snap, l_slow, None, body))
+        self.emit_l()
+        em.label(l_back)
+
+    def v_phase(self, kb, first=False, dma=False, next_frags=(), vb_tile=None):
+        """Softmax of the sub-tile at k0 (sub-tile kb of the K tile at v_kb);
+        then the DMA of tile u+AHEAD (odd sub-tiles), the V base of the next
+        P.V and the prefetch of the next MFMA phase's first fragments."""
+        em = self.em
+
+        def body(masked):
+            if masked:
+                self.emit_mask()
+            if first:
+                self.emit_rowmax_init()
+            self.emit_softmax()
+
+        self.emit_masked_branch(body, "f" if first else "")
+        if first:
+            self.emit_l(first=True)
+        else:
+            self.emit_slow(kb)
+        if dma:
+            em.salu(f"s_add_u32 {self.s_y[5]}, {self.s_u}, {AHEAD}")
+            self.emit_dma(self.s_y[5])
+        if vb_tile is not None:
+            self.set_vb(vb_tile)
+        self.prefetch(list(next_frags))
+        em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
+        em.salu("s_barrier")
+
+    def set_kb(self, tile):
+        """v_kb = K operand base of the tile index in sgpr `tile`."""
+        em, x = self.em, self.s_x[4]
+        em.salu(f"s_and_b32 {x}, {tile}, {SLOTS - 1}")
+        em.salu(f"s_mul_i32 {x}, {x}, {self.TILE}")
+        em.valu(f"v_add_u32 {self.v_kb}, {x}, {self.v_klane}", dst=[str(self.v_kb)], src=[str(self.v_klane)])
+
+    def set_vb(self, tile):
+        em, x = self.em, self.s_x[4]
+        em.salu(f"s_and_b32 {x}, {tile}, {SLOTS - 1}")
+        em.salu(f"s_mul_i32 {x}, {x}, {self.TILE}")
+        em.valu(f"v_add_u32 {self.v_vb}, {x}, {self.v_vlane}", dst=[str(self.v_vb)], src=[str(self.v_vlane)])
+
+    # ------------------------------------------------------------------------
+    # epilogue
+    # ------------------------------------------------------------------------
+    def epilogue(self, empty=False):
+        """O / l rounded to the input dtype and LSE = ln2 * (mc + log2 l) (-inf
+        when l = 0), for the wave's two query blocks.  With `empty`, zeros
+        and -inf (an item with no visible key)."""
+        em = self.em
+        em.drain()
+        F = [self.v_S[0], self.v_S[1]]
+        t = self.v_R[1]                   # scratch: rows, offsets, scale
+        u = self.v_R[2]
+        em.valu(f"v_lshrrev_b32 {t.r(0)}, 5, v0", dst=[t.r(0)], src=["v0"])
+        em.valu(f"v_lshlrev_b32 {t.r(3)}, 4, {t.r(0)}", dst=[t.r(3)], src=[t.r(0)])   # 16h
+        em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {self.D * 2}")
+        for qb in range(2):
+            l = self.v_l.r(qb)
+            if empty:
+                em.valu(f"v_mov_b32 {t.r(1)}, 0", dst=[t.r(1)])
+                em.valu(f"v_mov_b32 {l}, 0", dst=[l])
+            else:
+                em.valu(f"v_mov_b32 {t.r(0)}, {l}", dst=[t.r(0)], src=[l])
+                em.valu(f"v_permlane32_swap_b32 {l}, {t.r(0)}", dst=[l, t.r(0)], src=[l, t.r(0)])
+                em.valu(f"v_add_f32 {l}, {l}, {t.r(0)}", dst=[l], src=[l, t.r(0)])
+                em.valu(f"v_rcp_f32 {t.r(1)}, {l}", dst=[t.r(1)], src=[l], trans=True)
+                em.valu(f"v_cmp_lt_f32 vcc, 0, {l}", src=[l])
+                em.valu(f"v_cndmask_b32 {t.r(1)}, 0, {t.r(1)}, vcc", dst=[t.r(1)], src=[t.r(1)])
+            self.row_of_block(qb, u.r(0))
+            em.valu(f"v_mul_lo_u32 {t.r(2)}, {u.r(0)}, {self.s_x[0]}", dst=[t.r(2)], src=[u.r(0)])
+            em.valu(f"v_add_u32 {t.r(2)}, {t.r(2)}, {t.r(3)}", dst=[t.r(2)], src=[t.r(2), t.r(3)])
+            for db in range(self.NDB):
+                blk = self.a_O[qb][db]
+                for jp in range(2):
+                    k = 2 * db + jp
+                    Fk, o = F[k % 2], 8 + 4 * ((k // 2) % 2)
+                    for jj in range(2):
+                        j = 2 * jp + jj
+                        for r in range(4):
+                            dst = Fk.r(4 * jj + r)
+                            if empty:
+                                em.valu(f"v_mov_b32 {dst}, 0", dst=[dst])
+                            else:
+                                em.valu(f"v_accvgpr_read_b32 {dst}, {blk.r(4 * j + r)}", dst=[dst],
+                                        src=[blk.r(4 * j + r)])
+                                em.valu(f"v_mul_f32 {dst}, {dst}, {t.r(1)}", dst=[dst], src=[dst, t.r(1)])
+                        for c in range(2):
+                            a, b = Fk.r(4 * jj + 2 * c), Fk.r(4 * jj + 2 * c + 1)
+                            em.valu(f"{self.cvt_op} {Fk.r(o + 2 * jj + c)}, {a}, {b}",
+                                    dst=[Fk.r(o + 2 * jj + c)], src=[a, b])
+                    for c in range(2):
+                        xx, yy = Fk.r(o + c), Fk.r(o + 2 + c)
+                        em.valu(f"v_permlane32_swap_b32 {xx}, {yy}", dst=[xx, yy], src=[xx, yy])
+                    em.vmem(f"buffer_store_dwordx4 {Fk.r(o, 4)}, {t.r(2)}, {self.s_ro}, 0 offen "
+                            f"offset:{64 * db + 32 * jp}", src=[Fk.r(o, 4), t.r(2)])
+            # LSE
+            em.valu(f"v_lshlrev_b32 {u.r(1)}, 2, {u.r(0)}", dst=[u.r(1)], src=[u.r(0)])
+            if empty:
+                em.valu(f"v_mov_b32 {u.r(2)}, {self.s_neg}", dst=[u.r(2)])
+            else:
+                em.valu(f"v_log_f32 {u.r(2)}, {l}", dst=[u.r(2)], src=[l], trans=True)
+                em.valu(f"v_add_f32 {u.r(2)}, {self.v_mc.r(qb)}, {u.r(2)}", dst=[u.r(2)],
+                        src=[self.v_mc.r(qb), u.r(2)])
+                em.valu(f"v_mul_f32 {u.r(2)}, {f32_hex(LN2)}, {u.r(2)}", dst=[u.r(2)], src=[u.r(2)])
+                em.valu(f"v_mov_b32 {u.r(3)}, {self.s_neg}", dst=[u.r(3)])
+                em.valu(f"v_cndmask_b32 {u.r(2)}, {u.r(3)}, {u.r(2)}, vcc", dst=[u.r(2)], src=[u.r(2), u.r(3)])
+            # one lane per row stores its LSE (lanes >= 32 hold the same rows)
+            em.vmem(f"buffer_store_dword {u.r(2)}, {u.r(1)}, {self.s_rl}, 0 offen", src=[u.r(2), u.r(1)])
+
+    # ------------------------------------------------------------------------
+    def body(self):
+        em = self.em
+        self.alloc()
+        self.kernel_setup()
+        self.lane_consts()
+        em.drain()
+        l_item, l_exit, l_empty = self.lab("item"), self.lab("exit"), self.lab("empty")
+        l_loop, l_last = self.lab("loop"), self.lab("last")
+        em.label(l_item)
+        self.item_setup(l_exit)
+        self.out_desc()
+        em.salu(f"s_cmp_eq_u32 {self.s_ntiles}, 0")
+        em.salu(f"s_cbranch_scc1 {l_empty}")
+        # ---- prologue: Q, tiles 0 .. AHEAD-1 -------------------------------------
+        self.load_q()
+        for tt in range(AHEAD):
+            em.salu(f"s_mov_b32 {self.s_y[5]}, {tt}")
+            self.emit_dma(self.s_y[5])
+        em.salu(f"s_mov_b32 {self.s_u}, 0")
+        em.salu(f"s_mov_b32 {self.s_k0}, 0")
+        self.set_kb(self.s_u)
+        self.set_vb(self.s_u)
+        em.drain()
+        em.salu(f"s_waitcnt vmcnt({4 * (AHEAD - 1)})")     # Q and tile 0
+        em.salu("s_barrier")
+        self.prefetch(self.qk_frags(0))
+        # waves 4-7 run one phase behind
+        l_g0 = self.lab("g0")
+        em.salu(f"s_cmp_lt_u32 {self.s_w}, 4")
+        em.salu(f"s_cbranch_scc1 {l_g0}")
+        em.salu("s_barrier")
+        em.label(l_g0)
+        # ---- tile 0 -------------------------------------------------------------------
+        self.m_phase(self.qk_frags(0))
+        em.salu("s_barrier")
+        self.v_phase(0, first=True, next_frags=self.pv_frags(0))
+        self.m_phase(self.pv_frags(0) + self.qk_frags(1), first_pv=True)
+        em.salu(f"s_waitcnt vmcnt({4})")                    # tile 1
+        em.salu("s_barrier")
+        self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
+        em.salu(f"s_add_u32 {self.s_u}, {self.s_u}, 1")
+        em.drain()
+        # ---- tiles 1 .. n-1 ---------------------------------------------------------
+        em.label(l_loop)
+        em.salu(f"s_cmp_ge_u32 {self.s_u}, {self.s_ntiles}")
+        em.salu(f"s_cbranch_scc1 {l_last}")
+        self.set_kb(self.s_u)
+        self.m_phase(self.pv_frags(1) + self.qk_frags(0))
+        em.salu("s_barrier")
+        self.v_phase(0, next_frags=self.pv_frags(0), vb_tile=self.s_u)
+        self.m_phase(self.pv_frags(0) + self.qk_frags(1))
+        em.salu(f"s_waitcnt vmcnt({4})")                    # tile u+1
+        em.salu("s_barrier")
+        self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
+        em.salu(f"s_add_u32 {self.s_u}, {self.s_u}, 1")
+        em.drain()
+        em.salu(f"s_branch {l_loop}")
+        # ---- last P.V, epilogue ------------------------------------------------------
+        em.label(l_last)
+        self.m_phase(self.pv_frags(1))
+        em.salu("s_barrier")
+        self.epilogue()
+        l_g1 = self.lab("g1")
+        em.salu(f"s_cmp_ge_u32 {self.s_w}, 4")
+        em.salu(f"s_cbranch_scc1 {l_g1}")
+        em.salu("s_barrier")
+        em.label(l_g1)
+        em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        em.drain()
+        em.salu(f"s_branch {l_item}")
+        # ---- an item without visible keys ----------------------------------------
+        em.label(l_empty)
+        self.epilogue(empty=True)
+        em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        em.drain()
+        em.salu(f"s_branch {l_item}")
+        em.label(l_exit)
+        em.salu("s_waitcnt vmcnt(0)")
+        em.salu("s_endpgm")
+        for snap, l_from, l_join, fn in self.deferred:
+            em.restore(snap)
+            em.label(l_from)
+            fn()
+            em.drain()
+            if l_join is not None:
+                em.salu(f"s_branch {l_join}")
+
+    # ------------------------------------------------------------------------
+    def assemble_text(self):
+        self.body()
+        name = self.name
+        nv, na = self.nvgpr, self.nagpr
+        total = nv + na
+        out = ['\t.text', f"\t.globl {name}", "\t.p2align 8", f"\t.type {name},@function", f"{name}:",
+               self.em.text(), f"\t.size {name}, .-{name}", "\t.rodata", "\t.p2align 6",
+               f"\t.amdhsa_kernel {name}"]
+        for k, v in [
+            ("group_segment_fixed_size", self.LDS), ("private_segment_fixed_size", 0),
+            ("kernarg_size", 80), ("user_sgpr_count", 2),
+            ("user_sgpr_dispatch_ptr", 0), ("user_sgpr_queue_ptr", 0),
+            ("user_sgpr_kernarg_segment_ptr", 1), ("user_sgpr_dispatch_id", 0),
+            ("user_sgpr_kernarg_preload_length", 0), ("user_sgpr_kernarg_preload_offset", 0),
+            ("user_sgpr_private_segment_size", 0), ("uses_dynamic_stack", 0),
+            ("enable_private_segment", 0), ("system_sgpr_workgroup_id_x", 1),
+            ("system_sgpr_workgroup_id_y", 1), ("system_sgpr_workgroup_id_z", 1),
+            ("system_sgpr_workgroup_info", 0), ("system_vgpr_workitem_id", 0),
+            ("next_free_vgpr", total), ("next_free_sgpr", self.nsgpr), ("accum_offset", nv),
+            ("reserve_vcc", 1), ("float_round_mode_32", 0), ("float_round_mode_16_64", 0),
+            ("float_denorm_mode_32", 3), ("float_denorm_mode_16_64", 3), ("dx10_clamp", 1),
+            ("ieee_mode", 1), ("fp16_overflow", 0), ("tg_split", 0),
+        ]:
+            out.append(f"\t\t.amdhsa_{k} {v}")
+        out.append("\t.end_amdhsa_kernel")
+        return "\n".join(out) + "\n", dict(name=name, nv=nv, na=na, total=total, lds=self.LDS,
+                                          ns=self.nsgpr + 2, wg=BM)

@@ -1,11 +1,16 @@
 // fa_launch.cpp -- loads the gfx950 attention kernels (assembled from the
-// generator in attention_forward_05_amd/asm and embedded in this library as a
-// code object) and launches them.
+// generators in attention_forward_05_amd/asm and embedded in this library as
+// a code object) and launches them.
+//
+// Two kernel shapes: four waves on 256-row query tiles (every D), and, for
+// D = 128 when the 512-row tiles alone give every compute unit an item,
+// eight waves (two per SIMD, alternating MFMA and softmax phases) on 512-row
+// tiles, which halves the K/V traffic into LDS per FLOP.
 //
 // The kernels are persistent: the grid has G = min(items, compute units)
 // workgroups, one per CU, and workgroup g takes item r*G + (g or G-1-g,
-// alternating by round r) of the (batch, q-head, 256-row query tile) items,
-// which the kernel orders longest first.  Workgroups are handed to the 8
+// alternating by round r) of the (batch, q-head, query tile) items, which the
+// kernel orders longest first.  Workgroups are handed to the 8
 // XCDs round-robin by id, so within a round each XCD sees one residue of the
 // head slot mod 8; the kernel maps slot s to head (s % 8) * (Hq / 8) + s / 8
 // when Hq % 8 == 0, so each XCD serves a contiguous run of heads (whole GQA
@@ -25,7 +30,8 @@ extern "C" const unsigned long fa_hsaco_size;
 namespace fa {
 namespace {
 
-constexpr int kBM = 256;       // query rows per workgroup
+constexpr int kBM = 256;       // query rows per workgroup (four-wave kernels)
+constexpr int kBM8 = 512;      // query rows per workgroup (eight-wave kernels)
 constexpr int kBN = 64;        // keys per tile
 constexpr int kMaxDevices = 64;
 
@@ -43,13 +49,15 @@ struct alignas(8) KernArgs {
 };
 static_assert(sizeof(KernArgs) == 80, "kernarg layout of the generated kernels");
 
-const char* kNames[4] = {"fa_fwd_bf16_d128_gfx950", "fa_fwd_bf16_d64_gfx950",
-                         "fa_fwd_f16_d128_gfx950", "fa_fwd_f16_d64_gfx950"};
+constexpr int kKernels = 6;
+const char* kNames[kKernels] = {"fa_fwd_bf16_d128_gfx950", "fa_fwd_bf16_d64_gfx950",
+                                "fa_fwd_f16_d128_gfx950",  "fa_fwd_f16_d64_gfx950",
+                                "fa_fwd_bf16_d128_x8_gfx950", "fa_fwd_f16_d128_x8_gfx950"};
 
 struct DeviceKernels {
   bool loaded = false;
   hipModule_t mod = nullptr;
-  hipFunction_t fn[4] = {};
+  hipFunction_t fn[kKernels] = {};
   int cus = 0;  // compute units of the device
 };
 
@@ -66,7 +74,7 @@ hipError_t kernels_for_current_device(DeviceKernels** out) {
   if (!d.loaded) {
     e = hipModuleLoadData(&d.mod, fa_hsaco_data);
     if (e != hipSuccess) return e;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKernels; ++i) {
       e = hipModuleGetFunction(&d.fn[i], d.mod, kNames[i]);
       if (e != hipSuccess) return e;
     }
@@ -98,13 +106,19 @@ int64_t work_items(int B, int Sq, int Hq) {
 }
 
 int query_tiles(int Sq) { return (Sq + kBM - 1) / kBM; }
+
+bool use_eight_waves(int B, int Sq, int Hq, int D, int cus) {
+  return D == 128 && (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq >= cus;
+}
 int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
 
 hipError_t launch(const LaunchArgs& a) {
   DeviceKernels* dk = nullptr;
   hipError_t e = kernels_for_current_device(&dk);
   if (e != hipSuccess) return e;
-  const int variant = (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
+  const bool x8 = use_eight_waves(a.B, a.Sq, a.Hq, a.D, dk->cus);
+  const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
+                         : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
   KernArgs ka;
   memset(&ka, 0, sizeof(ka));
   ka.q = a.q;
@@ -119,7 +133,7 @@ hipError_t launch(const LaunchArgs& a) {
   ka.Hkv = a.Hkv;
   ka.causal = a.causal;
   ka.c = a.c;
-  const int64_t nq = query_tiles(a.Sq);
+  const int64_t nq = x8 ? (a.Sq + kBM8 - 1) / kBM8 : query_tiles(a.Sq);
   const int64_t items = nq * a.B * a.Hq;
   const int64_t grid = items < dk->cus ? items : dk->cus;
   ka.nq_grid = (uint32_t)nq | ((uint32_t)grid << 16);
@@ -128,8 +142,8 @@ hipError_t launch(const LaunchArgs& a) {
   size_t size = sizeof(ka);
   void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &ka, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
                     HIP_LAUNCH_PARAM_END};
-  e = hipModuleLaunchKernel(dk->fn[variant], (unsigned)grid, 1, 1, 256, 1, 1, 0, a.stream,
-                            nullptr, config);
+  e = hipModuleLaunchKernel(dk->fn[variant], (unsigned)grid, 1, 1, x8 ? 512 : 256, 1, 1, 0,
+                            a.stream, nullptr, config);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

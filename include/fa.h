@@ -50,9 +50,9 @@ typedef enum {
                               16-byte aligned, o overlapping q/k/v, size overflow */
   FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64 or 128,
                               scale < 0, sizes beyond the kernel's limits
-                              (ceil(Sq/256) and B at most 65535, ceil(Skv/64)
-                              below 65536, Sq*Hq*D*2 bytes, B*Sq*Hq and B*Skv
-                              below 2^31) */
+                              (ceil(Sq/256) at most 65535, B*Hq*ceil(Sq/256)
+                              below 2^24, ceil(Skv/64) below 65536,
+                              Sq*Hq*D*2 bytes, B*Sq*Hq and B*Skv below 2^31) */
   FA_ERR_HIP = -3          /* the HIP runtime reported an error loading the
                               kernels or at launch */
 } fa_status;

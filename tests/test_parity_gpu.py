@@ -54,8 +54,9 @@ def check(o, lse, o_ref, lse_ref, what=""):
     return do.max(), do.mean()
 
 
-def full_case(fa, B, Sq, Skv, Hq, Hkv, D, causal, dtype="bf16", seed=0, scale=None, dist="normal"):
-    q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, D, dtype, seed, dist=dist)
+def full_case(fa, B, Sq, Skv, Hq, Hkv, D, causal, dtype="bf16", seed=0, scale=None, dist="normal",
+              boost=0.0):
+    q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, D, dtype, seed, k_row_boost_frac=boost, dist=dist)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o, lse = run_gpu(fa, q, k, v, causal, scale)
@@ -141,6 +142,39 @@ def test_deterministic_and_side_stream(fa):
 def test_uniform_inputs_and_large_logits(fa):
     full_case(fa, 1, 512, 512, 2, 2, 128, True, "bf16", seed=9, dist="uniform")
     full_case(fa, 1, 256, 777, 2, 1, 128, False, "f16", seed=10, scale=1.0)
+
+
+# ---------------------------------------------------------------------------
+# the eight-wave kernel: D = 128 with at least 256 (batch, q-head, 512-row
+# query tile) items, i.e. one per compute unit of an MI355X
+# ---------------------------------------------------------------------------
+
+X8_CASES = [
+    # B, Sq, Skv, Hq, Hkv, causal, dtype
+    (1, 512, 512, 256, 256, True, "bf16"),     # one query tile, the whole diagonal
+    (1, 1000, 1000, 128, 32, True, "bf16"),    # ragged second tile, GQA 4
+    (2, 300, 777, 128, 16, False, "bf16"),     # ragged key tail, GQA 8
+    (1, 200, 1500, 256, 32, True, "f16"),      # bottom-right mask, Sq < Skv
+    (1, 600, 100, 256, 256, True, "bf16"),     # rows with no visible key
+    (1, 520, 600, 256, 64, False, "f16"),      # 8-row second query tile
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype", X8_CASES)
+def test_eight_wave_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype):
+    full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 3 * Skv + Hkv)
+
+
+@pytest.mark.parametrize("case", ["scale1", "kboost"])
+def test_eight_wave_slow_path(fa, case):
+    """Logits large enough that the reference max moves often (the slow
+    path): scale 1 on N(0, 1) inputs; 1% of key rows scaled by 8.  fp16:
+    with scale 1 the softmax is nearly one-hot and bf16 rounding of P and O
+    alone reaches the 2e-2 bound (both kernels measure about 2e-2 there)."""
+    if case == "scale1":
+        full_case(fa, 1, 512, 512, 256, 128, 128, True, "f16", seed=21, scale=1.0)
+    else:
+        full_case(fa, 1, 256, 1024, 256, 8, 128, True, "f16", seed=22, boost=0.01)
 
 
 # ---------------------------------------------------------------------------
