@@ -111,7 +111,11 @@ class Gen8:
         t = S.take
         r["s_hq"], r["s_qt"], r["s_b"], r["s_hk"] = t("hq", 1), t("qt", 1), t("b", 1), t("hk", 1)
         r["s_w"], r["s_q0"], r["s_off"], r["s_ntiles"] = t("w", 1), t("q0", 1), t("off", 1), t("nt", 1)
-        r["s_kvfull"], r["s_rowlim"], r["s_rowb"], r["s_u"] = t("kvf", 1), t("rowlim", 1), t("rowb", 1), t("u", 1)
+        r["s_rowlim"], r["s_rowb"], r["s_u"] = t("rowlim", 1), t("rowb", 1), t("u", 1)
+        # per query block b: sub-tiles whose first key k0 <= fu_b are seen in
+        # full by every row of the block; k0 > dl_b by none of them
+        r["s_fu"] = [t("fu0", 1), t("fu1", 1)]
+        r["s_dl"] = [t("dl0", 1), t("dl1", 1)]
         r["s_rb"] = [t("rb0", 1), t("rb1", 1)]
         r["s_ro"] = t("ro", 4, 4)
         r["s_rl"] = t("rl", 4, 4)
@@ -287,13 +291,18 @@ class Gen8:
         em.salu(f"s_lshr_b32 {self.s_ntiles}, {x[0]}, 6")
         em.salu(f"s_lshl_b32 {x[0]}, {self.s_ntiles}, 6")
         em.salu(f"s_min_u32 {self.s_rowlim}, {x[0]}, s20")
-        # keys below kv_full are visible to every row of the wave (its lowest
-        # row is the first of block 0)
-        em.salu(f"s_add_i32 {x[0]}, {self.s_rb[0]}, {self.s_off}")
-        em.salu(f"s_add_i32 {x[0]}, {x[0]}, 1")
-        em.salu(f"s_min_i32 {x[0]}, {x[0]}, s20")
+        # block thresholds: a row's last visible key is min(row + off, Skv-1)
+        # (causal) or Skv-1; fu_b = that of the block's first row - 31,
+        # dl_b = that of its last row
+        em.salu(f"s_sub_i32 {x[1]}, s20, 1")
         em.salu("s_cmp_eq_u32 s23, 0")
-        em.salu(f"s_cselect_b32 {self.s_kvfull}, s20, {x[0]}")
+        em.salu(f"s_cselect_b32 {x[2]}, s20, {self.s_off}")
+        for qb in range(2):
+            em.salu(f"s_add_i32 {x[0]}, {self.s_rb[qb]}, {x[2]}")
+            em.salu(f"s_min_i32 {self.s_fu[qb]}, {x[0]}, {x[1]}")
+            em.salu(f"s_sub_i32 {self.s_fu[qb]}, {self.s_fu[qb]}, 31")
+            em.salu(f"s_add_i32 {x[0]}, {x[0]}, 31")
+            em.salu(f"s_min_i32 {self.s_dl[qb]}, {x[0]}, {x[1]}")
         # K/V batch/head bases (bytes)
         em.salu(f"s_mul_i32 {x[0]}, {self.s_b}, s20")
         em.salu(f"s_mul_i32 {x[2]}, {x[0]}, {self.s_rowb}")
@@ -453,23 +462,99 @@ class Gen8:
         for i in range(min(2, len(frags))):
             frags[i][0](i, t.r(i))
 
-    def m_phase(self, frags, first_pv=False):
-        """MFMAs of the fragments in order, both query blocks per fragment;
-        fragments 0 and 1 are already in flight; fragment i+2 is read into
-        the buffer of fragment i-1 after the first MFMA of fragment i."""
+    def m_phase(self, pv, qk, first_pv=False, pv_blocks=(0, 1), qk_blocks=(0, 1)):
+        """MFMAs of the P.V fragments `pv` (for the query blocks pv_blocks)
+        then of the S^T fragments `qk` (for qk_blocks), each fragment once for
+        each of its blocks.  The first two fragments of pv + qk are already in
+        flight (buffers 0, 1); fragment i+2 is read into the buffer of
+        fragment i-1 after the first MFMA of fragment i."""
         t = self.v_t
+        full = list(pv) + list(qk)
+        frags = [(f, pv_blocks) for f in (pv if pv_blocks else [])] + \
+                [(f, qk_blocks) for f in (qk if qk_blocks else [])]
         n = len(frags)
-        for i, (reads, tag) in enumerate(frags):
+        if [f for f, _ in frags[:2]] != full[:2]:
+            for i in range(min(2, n)):
+                frags[i][0][0](i, t.r(i))
+        for i, ((reads, tag), blocks) in enumerate(frags):
             buf = i % 3
-            self.frag_mfma(tag, buf, 0, first_pv)
-            if i + 2 < n:
-                frags[i + 2][0]((i + 2) % 3, t.r((i + 2) % 2))
-            self.frag_mfma(tag, buf, 1, first_pv)
+            for k, qb in enumerate(blocks):
+                self.frag_mfma(tag, buf, qb, first_pv)
+                if k == 0 and i + 2 < n:
+                    frags[i + 2][0][0]((i + 2) % 3, t.r((i + 2) % 2))
+
+    def m_phase_sel(self, pv, qk, first_pv=False):
+        """The MFMA phase with MFMAs only for live query blocks.  A block is
+        live for a sub-tile whose first key k0 is at most dl_b, the last key
+        any of its rows sees (block 0's rows come first, so it dies first).
+        At the phase start s_k0 is the first key of the S^T sub-tile; the
+        P.V sub-tile starts 32 keys earlier.  Every block live is the common
+        case; the other combinations run out of line."""
+        em, k0, dl, x = self.em, self.s_k0, self.s_dl, self.s_x[0]
+        l_v, l_join = self.lab("mvar"), self.lab("mjoin")
+        test = dl[0]
+        if not qk:                                 # P.V only: the previous sub-tile
+            em.salu(f"s_sub_u32 {x}, {k0}, 32")
+            em.salu(f"s_cmp_le_i32 {x}, {dl[0]}")
+        else:
+            em.salu(f"s_cmp_le_i32 {k0}, {dl[0]}")
+        em.salu(f"s_cbranch_scc0 {l_v}")
+        snap = em.snapshot()
+        self.m_phase(pv, qk, first_pv)
+        em.label(l_join)
+
+        def variants():
+            # block 0 is not live for the S^T sub-tile (or, P.V only, for P.V)
+            B = (1,)
+            if not qk:
+                l00 = self.lab("m00")
+                em.salu(f"s_cmp_le_i32 {x}, {dl[1]}")
+                em.salu(f"s_cbranch_scc0 {l00}")
+                self._mvar(snap, l_join, pv, qk, first_pv, B, ())
+                em.label(l00)
+                self._mvar(snap, l_join, pv, qk, first_pv, (), ())
+                return
+            if not pv:
+                l0 = self.lab("m00")
+                em.salu(f"s_cmp_le_i32 {k0}, {dl[1]}")
+                em.salu(f"s_cbranch_scc0 {l0}")
+                self._mvar(snap, l_join, pv, qk, first_pv, (), B)
+                em.label(l0)
+                self._mvar(snap, l_join, pv, qk, first_pv, (), ())
+                return
+            l_pv2, l_22, l_32, l_00 = self.lab("mpv2"), self.lab("m22"), self.lab("m32"), self.lab("m00")
+            em.salu(f"s_sub_u32 {x}, {k0}, 32")
+            em.salu(f"s_cmp_le_i32 {x}, {dl[0]}")
+            em.salu(f"s_cbranch_scc0 {l_pv2}")
+            em.salu(f"s_cmp_le_i32 {k0}, {dl[1]}")
+            em.salu(f"s_cbranch_scc1 {l_32}")
+            self._mvar(snap, l_join, pv, qk, first_pv, (0, 1), ())
+            em.label(l_32)
+            self._mvar(snap, l_join, pv, qk, first_pv, (0, 1), B)
+            em.label(l_pv2)
+            em.salu(f"s_cmp_le_i32 {x}, {dl[1]}")
+            em.salu(f"s_cbranch_scc0 {l_00}")
+            em.salu(f"s_cmp_le_i32 {k0}, {dl[1]}")
+            em.salu(f"s_cbranch_scc1 {l_22}")
+            self._mvar(snap, l_join, pv, qk, first_pv, B, ())
+            em.label(l_22)
+            self._mvar(snap, l_join, pv, qk, first_pv, B, B)
+            em.label(l_00)
+            self._mvar(snap, l_join, pv, qk, first_pv, (), ())
+
+        self.deferred.append((snap, l_v, None, variants))
+
+    def _mvar(self, snap, l_join, pv, qk, first_pv, pvb, qkb):
+        em = self.em
+        em.restore(snap)
+        self.m_phase(pv, qk, first_pv, pvb, qkb)
+        em.drain()
+        em.salu(f"s_branch {l_join}")
 
     # ------------------------------------------------------------------------
     # softmax phase
     # ------------------------------------------------------------------------
-    def emit_mask(self):
+    def emit_mask(self, blocks=(0, 1)):
         """S entries of keys past each row's last visible key -> -inf.
         Register i of a block holds key k0 + 8*(i >> 2) + 4h + (i & 3); the
         last visible key is min(row + off, Skv - 1) (causal) or Skv - 1."""
@@ -483,7 +568,7 @@ class Gen8:
         em.salu("s_cmp_eq_u32 s23, 0")
         em.salu(f"s_cselect_b32 {x[2]}, s20, {self.s_off}")                  # row offset of the limit
         em.valu(f"v_mov_b32 {ninf}, {self.s_neg}", dst=[ninf])
-        for qb in range(2):
+        for qb in blocks:
             S = self.v_S[qb]
             self.row_of_block(qb, d)
             em.valu(f"v_add_u32 {d}, {x[2]}, {d}", dst=[d], src=[d])
@@ -495,11 +580,16 @@ class Gen8:
                 em.valu(f"v_cmp_lt_i32 vcc, {d}, {ci}", src=[d])
                 em.valu(f"v_cndmask_b32 {S.r(i)}, {S.r(i)}, {ninf}, vcc", dst=[S.r(i)], src=[S.r(i), ninf])
 
-    def emit_rowmax_init(self):
-        """First sub-tile: mc = c * rowmax (0 for rows with every key masked)."""
+    def emit_rowmax_init(self, blocks=(0, 1)):
+        """First sub-tile: mc = c * rowmax (0 for rows with every key masked,
+        and for blocks without a visible key)."""
         em = self.em
         t = self.v_t
         for qb in range(2):
+            mc = self.v_mc.r(qb)
+            if qb not in blocks:
+                em.valu(f"v_mov_b32 {mc}, 0", dst=[mc])
+                continue
             S, mx, tmp = self.v_S[qb], t.r(0), t.r(1)
             em.valu(f"v_max3_f32 {mx}, {S.r(0)}, {S.r(1)}, {S.r(2)}", dst=[mx], src=[S.r(0), S.r(1), S.r(2)])
             for i in range(3, 15, 2):
@@ -508,14 +598,14 @@ class Gen8:
             em.valu(f"v_mov_b32 {tmp}, {mx}", dst=[tmp], src=[mx])
             em.valu(f"v_permlane32_swap_b32 {mx}, {tmp}", dst=[mx, tmp], src=[mx, tmp])
             em.valu(f"v_max_f32 {mx}, {mx}, {tmp}", dst=[mx], src=[mx, tmp])
-            mc = self.v_mc.r(qb)
             em.valu(f"v_mul_f32 {mc}, s24, {mx}", dst=[mc], src=[mx])
             em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {mx}", src=[mx])
             em.valu(f"v_cndmask_b32 {mc}, {mc}, 0, vcc", dst=[mc], src=[mc])
 
-    def softmax_ops(self):
+    def softmax_ops(self, blocks=(0, 1)):
         """In place: S = 2^(c*S - mc); rs = lane sums per block; P = S rounded
-        (over the first 8 registers of each block); the trigger masks."""
+        (over the first 8 registers of each block); the trigger masks.  Blocks
+        outside `blocks` get rs = 0 and a clear trigger mask."""
         em = self.em
         out = []
         E = []
@@ -542,20 +632,25 @@ class Gen8:
                     f"v_add_f32 {acc}, {acc}, {S.r(i)}", dst=[acc], src=[acc, S.r(i)]))
             s.append(lambda ra=ra, rb=rb: em.valu(f"v_add_f32 {ra}, {ra}, {rb}", dst=[ra], src=[ra, rb]))
             Ssum.append(s)
-        # order: exponentials of both blocks chunk by chunk, the sums of a
+        # order: exponentials of the blocks chunk by chunk, the sums of a
         # chunk one chunk later
         for c4 in range(4):
-            for qb in range(2):
+            for qb in blocks:
                 out += E[qb][8 * c4:8 * c4 + 8]
             if c4 >= 1:
-                for qb in range(2):
+                for qb in blocks:
                     out += Ssum[qb][4 * (c4 - 1):4 * c4]
-        for qb in range(2):
+        for qb in blocks:
             out += Ssum[qb][12:]
         for qb, msk in ((0, self.s_m1), (1, self.s_m2)):
-            out.append(lambda qb=qb, msk=msk: em.valu(
-                f"v_cmp_lt_f32 {msk}, {self.s_thr}, {self.v_rs.r(qb)}", src=[self.v_rs.r(qb)]))
-        for qb in range(2):
+            if qb in blocks:
+                out.append(lambda qb=qb, msk=msk: em.valu(
+                    f"v_cmp_lt_f32 {msk}, {self.s_thr}, {self.v_rs.r(qb)}", src=[self.v_rs.r(qb)]))
+            else:
+                out.append(lambda qb=qb, msk=msk: (
+                    em.valu(f"v_mov_b32 {self.v_rs.r(qb)}, 0", dst=[self.v_rs.r(qb)]),
+                    em.salu(f"s_mov_b64 {msk}, 0")))
+        for qb in blocks:
             S = self.v_S[qb]
             for k in range(8):
                 lo, hi = S.r(2 * k), S.r(2 * k + 1)
@@ -563,8 +658,8 @@ class Gen8:
                     f"{self.cvt_op} {S.r(k)}, {lo}, {hi}", dst=[S.r(k)], src=[lo, hi]))
         return out
 
-    def emit_softmax(self):
-        for f in self.softmax_ops():
+    def emit_softmax(self, blocks=(0, 1)):
+        for f in self.softmax_ops(blocks):
             f()
 
     def emit_l(self, first=False):
@@ -576,18 +671,47 @@ class Gen8:
             else:
                 em.valu(f"v_add_f32 {l}, {l}, {rs}", dst=[l], src=[l, rs])
 
-    def emit_masked_branch(self, body, tag):
-        """Emit `body(masked)` with the masked copy out of line, chosen when
-        the sub-tile at k0 reaches past kv_full."""
-        em = self.em
-        l_mask, l_join = self.lab(f"mask{tag}"), self.lab(f"join{tag}")
-        em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_k0}, 32")
-        em.salu(f"s_cmp_gt_i32 {self.s_x[0]}, {self.s_kvfull}")
-        em.salu(f"s_cbranch_scc1 {l_mask}")
+    def emit_state_branch(self, body, tag):
+        """Emit body(states) for the block states of the sub-tile at k0:
+        'F' every row sees every key (k0 <= fu_b), 'D' no row sees a key
+        (k0 > dl_b), else 'M' (masked).  Block 0 is never ahead of block 1,
+        so the common case is one compare ((F, F)); the others, (M, F), (M, M),
+        (D, F), (D, M) and (D, D), run out of line."""
+        em, k0, fu, dl = self.em, self.s_k0, self.s_fu, self.s_dl
+        l_v, l_join = self.lab(f"vvar{tag}"), self.lab(f"vjoin{tag}")
+        em.salu(f"s_cmp_le_i32 {k0}, {fu[0]}")
+        em.salu(f"s_cbranch_scc0 {l_v}")
         snap = em.snapshot()
-        body(False)
+        body(("F", "F"))
         em.label(l_join)
-        self.deferred.append((snap, l_mask, l_join, lambda: body(True)))
+
+        def one(st):
+            em.restore(snap)
+            body(st)
+            em.drain()
+            em.salu(f"s_branch {l_join}")
+
+        def variants():
+            l_d, l_mf, l_df, l_dd = self.lab("vd"), self.lab("vmf"), self.lab("vdf"), self.lab("vdd")
+            em.salu(f"s_cmp_gt_i32 {k0}, {dl[0]}")
+            em.salu(f"s_cbranch_scc1 {l_d}")
+            em.salu(f"s_cmp_le_i32 {k0}, {fu[1]}")
+            em.salu(f"s_cbranch_scc1 {l_mf}")
+            one(("M", "M"))
+            em.label(l_mf)
+            one(("M", "F"))
+            em.label(l_d)
+            em.salu(f"s_cmp_le_i32 {k0}, {fu[1]}")
+            em.salu(f"s_cbranch_scc1 {l_df}")
+            em.salu(f"s_cmp_gt_i32 {k0}, {dl[1]}")
+            em.salu(f"s_cbranch_scc1 {l_dd}")
+            one(("D", "M"))
+            em.label(l_df)
+            one(("D", "F"))
+            em.label(l_dd)
+            one(("D", "D"))
+
+        self.deferred.append((snap, l_v, None, variants))
 
     def emit_slow(self, kb):
         """Out-of-line slow path of the softmax of sub-tile kb of the K tile at
@@ -609,8 +733,7 @@ class Gen8:
                     self.frag_mfma(tag, i % 3, qb)
             em.drain()
             l_nm = self.lab("slownm")
-            em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_k0}, 32")
-            em.salu(f"s_cmp_gt_i32 {self.s_x[0]}, {self.s_kvfull}")
+            em.salu(f"s_cmp_gt_i32 {self.s_k0}, {self.s_fu[0]}")
             em.salu(f"s_cbranch_scc0 {l_nm}")
             self.emit_mask()
             em.drain()
@@ -654,14 +777,16 @@ class Gen8:
         P.V and the prefetch of the next MFMA phase's first fragments."""
         em = self.em
 
-        def body(masked):
+        def body(st):
+            live = tuple(qb for qb in (0, 1) if st[qb] != "D")
+            masked = tuple(qb for qb in (0, 1) if st[qb] == "M")
             if masked:
-                self.emit_mask()
+                self.emit_mask(masked)
             if first:
-                self.emit_rowmax_init()
-            self.emit_softmax()
+                self.emit_rowmax_init(live)
+            self.emit_softmax(live)
 
-        self.emit_masked_branch(body, "f" if first else "")
+        self.emit_state_branch(body, "f" if first else "")
         if first:
             self.emit_l(first=True)
         else:
@@ -674,6 +799,34 @@ class Gen8:
         self.prefetch(list(next_frags))
         em.salu(f"s_add_u32 {self.s_k0}, {self.s_k0}, 32")
         em.salu("s_barrier")
+
+    def zero_dead_blocks(self):
+        """O^T of a query block none of whose rows sees a key (dl_b < 0, only
+        with a causal mask and Sq > Skv) is never accumulated into: clear it
+        (out of line, MFMAs of zero operands)."""
+        em = self.em
+        l_z, l_back = self.lab("zero"), self.lab("zback")
+        em.salu(f"s_cmp_lt_i32 {self.s_dl[0]}, 0")
+        em.salu(f"s_cbranch_scc1 {l_z}")
+        snap = em.snapshot()
+        em.label(l_back)
+
+        def body():
+            Z = self.v_R[2]
+            for i in range(4):
+                em.valu(f"v_mov_b32 {Z.r(i)}, 0", dst=[Z.r(i)])
+            for qb in range(2):
+                l_skip = self.lab("zskip")
+                em.salu(f"s_cmp_lt_i32 {self.s_dl[qb]}, 0")
+                em.salu(f"s_cbranch_scc0 {l_skip}")
+                for db in range(self.NDB):
+                    em.mfma(self.mfma_op, str(self.a_O[qb][db]), str(Z), str(Z), "0")
+                em.drain()
+                em.label(l_skip)
+            em.drain()
+            em.salu(f"s_branch {l_back}")
+
+        self.deferred.append((snap, l_z, None, body))
 
     def set_kb(self, tile):
         """v_kb = K operand base of the tile index in sgpr `tile`."""
@@ -782,6 +935,7 @@ class Gen8:
         em.drain()
         em.salu(f"s_waitcnt vmcnt({4 * (AHEAD - 1)})")     # Q and tile 0
         em.salu("s_barrier")
+        self.zero_dead_blocks()
         self.prefetch(self.qk_frags(0))
         # waves 4-7 run one phase behind
         l_g0 = self.lab("g0")
@@ -790,10 +944,10 @@ class Gen8:
         em.salu("s_barrier")
         em.label(l_g0)
         # ---- tile 0 -------------------------------------------------------------------
-        self.m_phase(self.qk_frags(0))
+        self.m_phase_sel([], self.qk_frags(0))
         em.salu("s_barrier")
         self.v_phase(0, first=True, next_frags=self.pv_frags(0))
-        self.m_phase(self.pv_frags(0) + self.qk_frags(1), first_pv=True)
+        self.m_phase_sel(self.pv_frags(0), self.qk_frags(1), first_pv=True)
         em.salu(f"s_waitcnt vmcnt({4})")                    # tile 1
         em.salu("s_barrier")
         self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
@@ -804,10 +958,10 @@ class Gen8:
         em.salu(f"s_cmp_ge_u32 {self.s_u}, {self.s_ntiles}")
         em.salu(f"s_cbranch_scc1 {l_last}")
         self.set_kb(self.s_u)
-        self.m_phase(self.pv_frags(1) + self.qk_frags(0))
+        self.m_phase_sel(self.pv_frags(1), self.qk_frags(0))
         em.salu("s_barrier")
         self.v_phase(0, next_frags=self.pv_frags(0), vb_tile=self.s_u)
-        self.m_phase(self.pv_frags(0) + self.qk_frags(1))
+        self.m_phase_sel(self.pv_frags(0), self.qk_frags(1))
         em.salu(f"s_waitcnt vmcnt({4})")                    # tile u+1
         em.salu("s_barrier")
         self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
@@ -816,7 +970,7 @@ class Gen8:
         em.salu(f"s_branch {l_loop}")
         # ---- last P.V, epilogue ------------------------------------------------------
         em.label(l_last)
-        self.m_phase(self.pv_frags(1))
+        self.m_phase_sel(self.pv_frags(1), [])
         em.salu("s_barrier")
         self.epilogue()
         l_g1 = self.lab("g1")
