@@ -16,9 +16,9 @@ the visible keys of its kv-head, in tiles of 64 keys):
 
 * Eight waves, two per SIMD (waves w and w+4 share one).  Wave w owns the
   32-row query blocks w and 15-w of the 512-row tile (a causal diagonal then
-  costs every wave about the same), 64 rows in all: O^T (128 AGPRs) and Q
-  (64 AGPRs) stay in registers, 64 VGPRs hold S/P (32), a ring of three MFMA
-  operand buffers (12) and the rest.
+  costs every wave about the same), 64 rows in all: O^T (128 VGPRs) and Q
+  (64 AGPRs) stay in registers, 64 more VGPRs hold S/P (32), a ring of three
+  MFMA operand buffers (12) and the rest: 256 registers, two waves per SIMD.
 * Each wave alternates an MFMA phase (P.V of sub-tile j-1 then S^T = K.Q^T
   of sub-tile j: 32 MFMAs, operands streamed from LDS through the ring) and
   a softmax phase (exponentials, row sums, conversion of P, in place).
@@ -85,8 +85,8 @@ class Gen8:
 
     # ------------------------------------------------------------------------
     def alloc(self):
-        V = Alloc("v", 0, 64)
-        A = Alloc("a", 0, 192)
+        V = Alloc("v", 0, 192)
+        A = Alloc("a", 0, 64)
         S = Alloc("s", 28, 102)
         r = self.__dict__
         r["v_lane"] = V.take("lane", 1)        # v0: lane id (after kernel_setup)
@@ -102,12 +102,16 @@ class Gen8:
         r["v_l"] = V.take("l", 2)              # per-lane partial row sums
         r["v_rs"] = V.take("rs", 2)            # partial row sums of the current sub-tile
         r["v_t"] = V.take("tmp", 5)
-        self.nvgpr = 64
         assert V.next <= 64, V.next
-        r["a_O"] = [[A.take(f"O{q}{d}", 16, 4) for d in range(self.NDB)] for q in range(2)]
+        V.next = 64
+        # O^T accumulators in VGPRs (the epilogue and the slow path scale them
+        # in place), Q in AGPRs (only ever an MFMA operand)
+        r["v_O"] = [[V.take(f"O{q}{d}", 16, 4) for d in range(self.NDB)] for q in range(2)]
+        self.nvgpr = 192
+        assert V.next == 192
         r["a_Q"] = [[A.take(f"Q{q}{s}", 4, 4) for s in range(self.NS)] for q in range(2)]
-        self.nagpr = 192
-        assert A.next == 192
+        self.nagpr = 64
+        assert A.next == 64
         t = S.take
         r["s_hq"], r["s_qt"], r["s_b"], r["s_hk"] = t("hq", 1), t("qt", 1), t("b", 1), t("hk", 1)
         r["s_w"], r["s_q0"], r["s_off"], r["s_ntiles"] = t("w", 1), t("q0", 1), t("off", 1), t("nt", 1)
@@ -419,9 +423,11 @@ class Gen8:
         at v_vb): two transposing reads.  Returns (reads(buf, tmp), mfmas(buf))."""
         em = self.em
 
-        def reads(buf, tmp):
+        def reads(buf, _tmp):
             R = self.v_R[buf]
-            em.valu(f"v_xor_b32 {tmp}, {db << 6}, {self.v_vb}", dst=[tmp], src=[str(self.v_vb)])
+            tmp = self.v_t.r(2 + db % 2)
+            if th == 0:
+                em.valu(f"v_xor_b32 {tmp}, {db << 6}, {self.v_vb}", dst=[tmp], src=[str(self.v_vb)])
             for e in range(2):
                 off = (32 * kb + 16 * th + 8 * e) * self.ROW
                 em.ds_read(f"ds_read_b64_tr_b16 {R.r(2 * e, 2)}, {tmp} offset:{off}", R.r(2 * e, 2), tmp)
@@ -442,7 +448,7 @@ class Gen8:
         R = str(self.v_R[buf])
         if tag[0] == "v":
             _, db, th = tag
-            o = str(self.a_O[qb][db])
+            o = str(self.v_O[qb][db])
             c = "0" if (first_pv and th == 0) else o
             em.mfma(self.mfma_op, o, R, self.v_S[qb].r(4 * th, 4), c)
         else:
@@ -756,12 +762,9 @@ class Gen8:
                 em.valu(f"v_mov_b32 {mc}, {mx}", dst=[mc], src=[mx])
                 em.valu(f"v_mul_f32 {l}, {l}, {a}", dst=[l], src=[l, a])
                 for db in range(self.NDB):
-                    blk = self.a_O[qb][db]
+                    blk = self.v_O[qb][db]
                     for i in range(16):
-                        tr = self.v_R[0].r(i & 3)
-                        em.valu(f"v_accvgpr_read_b32 {tr}, {blk.r(i)}", dst=[tr], src=[blk.r(i)])
-                        em.valu(f"v_mul_f32 {tr}, {tr}, {a}", dst=[tr], src=[tr, a])
-                        em.valu(f"v_accvgpr_write_b32 {blk.r(i)}, {tr}", dst=[blk.r(i)], src=[tr])
+                        em.valu(f"v_mul_f32 {blk.r(i)}, {blk.r(i)}, {a}", dst=[blk.r(i)], src=[blk.r(i), a])
             self.emit_softmax()
             self.emit_l()
             em.drain()
@@ -820,7 +823,7 @@ class Gen8:
                 em.salu(f"s_cmp_lt_i32 {self.s_dl[qb]}, 0")
                 em.salu(f"s_cbranch_scc0 {l_skip}")
                 for db in range(self.NDB):
-                    em.mfma(self.mfma_op, str(self.a_O[qb][db]), str(Z), str(Z), "0")
+                    em.mfma(self.mfma_op, str(self.v_O[qb][db]), str(Z), str(Z), "0")
                 em.drain()
                 em.label(l_skip)
             em.drain()
@@ -872,27 +875,26 @@ class Gen8:
             em.valu(f"v_mul_lo_u32 {t.r(2)}, {u.r(0)}, {self.s_x[0]}", dst=[t.r(2)], src=[u.r(0)])
             em.valu(f"v_add_u32 {t.r(2)}, {t.r(2)}, {t.r(3)}", dst=[t.r(2)], src=[t.r(2), t.r(3)])
             for db in range(self.NDB):
-                blk = self.a_O[qb][db]
+                blk = self.v_O[qb][db]
                 for jp in range(2):
                     k = 2 * db + jp
                     Fk, o = F[k % 2], 8 + 4 * ((k // 2) % 2)
-                    for jj in range(2):
-                        j = 2 * jp + jj
-                        for r in range(4):
-                            dst = Fk.r(4 * jj + r)
-                            if empty:
-                                em.valu(f"v_mov_b32 {dst}, 0", dst=[dst])
-                            else:
-                                em.valu(f"v_accvgpr_read_b32 {dst}, {blk.r(4 * j + r)}", dst=[dst],
-                                        src=[blk.r(4 * j + r)])
-                                em.valu(f"v_mul_f32 {dst}, {dst}, {t.r(1)}", dst=[dst], src=[dst, t.r(1)])
+                    if empty:
+                        for c in range(4):
+                            em.valu(f"v_mov_b32 {Fk.r(o + c)}, 0", dst=[Fk.r(o + c)])
+                    else:
+                        for jj in range(2):
+                            j = 2 * jp + jj
+                            for r in range(4):
+                                x_ = blk.r(4 * j + r)
+                                em.valu(f"v_mul_f32 {x_}, {x_}, {t.r(1)}", dst=[x_], src=[x_, t.r(1)])
+                            for c in range(2):
+                                a, b = blk.r(4 * j + 2 * c), blk.r(4 * j + 2 * c + 1)
+                                em.valu(f"{self.cvt_op} {Fk.r(o + 2 * jj + c)}, {a}, {b}",
+                                        dst=[Fk.r(o + 2 * jj + c)], src=[a, b])
                         for c in range(2):
-                            a, b = Fk.r(4 * jj + 2 * c), Fk.r(4 * jj + 2 * c + 1)
-                            em.valu(f"{self.cvt_op} {Fk.r(o + 2 * jj + c)}, {a}, {b}",
-                                    dst=[Fk.r(o + 2 * jj + c)], src=[a, b])
-                    for c in range(2):
-                        xx, yy = Fk.r(o + c), Fk.r(o + 2 + c)
-                        em.valu(f"v_permlane32_swap_b32 {xx}, {yy}", dst=[xx, yy], src=[xx, yy])
+                            xx, yy = Fk.r(o + c), Fk.r(o + 2 + c)
+                            em.valu(f"v_permlane32_swap_b32 {xx}, {yy}", dst=[xx, yy], src=[xx, yy])
                     em.vmem(f"buffer_store_dwordx4 {Fk.r(o, 4)}, {t.r(2)}, {self.s_ro}, 0 offen "
                             f"offset:{64 * db + 32 * jp}", src=[Fk.r(o, 4), t.r(2)])
             # LSE
