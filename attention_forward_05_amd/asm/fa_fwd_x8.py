@@ -73,8 +73,9 @@ class Gen8:
         self.DPW = (BN // WAVES) // self.RPD  # DMA instructions per wave per K (or V) tile
         self.KREG = 0
         self.VREG = SLOTS * self.TILE
-        self.LDS = 2 * SLOTS * self.TILE
-        assert self.VREG == 65536 and self.DPW == 2
+        self.DUMP = 2 * SLOTS * self.TILE    # spare K and V tile for all-zero tiles
+        self.LDS = self.DUMP + 2 * self.TILE
+        assert self.VREG == 65536 and self.DPW == 2 and self.LDS <= 160 * 1024
         self.em = Emitter()
         self._lab = 0
         self.deferred = []
@@ -113,8 +114,9 @@ class Gen8:
         self.nagpr = 64
         assert A.next == 64
         t = S.take
+        # the current item
         r["s_hq"], r["s_qt"], r["s_b"], r["s_hk"] = t("hq", 1), t("qt", 1), t("b", 1), t("hk", 1)
-        r["s_w"], r["s_q0"], r["s_off"], r["s_ntiles"] = t("w", 1), t("q0", 1), t("off", 1), t("nt", 1)
+        r["s_w"], r["s_off"], r["s_ntiles"] = t("w", 1), t("off", 1), t("nt", 1)
         r["s_rowlim"], r["s_rowb"], r["s_u"] = t("rowlim", 1), t("rowb", 1), t("u", 1)
         # per query block b: sub-tiles whose first key k0 <= fu_b are seen in
         # full by every row of the block; k0 > dl_b by none of them
@@ -124,21 +126,23 @@ class Gen8:
         r["s_ro"] = t("ro", 4, 4)
         r["s_rl"] = t("rl", 4, 4)
         r["s_rk"] = t("rk", 4, 4)
-        r["s_rq"] = r["s_rk"]                  # Q loads are issued before the first K descriptor
+        r["s_rq"] = r["s_rk"]                  # Q loads are issued before a K descriptor is built
         r["s_rv"] = t("rv", 4, 4)
         r["s_g"], r["s_r"] = t("wg", 1), t("round", 1)
-        r["s_nitems"], r["s_P"] = t("nitems", 1), t("pairs", 1)
         r["s_kbase"] = t("kbase", 2, 2)
         r["s_vbase"] = t("vbase", 2, 2)
         r["s_k0"] = t("k0", 1)                 # first key of the current softmax sub-tile
-        r["s_kdw"], r["s_vdw"], r["s_wrow"] = t("kdw", 1), t("vdw", 1), t("wrow", 1)
+        r["s_wrow"] = t("wrow", 1)
+        r["s_ring"] = t("ring", 1)             # LDS slot of the item's tile 0
+        # the next item: ids, K/V bases, row limit and tile count (0: none)
+        r["s_nb"], r["s_nhq"], r["s_nqt"] = t("nb", 1), t("nhq", 1), t("nqt", 1)
+        r["s_nkb"] = t("nkb", 2, 2)
+        r["s_nvb"] = t("nvb", 2, 2)
+        r["s_nrl"], r["s_nnt"] = t("nrl", 1), t("nnt", 1)
         r["s_x"] = [t(f"x{i}", 1) for i in range(6)]
         r["s_y"] = [t(f"y{i}", 1) for i in range(6)]
         r["s_m1"], r["s_m2"] = t("msk1", 2, 2), t("msk2", 2, 2)
-        r["s_or"] = t("orpair", 2, 2)
-        r["s_neg"] = t("neginf", 1)
         r["s_thr"] = t("thr", 1)
-        r["s_row"] = t("row", 1)
         self.nsgpr = S.next
 
     # ------------------------------------------------------------------------
@@ -153,25 +157,20 @@ class Gen8:
         em.valu("v_and_b32 v0, 63, v0", dst=["v0"], src=["v0"])
         em.salu(f"s_mov_b32 {self.s_g}, s2")
         em.salu(f"s_mov_b32 {self.s_r}, 0")
+        em.salu(f"s_mov_b32 {self.s_ring}, 0")
         em.salu("s_waitcnt lgkmcnt(0)")
-        em.salu(f"s_mov_b32 {self.s_neg}, 0xff800000")
         em.salu(f"s_mov_b32 {self.s_thr}, {f32_hex(THRESH)}")
-        em.salu(f"s_mov_b32 {self.s_row}, {self.ROW}")
         em.salu(f"s_mul_i32 {self.s_rowb}, s22, {D * 2}")          # K/V row stride
-        em.salu(f"s_mul_i32 {self.s_P}, s18, s21")                 # (batch, head) pairs
-        em.salu(f"s_and_b32 {self.s_x[0]}, s25, 0xffff")           # query tiles
-        em.salu(f"s_mul_i32 {self.s_nitems}, {self.s_P}, {self.s_x[0]}")
         em.salu(f"s_mul_i32 {self.s_wrow}, {self.s_w}, {(BN // WAVES) * self.ROW}")
 
     def tmps(self):
         """Scratch VGPRs for set-up code (the S registers are free then)."""
         return [self.v_S[i // 16].r(i % 16) for i in range(32)]
 
-    def emit_div(self, num, den, q, rem, t):
+    def emit_div(self, num, den, q, rem, dv, z):
         """q = num / den, rem = num - q*den for num, den < 2^24 (VGPR num,
         SGPR den): float reciprocal estimate, then one correction each way."""
         em = self.em
-        dv, z = t[0], t[1]
         em.valu(f"v_mov_b32 {dv}, {den}", dst=[dv])
         em.valu(f"v_cvt_f32_u32 {q}, {num}", dst=[q], src=[num])
         em.valu(f"v_cvt_f32_u32 {rem}, {dv}", dst=[rem], src=[dv])
@@ -235,66 +234,96 @@ class Gen8:
         em.valu(f"v_xor_b32 {t[4]}, {t[4]}, {t[3]}", dst=[t[4]], src=[t[4], t[3]])
         em.valu(f"v_and_b32 {t[5]}, 1, {lane}", dst=[t[5]], src=[lane])
         em.valu(f"v_lshlrev_b32 {t[5]}, 3, {t[5]}", dst=[t[5]], src=[t[5]])
-        em.valu(f"v_mad_u32_u24 {t[5]}, {t[2]}, {self.s_row}, {t[5]}", dst=[t[5]], src=[t[2], t[5]])
+        em.salu(f"s_mov_b32 {self.s_x[0]}, {self.ROW}")
+        em.valu(f"v_mad_u32_u24 {t[5]}, {t[2]}, {self.s_x[0]}, {t[5]}", dst=[t[5]], src=[t[2], t[5]])
         em.valu(f"v_lshl_add_u32 {t[5]}, {t[4]}, 4, {t[5]}", dst=[t[5]], src=[t[4], t[5]])
         em.valu(f"v_add_u32 {self.v_vlane}, {self.VREG}, {t[5]}", dst=[str(self.v_vlane)], src=[t[5]])
 
-    def item_setup(self, l_exit):
-        """Decode this round's item; rows, key range, thresholds, resources."""
-        em, D = self.em, self.D
-        x = self.s_x
-        t = self.tmps()
+    # Items (batch, q-head, 512-row query tile) in decreasing key count;
+    # workgroup g of G takes item r*G + (g or G-1-g, by the parity of round r).
+    def decode(self, rsg, out, l_none):
+        """(b, hq, qt) of the item of round `rsg` (sgpr) into the sgprs `out`;
+        branches to l_none when there is no such item.  Uses the v_t temps."""
+        em, x, t = self.em, self.s_x, self.v_t
+        ob, ohq, oqt = out
         em.salu(f"s_lshr_b32 {x[1]}, s25, 16")                     # G
-        em.salu(f"s_mul_i32 {x[0]}, {self.s_r}, {x[1]}")
-        em.salu(f"s_sub_u32 {x[2]}, {x[1]}, 1")
-        em.salu(f"s_sub_u32 {x[2]}, {x[2]}, {self.s_g}")
-        em.salu(f"s_bitcmp1_b32 {self.s_r}, 0")
-        em.salu(f"s_cselect_b32 {x[2]}, {x[2]}, {self.s_g}")
-        em.salu(f"s_add_u32 {x[0]}, {x[0]}, {x[2]}")                # idx
-        em.salu(f"s_cmp_ge_u32 {x[0]}, {self.s_nitems}")
-        em.salu(f"s_cbranch_scc1 {l_exit}")
-        em.valu(f"v_mov_b32 {t[2]}, {x[0]}", dst=[t[2]])
-        self.emit_div(t[2], self.s_P, t[3], t[4], t[8:10])
-        self.emit_div(t[4], "s21", t[5], t[6], t[8:10])
-        em.valu(f"v_readfirstlane_b32 {x[3]}, {t[3]}", src=[t[3]])       # level
-        em.valu(f"v_readfirstlane_b32 {self.s_b}, {t[5]}", src=[t[5]])   # b
-        em.valu(f"v_readfirstlane_b32 {x[4]}, {t[6]}", src=[t[6]])       # head slot
+        em.salu(f"s_mul_i32 {x[2]}, {rsg}, {x[1]}")
+        em.salu(f"s_sub_u32 {x[3]}, {x[1]}, 1")
+        em.salu(f"s_sub_u32 {x[3]}, {x[3]}, {self.s_g}")
+        em.salu(f"s_bitcmp1_b32 {rsg}, 0")
+        em.salu(f"s_cselect_b32 {x[3]}, {x[3]}, {self.s_g}")
+        em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[3]}")                # idx
+        em.salu(f"s_mul_i32 {x[4]}, s18, s21")                      # (batch, head) pairs
+        em.salu(f"s_and_b32 {x[5]}, s25, 0xffff")                   # query tiles
+        em.salu(f"s_mul_i32 {x[1]}, {x[4]}, {x[5]}")
+        em.salu(f"s_cmp_ge_u32 {x[2]}, {x[1]}")
+        em.salu(f"s_cbranch_scc1 {l_none}")
+        em.valu(f"v_mov_b32 {t.r(0)}, {x[2]}", dst=[t.r(0)])
+        self.emit_div(t.r(0), x[4], t.r(1), t.r(2), t.r(3), t.r(4))        # level, within
+        em.valu(f"v_readfirstlane_b32 {x[3]}, {t.r(1)}", src=[t.r(1)])
+        self.emit_div(t.r(2), "s21", t.r(3), t.r(4), t.r(0), t.r(1))       # b, head slot
+        em.valu(f"v_readfirstlane_b32 {ob}, {t.r(3)}", src=[t.r(3)])
+        em.valu(f"v_readfirstlane_b32 {x[4]}, {t.r(4)}", src=[t.r(4)])
         # hq: contiguous head groups over the 8 XCDs
         em.salu("s_cmp_eq_u32 s27, 0")
-        em.salu(f"s_cselect_b32 {x[5]}, 0, 7")
-        em.salu(f"s_and_b32 {self.s_hq}, {x[4]}, {x[5]}")
-        em.salu(f"s_mul_i32 {self.s_hq}, {self.s_hq}, s27")
+        em.salu(f"s_cselect_b32 {x[2]}, 0, 7")
+        em.salu(f"s_and_b32 {ohq}, {x[4]}, {x[2]}")
+        em.salu(f"s_mul_i32 {ohq}, {ohq}, s27")
         em.salu("s_cmp_eq_u32 s27, 0")
-        em.salu(f"s_cselect_b32 {x[5]}, 0, 3")
-        em.salu(f"s_lshr_b32 {x[5]}, {x[4]}, {x[5]}")
-        em.salu(f"s_add_u32 {self.s_hq}, {self.s_hq}, {x[5]}")
+        em.salu(f"s_cselect_b32 {x[2]}, 0, 3")
+        em.salu(f"s_lshr_b32 {x[2]}, {x[4]}, {x[2]}")
+        em.salu(f"s_add_u32 {ohq}, {ohq}, {x[2]}")
         # query tile: longest causal tiles first
-        em.salu(f"s_and_b32 {x[5]}, s25, 0xffff")
         em.salu(f"s_sub_u32 {x[5]}, {x[5]}, 1")
         em.salu(f"s_sub_u32 {x[5]}, {x[5]}, {x[3]}")
         em.salu("s_cmp_eq_u32 s23, 0")
-        em.salu(f"s_cselect_b32 {self.s_qt}, {x[3]}, {x[5]}")
-        em.salu(f"s_mul_i32 {self.s_hk}, {self.s_hq}, s26")
-        em.salu(f"s_lshr_b32 {self.s_hk}, {self.s_hk}, 20")
-        # rows: q0 = 512 qt; blocks w and 15-w of 32 rows
-        em.salu(f"s_lshl_b32 {self.s_q0}, {self.s_qt}, 9")
-        em.salu(f"s_lshl_b32 {x[0]}, {self.s_w}, 5")
-        em.salu(f"s_add_u32 {self.s_rb[0]}, {self.s_q0}, {x[0]}")
-        em.salu(f"s_sub_u32 {self.s_rb[1]}, {self.s_q0}, {x[0]}")
-        em.salu(f"s_add_u32 {self.s_rb[1]}, {self.s_rb[1]}, {32 * 15}")
-        em.salu(f"s_sub_i32 {self.s_off}, s20, s19")              # Skv - Sq
-        # key tiles: kv_end = causal ? min(Skv, min(q0 + 512, Sq) + off) : Skv
-        em.salu(f"s_add_u32 {x[0]}, {self.s_q0}, {BM}")
+        em.salu(f"s_cselect_b32 {oqt}, {x[3]}, {x[5]}")
+
+    def kv_range(self, qt, nt, rowlim):
+        """Key tiles of query tile qt: kv_end = causal ? min(Skv, min(512 qt + 512,
+        Sq) + Skv - Sq) : Skv; nt = ceil(kv_end / 64), rowlim = min(64 nt, Skv)."""
+        em, x = self.em, self.s_x
+        em.salu(f"s_lshl_b32 {x[0]}, {qt}, 9")
+        em.salu(f"s_add_u32 {x[0]}, {x[0]}, {BM}")
         em.salu(f"s_min_i32 {x[0]}, {x[0]}, s19")
-        em.salu(f"s_add_i32 {x[0]}, {x[0]}, {self.s_off}")
+        em.salu(f"s_sub_i32 {x[1]}, s20, s19")
+        em.salu(f"s_add_i32 {x[0]}, {x[0]}, {x[1]}")
         em.salu(f"s_min_i32 {x[0]}, {x[0]}, s20")
         em.salu("s_cmp_eq_u32 s23, 0")
         em.salu(f"s_cselect_b32 {x[0]}, s20, {x[0]}")
         em.salu(f"s_max_i32 {x[0]}, {x[0]}, 0")
         em.salu(f"s_add_u32 {x[0]}, {x[0]}, {BN - 1}")
-        em.salu(f"s_lshr_b32 {self.s_ntiles}, {x[0]}, 6")
-        em.salu(f"s_lshl_b32 {x[0]}, {self.s_ntiles}, 6")
-        em.salu(f"s_min_u32 {self.s_rowlim}, {x[0]}, s20")
+        em.salu(f"s_lshr_b32 {nt}, {x[0]}, 6")
+        em.salu(f"s_lshl_b32 {x[0]}, {nt}, 6")
+        em.salu(f"s_min_u32 {rowlim}, {x[0]}, s20")
+
+    def kv_bases(self, b, hq, kb, vb):
+        """K and V byte bases of (b, kv-head of hq): kv-head = (hq * gmagic) >> 20."""
+        em, x, D = self.em, self.s_x, self.D
+        em.salu(f"s_mul_i32 {x[5]}, {hq}, s26")
+        em.salu(f"s_lshr_b32 {x[5]}, {x[5]}, 20")
+        em.salu(f"s_mul_i32 {x[0]}, {b}, s20")
+        em.salu(f"s_mul_i32 {x[2]}, {x[0]}, {self.s_rowb}")
+        em.salu(f"s_mul_hi_u32 {x[3]}, {x[0]}, {self.s_rowb}")
+        em.salu(f"s_mul_i32 {x[4]}, {x[5]}, {D * 2}")
+        em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[4]}")
+        em.salu(f"s_addc_u32 {x[3]}, {x[3]}, 0")
+        em.salu(f"s_add_u32 {kb.r(0)}, s10, {x[2]}")
+        em.salu(f"s_addc_u32 {kb.r(1)}, s11, {x[3]}")
+        em.salu(f"s_add_u32 {vb.r(0)}, s12, {x[2]}")
+        em.salu(f"s_addc_u32 {vb.r(1)}, s13, {x[3]}")
+
+    def derive(self):
+        """The current item's rows, key range, block thresholds, K/V bases and
+        O / LSE resources, from s_b, s_hq, s_qt."""
+        em, x = self.em, self.s_x
+        em.salu(f"s_lshl_b32 {x[0]}, {self.s_qt}, 9")               # q0
+        em.salu(f"s_lshl_b32 {x[1]}, {self.s_w}, 5")
+        em.salu(f"s_add_u32 {self.s_rb[0]}, {x[0]}, {x[1]}")
+        em.salu(f"s_sub_u32 {self.s_rb[1]}, {x[0]}, {x[1]}")
+        em.salu(f"s_add_u32 {self.s_rb[1]}, {self.s_rb[1]}, {32 * 15}")
+        em.salu(f"s_sub_i32 {self.s_off}, s20, s19")              # Skv - Sq
+        self.kv_range(self.s_qt, self.s_ntiles, self.s_rowlim)
         # block thresholds: a row's last visible key is min(row + off, Skv-1)
         # (causal) or Skv-1; fu_b = that of the block's first row - 31,
         # dl_b = that of its last row
@@ -307,28 +336,33 @@ class Gen8:
             em.salu(f"s_sub_i32 {self.s_fu[qb]}, {self.s_fu[qb]}, 31")
             em.salu(f"s_add_i32 {x[0]}, {x[0]}, 31")
             em.salu(f"s_min_i32 {self.s_dl[qb]}, {x[0]}, {x[1]}")
-        # K/V batch/head bases (bytes)
-        em.salu(f"s_mul_i32 {x[0]}, {self.s_b}, s20")
-        em.salu(f"s_mul_i32 {x[2]}, {x[0]}, {self.s_rowb}")
-        em.salu(f"s_mul_hi_u32 {x[3]}, {x[0]}, {self.s_rowb}")
-        em.salu(f"s_mul_i32 {x[4]}, {self.s_hk}, {D * 2}")
-        em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[4]}")
-        em.salu(f"s_addc_u32 {x[3]}, {x[3]}, 0")
-        em.salu(f"s_add_u32 {self.s_kbase.r(0)}, s10, {x[2]}")
-        em.salu(f"s_addc_u32 {self.s_kbase.r(1)}, s11, {x[3]}")
-        em.salu(f"s_add_u32 {self.s_vbase.r(0)}, s12, {x[2]}")
-        em.salu(f"s_addc_u32 {self.s_vbase.r(1)}, s13, {x[3]}")
-        self.emit_qo_desc(self.s_rq, 8)
+        self.kv_bases(self.s_b, self.s_hq, self.s_kbase, self.s_vbase)
+        self.out_desc()
 
-    def emit_qo_desc(self, rs, base):
-        """Q (base s8) or O (base s14) buffer resource of the item."""
+    def next_info(self, l_done):
+        """Decode the item of round r+1 into s_nb/s_nhq/s_nqt with its K/V
+        bases, row limit and tile count (s_nnt = 0 when there is none)."""
+        em = self.em
+        l_none = self.lab("nonext")
+        em.salu(f"s_add_u32 {self.s_y[0]}, {self.s_r}, 1")
+        self.decode(self.s_y[0], (self.s_nb, self.s_nhq, self.s_nqt), l_none)
+        self.kv_range(self.s_nqt, self.s_nnt, self.s_nrl)
+        self.kv_bases(self.s_nb, self.s_nhq, self.s_nkb, self.s_nvb)
+        em.salu(f"s_branch {l_done}")
+        em.label(l_none)
+        em.salu(f"s_mov_b32 {self.s_nnt}, 0")
+        em.salu(f"s_mov_b32 {self.s_nrl}, 0")
+        em.label(l_done)
+
+    def emit_qo_desc(self, rs, base, b, hq):
+        """Q (base s8) or O (base s14) buffer resource of (b, hq)."""
         em, D, x = self.em, self.D, self.s_x
         em.salu(f"s_mul_i32 {x[0]}, s19, s21")
-        em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, {x[0]}")
-        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
+        em.salu(f"s_mul_i32 {x[4]}, {b}, {x[0]}")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {hq}")
         em.salu(f"s_mul_i32 {x[2]}, {x[4]}, {D * 2}")
         em.salu(f"s_mul_hi_u32 {x[3]}, {x[4]}, {D * 2}")
-        em.salu(f"s_sub_u32 {x[5]}, {x[0]}, {self.s_hq}")
+        em.salu(f"s_sub_u32 {x[5]}, {x[0]}, {hq}")
         em.salu(f"s_mul_i32 {x[5]}, {x[5]}, {D * 2}")
         em.salu(f"s_add_u32 {rs.r(0)}, s{base}, {x[2]}")
         em.salu(f"s_addc_u32 {rs.r(1)}, s{base + 1}, {x[3]}")
@@ -337,9 +371,9 @@ class Gen8:
         em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
 
     def out_desc(self):
-        """O and LSE buffer resources of the item."""
+        """O and LSE buffer resources of the current item."""
         em, x = self.em, self.s_x
-        self.emit_qo_desc(self.s_ro, 14)
+        self.emit_qo_desc(self.s_ro, 14, self.s_b, self.s_hq)
         em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, s21")
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s19")
@@ -360,32 +394,40 @@ class Gen8:
         em.valu(f"v_and_b32 {dst}, 31, v0", dst=[dst], src=["v0"])
         em.valu(f"v_add_u32 {dst}, {self.s_rb[qb]}, {dst}", dst=[dst], src=[dst])
 
-    def load_q(self):
-        """The wave's 64 Q rows straight into the Q AGPRs."""
-        em = self.em
-        t = self.tmps()
-        em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {self.D * 2}")
-        em.valu(f"v_lshrrev_b32 {t[4]}, 5, v0", dst=[t[4]], src=["v0"])
-        em.valu(f"v_lshlrev_b32 {t[4]}, 4, {t[4]}", dst=[t[4]], src=[t[4]])
+    def load_q(self, b, hq, qt):
+        """Q rows of the wave (blocks w and 15-w of query tile qt of (b, hq))
+        straight into the Q AGPRs (16 loads)."""
+        em, x, t = self.em, self.s_x, self.v_t
+        self.emit_qo_desc(self.s_rq, 8, b, hq)
+        em.salu(f"s_mul_i32 {x[0]}, s21, {self.D * 2}")
+        em.salu(f"s_lshl_b32 {x[1]}, {qt}, 9")
+        em.salu(f"s_lshl_b32 {x[2]}, {self.s_w}, 5")
+        em.salu(f"s_add_u32 {x[3]}, {x[1]}, {x[2]}")                 # row base, block 0
+        em.salu(f"s_sub_u32 {x[4]}, {x[1]}, {x[2]}")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {32 * 15}")               # block 1
+        em.valu(f"v_lshrrev_b32 {t.r(2)}, 5, v0", dst=[t.r(2)], src=["v0"])
+        em.valu(f"v_lshlrev_b32 {t.r(2)}, 4, {t.r(2)}", dst=[t.r(2)], src=[t.r(2)])
         for qb in range(2):
-            self.row_of_block(qb, t[0])
-            em.valu(f"v_mul_lo_u32 {t[5 + qb]}, {t[0]}, {self.s_x[0]}", dst=[t[5 + qb]], src=[t[0]])
-            em.valu(f"v_add_u32 {t[5 + qb]}, {t[5 + qb]}, {t[4]}", dst=[t[5 + qb]], src=[t[5 + qb], t[4]])
+            r_ = t.r(qb)
+            em.valu(f"v_and_b32 {r_}, 31, v0", dst=[r_], src=["v0"])
+            em.valu(f"v_add_u32 {r_}, {x[3 + qb]}, {r_}", dst=[r_], src=[r_])
+            em.valu(f"v_mul_lo_u32 {r_}, {r_}, {x[0]}", dst=[r_], src=[r_])
+            em.valu(f"v_add_u32 {r_}, {r_}, {t.r(2)}", dst=[r_], src=[r_, t.r(2)])
         for qb in range(2):
-            for s in range(self.NS):
-                dst = str(self.a_Q[qb][s])
-                em.vmem_load_to(f"buffer_load_dwordx4 {dst}, {t[5 + qb]}, {self.s_rq}, 0 offen offset:{32 * s}",
-                                dst, src=[t[5 + qb]])
+            for s_ in range(self.NS):
+                dst = str(self.a_Q[qb][s_])
+                em.vmem_load_to(f"buffer_load_dwordx4 {dst}, {t.r(qb)}, {self.s_rq}, 0 offen offset:{32 * s_}",
+                                dst, src=[t.r(qb)])
 
     # ------------------------------------------------------------------------
     # K/V DMA
     # ------------------------------------------------------------------------
-    def emit_dma_desc(self, tile):
-        """Buffer resources s_rk / s_rv of the tile index in sgpr `tile`:
-        base = head base + 64*tile*rowb, size = the bytes up to row_lim."""
+    def emit_dma_desc(self, tile, kb, vb, rowlim):
+        """Buffer resources s_rk / s_rv of tile `tile` (sgpr) of the K/V rows at
+        kb / vb: base + 64*tile*rowb, size = the bytes up to rowlim (0 past it)."""
         em, y, rb = self.em, self.s_y, self.s_rowb
         em.salu(f"s_lshl_b32 {y[0]}, {tile}, 6")
-        em.salu(f"s_sub_i32 {y[1]}, {self.s_rowlim}, {y[0]}")
+        em.salu(f"s_sub_i32 {y[1]}, {rowlim}, {y[0]}")
         em.salu(f"s_max_i32 {y[1]}, {y[1]}, 0")
         em.salu(f"s_mul_i32 {y[2]}, {y[1]}, {rb}")
         em.salu(f"s_mul_hi_u32 {y[3]}, {y[1]}, {rb}")
@@ -394,23 +436,41 @@ class Gen8:
         em.salu(f"s_min_u32 {y[2]}, {y[2]}, 0x7fffffff")
         em.salu(f"s_mul_i32 {y[3]}, {y[0]}, {rb}")
         em.salu(f"s_mul_hi_u32 {y[4]}, {y[0]}, {rb}")
-        for rs, bb in ((self.s_rk, self.s_kbase), (self.s_rv, self.s_vbase)):
+        for rs, bb in ((self.s_rk, kb), (self.s_rv, vb)):
             em.salu(f"s_add_u32 {rs.r(0)}, {bb.r(0)}, {y[3]}")
             em.salu(f"s_addc_u32 {rs.r(1)}, {bb.r(1)}, {y[4]}")
             em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
             em.salu(f"s_mov_b32 {rs.r(2)}, {y[2]}")
             em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
 
-    def emit_dma(self, tile):
-        """Issue the wave's 2 K and 2 V row loads of tile index `tile` (sgpr)
-        into LDS slot tile % SLOTS."""
-        em, y = self.em, self.s_y
-        self.emit_dma_desc(tile)
-        em.salu(f"s_and_b32 {y[5]}, {tile}, {SLOTS - 1}")
+    def emit_dma(self, g):
+        """The wave's 2 K and 2 V row loads of stream tile g (sgpr, counted from
+        the current item's tile 0): the current item's tile g when g < n,
+        else the next item's tile g - n.  A tile with keys goes to LDS slot
+        (ring + g) % 4; a tile past its item's last (all zeros) goes to the
+        spare region, so it never overwrites a slot in use."""
+        em, y, x = self.em, self.s_y, self.s_x
+        l_next, l_go, l_slot = self.lab("dnext"), self.lab("dgo"), self.lab("dslot")
+        em.salu(f"s_cmp_lt_u32 {g}, {self.s_ntiles}")
+        em.salu(f"s_cbranch_scc0 {l_next}")
+        self.emit_dma_desc(g, self.s_kbase, self.s_vbase, self.s_rowlim)
+        em.salu(f"s_branch {l_slot}")
+        em.label(l_next)
+        em.salu(f"s_sub_u32 {x[5]}, {g}, {self.s_ntiles}")
+        self.emit_dma_desc(x[5], self.s_nkb, self.s_nvb, self.s_nrl)
+        em.salu(f"s_cmp_lt_u32 {x[5]}, {self.s_nnt}")
+        em.salu(f"s_cbranch_scc1 {l_slot}")
+        em.salu(f"s_add_u32 {y[5]}, {self.s_wrow}, {self.DUMP}")          # K rows of the wave
+        em.salu(f"s_add_u32 {y[1]}, {y[5]}, {self.TILE}")                 # V rows of the wave
+        em.salu(f"s_branch {l_go}")
+        em.label(l_slot)
+        em.salu(f"s_add_u32 {y[5]}, {g}, {self.s_ring}")
+        em.salu(f"s_and_b32 {y[5]}, {y[5]}, {SLOTS - 1}")
         em.salu(f"s_mul_i32 {y[5]}, {y[5]}, {self.TILE}")
-        em.salu(f"s_add_u32 {self.s_kdw}, {y[5]}, {self.s_wrow}")
-        em.salu(f"s_add_u32 {self.s_vdw}, {self.s_kdw}, {self.VREG}")
-        for desc, slot, voff in ((self.s_rk, self.s_kdw, self.v_kdma), (self.s_rv, self.s_vdw, self.v_vdma)):
+        em.salu(f"s_add_u32 {y[5]}, {y[5]}, {self.s_wrow}")              # K rows of the wave
+        em.salu(f"s_add_u32 {y[1]}, {y[5]}, {self.VREG}")                # V rows of the wave
+        em.label(l_go)
+        for desc, slot, voff in ((self.s_rk, y[5], self.v_kdma), (self.s_rv, y[1], self.v_vdma)):
             for i in range(self.DPW):
                 em.salu(f"s_add_u32 m0, {slot}, {self.RPD * i * self.ROW}")
                 em.vmem(f"buffer_load_dwordx4 {voff.r(i)}, {desc}, 0 offen lds", src=[voff.r(i)])
@@ -573,7 +633,7 @@ class Gen8:
         em.salu(f"s_sub_i32 {x[1]}, s20, 1")                                  # Skv - 1
         em.salu("s_cmp_eq_u32 s23, 0")
         em.salu(f"s_cselect_b32 {x[2]}, s20, {self.s_off}")                  # row offset of the limit
-        em.valu(f"v_mov_b32 {ninf}, {self.s_neg}", dst=[ninf])
+        em.valu(f"v_mov_b32 {ninf}, 0xff800000", dst=[ninf])
         for qb in blocks:
             S = self.v_S[qb]
             self.row_of_block(qb, d)
@@ -605,7 +665,7 @@ class Gen8:
             em.valu(f"v_permlane32_swap_b32 {mx}, {tmp}", dst=[mx, tmp], src=[mx, tmp])
             em.valu(f"v_max_f32 {mx}, {mx}, {tmp}", dst=[mx], src=[mx, tmp])
             em.valu(f"v_mul_f32 {mc}, s24, {mx}", dst=[mc], src=[mx])
-            em.valu(f"v_cmp_eq_f32 vcc, {self.s_neg}, {mx}", src=[mx])
+            em.valu(f"v_cmp_eq_f32 vcc, 0xff800000, {mx}", src=[mx])
             em.valu(f"v_cndmask_b32 {mc}, {mc}, 0, vcc", dst=[mc], src=[mc])
 
     def softmax_ops(self, blocks=(0, 1)):
@@ -726,7 +786,7 @@ class Gen8:
         em = self.em
         t = self.v_t
         l_slow, l_back = self.lab("slow"), self.lab("back")
-        em.salu(f"s_or_b64 {self.s_or}, {self.s_m1}, {self.s_m2}")
+        em.salu(f"s_or_b64 {self.s_m1}, {self.s_m1}, {self.s_m2}")
         em.salu(f"s_cbranch_scc1 {l_slow}")
         snap = em.snapshot()
 
@@ -795,6 +855,16 @@ class Gen8:
         else:
             self.emit_slow(kb)
         if dma:
+            # the item's last softmax phase: Q of the next item (the Q AGPRs
+            # are free after the last S^T), ahead of its tile 2
+            l_noq = self.lab("noq")
+            em.salu(f"s_add_u32 {self.s_x[0]}, {self.s_u}, 1")
+            em.salu(f"s_cmp_eq_u32 {self.s_x[0]}, {self.s_ntiles}")
+            em.salu(f"s_cbranch_scc0 {l_noq}")
+            em.salu(f"s_cmp_eq_u32 {self.s_nnt}, 0")
+            em.salu(f"s_cbranch_scc1 {l_noq}")
+            self.load_q(self.s_nb, self.s_nhq, self.s_nqt)
+            em.label(l_noq)
             em.salu(f"s_add_u32 {self.s_y[5]}, {self.s_u}, {AHEAD}")
             self.emit_dma(self.s_y[5])
         if vb_tile is not None:
@@ -832,15 +902,18 @@ class Gen8:
         self.deferred.append((snap, l_z, None, body))
 
     def set_kb(self, tile):
-        """v_kb = K operand base of the tile index in sgpr `tile`."""
+        """v_kb = K operand base of the item's tile `tile` (sgpr or constant)."""
         em, x = self.em, self.s_x[4]
-        em.salu(f"s_and_b32 {x}, {tile}, {SLOTS - 1}")
+        em.salu(f"s_add_u32 {x}, {tile}, {self.s_ring}")
+        em.salu(f"s_and_b32 {x}, {x}, {SLOTS - 1}")
         em.salu(f"s_mul_i32 {x}, {x}, {self.TILE}")
         em.valu(f"v_add_u32 {self.v_kb}, {x}, {self.v_klane}", dst=[str(self.v_kb)], src=[str(self.v_klane)])
 
     def set_vb(self, tile):
+        """v_vb = V operand base of the item's tile `tile` (sgpr or constant)."""
         em, x = self.em, self.s_x[4]
-        em.salu(f"s_and_b32 {x}, {tile}, {SLOTS - 1}")
+        em.salu(f"s_add_u32 {x}, {tile}, {self.s_ring}")
+        em.salu(f"s_and_b32 {x}, {x}, {SLOTS - 1}")
         em.salu(f"s_mul_i32 {x}, {x}, {self.TILE}")
         em.valu(f"v_add_u32 {self.v_vb}, {x}, {self.v_vlane}", dst=[str(self.v_vb)], src=[str(self.v_vlane)])
 
@@ -900,40 +973,46 @@ class Gen8:
             # LSE
             em.valu(f"v_lshlrev_b32 {u.r(1)}, 2, {u.r(0)}", dst=[u.r(1)], src=[u.r(0)])
             if empty:
-                em.valu(f"v_mov_b32 {u.r(2)}, {self.s_neg}", dst=[u.r(2)])
+                em.valu(f"v_mov_b32 {u.r(2)}, 0xff800000", dst=[u.r(2)])
             else:
                 em.valu(f"v_log_f32 {u.r(2)}, {l}", dst=[u.r(2)], src=[l], trans=True)
                 em.valu(f"v_add_f32 {u.r(2)}, {self.v_mc.r(qb)}, {u.r(2)}", dst=[u.r(2)],
                         src=[self.v_mc.r(qb), u.r(2)])
                 em.valu(f"v_mul_f32 {u.r(2)}, {f32_hex(LN2)}, {u.r(2)}", dst=[u.r(2)], src=[u.r(2)])
-                em.valu(f"v_mov_b32 {u.r(3)}, {self.s_neg}", dst=[u.r(3)])
+                em.valu(f"v_mov_b32 {u.r(3)}, 0xff800000", dst=[u.r(3)])
                 em.valu(f"v_cndmask_b32 {u.r(2)}, {u.r(3)}, {u.r(2)}, vcc", dst=[u.r(2)], src=[u.r(2), u.r(3)])
             # one lane per row stores its LSE (lanes >= 32 hold the same rows)
             em.vmem(f"buffer_store_dword {u.r(2)}, {u.r(1)}, {self.s_rl}, 0 offen", src=[u.r(2), u.r(1)])
 
     # ------------------------------------------------------------------------
+    def item_start(self):
+        """Tile counters and operand bases of the (just derived) item."""
+        em = self.em
+        em.salu(f"s_mov_b32 {self.s_u}, 0")
+        em.salu(f"s_mov_b32 {self.s_k0}, 0")
+        self.set_kb(0)
+        self.set_vb(0)
+
     def body(self):
         em = self.em
         self.alloc()
         self.kernel_setup()
         self.lane_consts()
         em.drain()
-        l_item, l_exit, l_empty = self.lab("item"), self.lab("exit"), self.lab("empty")
-        l_loop, l_last = self.lab("loop"), self.lab("last")
-        em.label(l_item)
-        self.item_setup(l_exit)
-        self.out_desc()
+        l_exit, l_empty, l_item = self.lab("exit"), self.lab("empty"), self.lab("item")
+        l_loop, l_last, l_end = self.lab("loop"), self.lab("last"), self.lab("end")
+        # ---- the first item: Q and its tiles 0 .. AHEAD-1 ------------------------
+        # (every item with keys has at least AHEAD tiles: the launcher checks)
+        self.decode(self.s_r, (self.s_b, self.s_hq, self.s_qt), l_exit)
+        self.derive()
         em.salu(f"s_cmp_eq_u32 {self.s_ntiles}, 0")
         em.salu(f"s_cbranch_scc1 {l_empty}")
-        # ---- prologue: Q, tiles 0 .. AHEAD-1 -------------------------------------
-        self.load_q()
+        self.next_info(self.lab("nd"))
+        self.load_q(self.s_b, self.s_hq, self.s_qt)
         for tt in range(AHEAD):
             em.salu(f"s_mov_b32 {self.s_y[5]}, {tt}")
             self.emit_dma(self.s_y[5])
-        em.salu(f"s_mov_b32 {self.s_u}, 0")
-        em.salu(f"s_mov_b32 {self.s_k0}, 0")
-        self.set_kb(self.s_u)
-        self.set_vb(self.s_u)
+        self.item_start()
         em.drain()
         em.salu(f"s_waitcnt vmcnt({4 * (AHEAD - 1)})")     # Q and tile 0
         em.salu("s_barrier")
@@ -945,12 +1024,13 @@ class Gen8:
         em.salu(f"s_cbranch_scc1 {l_g0}")
         em.salu("s_barrier")
         em.label(l_g0)
-        # ---- tile 0 -------------------------------------------------------------------
+        # ---- one item: tile 0 ---------------------------------------------------------
+        em.label(l_item)
         self.m_phase_sel([], self.qk_frags(0))
         em.salu("s_barrier")
         self.v_phase(0, first=True, next_frags=self.pv_frags(0))
         self.m_phase_sel(self.pv_frags(0), self.qk_frags(1), first_pv=True)
-        em.salu(f"s_waitcnt vmcnt({4})")                    # tile 1
+        em.salu("s_waitcnt vmcnt(4)")                       # stream tile 1
         em.salu("s_barrier")
         self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
         em.salu(f"s_add_u32 {self.s_u}, {self.s_u}, 1")
@@ -964,31 +1044,56 @@ class Gen8:
         em.salu("s_barrier")
         self.v_phase(0, next_frags=self.pv_frags(0), vb_tile=self.s_u)
         self.m_phase_sel(self.pv_frags(0), self.qk_frags(1))
-        em.salu(f"s_waitcnt vmcnt({4})")                    # tile u+1
+        em.salu("s_waitcnt vmcnt(4)")                       # stream tile u+1
         em.salu("s_barrier")
         self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
         em.salu(f"s_add_u32 {self.s_u}, {self.s_u}, 1")
         em.drain()
         em.salu(f"s_branch {l_loop}")
-        # ---- last P.V, epilogue ------------------------------------------------------
+        # ---- last P.V; the epilogue phase (the other group's last P.V runs
+        # next to it); then the next item, whose Q and first tiles are in -----
         em.label(l_last)
         self.m_phase_sel(self.pv_frags(1), [])
         em.salu("s_barrier")
         self.epilogue()
+        em.salu(f"s_add_u32 {self.s_ring}, {self.s_ring}, {self.s_ntiles}")
+        em.salu(f"s_and_b32 {self.s_ring}, {self.s_ring}, {SLOTS - 1}")
+        em.salu(f"s_cmp_eq_u32 {self.s_nnt}, 0")
+        em.salu(f"s_cbranch_scc1 {l_end}")
+        em.salu(f"s_mov_b32 {self.s_b}, {self.s_nb}")
+        em.salu(f"s_mov_b32 {self.s_hq}, {self.s_nhq}")
+        em.salu(f"s_mov_b32 {self.s_qt}, {self.s_nqt}")
+        em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        self.derive()
+        self.next_info(self.lab("nd"))
+        self.item_start()
+        self.zero_dead_blocks()
+        # Q of this item (its tile 2 and the previous epilogue's 18 stores came later)
+        em.salu("s_waitcnt vmcnt(22)")
+        self.prefetch(self.qk_frags(0))
+        em.salu("s_barrier")
+        em.drain()
+        em.salu(f"s_branch {l_item}")
+        # ---- end of the items with keys: waves 0-3 balance the barrier count
+        em.label(l_end)
+        em.salu("s_barrier")
         l_g1 = self.lab("g1")
         em.salu(f"s_cmp_ge_u32 {self.s_w}, 4")
         em.salu(f"s_cbranch_scc1 {l_g1}")
         em.salu("s_barrier")
         em.label(l_g1)
         em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        self.decode(self.s_r, (self.s_b, self.s_hq, self.s_qt), l_exit)
+        self.derive()
         em.drain()
-        em.salu(f"s_branch {l_item}")
-        # ---- an item without visible keys ----------------------------------------
+        # ---- items without a visible key (they come after every item with keys)
         em.label(l_empty)
         self.epilogue(empty=True)
         em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
+        self.decode(self.s_r, (self.s_b, self.s_hq, self.s_qt), l_exit)
+        self.derive()
         em.drain()
-        em.salu(f"s_branch {l_item}")
+        em.salu(f"s_branch {l_empty}")
         em.label(l_exit)
         em.salu("s_waitcnt vmcnt(0)")
         em.salu("s_endpgm")

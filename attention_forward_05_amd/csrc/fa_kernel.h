@@ -26,8 +26,9 @@ int64_t work_items(int B, int Sq, int Hq);
 // Query tiles of 256 rows and key tiles of 64 keys.
 int query_tiles(int Sq);
 // Whether the eight-wave kernel (512-row query tiles, D = 128) runs: when its
-// items alone give each of the `cus` compute units one.
-bool use_eight_waves(int B, int Sq, int Hq, int D, int cus);
+// items alone give each of the `cus` compute units one and every item with a
+// visible key spans more than 128 keys.
+bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus);
 int key_tiles(int Skv);
 // Multiplier m with (hq * m) >> 20 == hq / (Hq / Hkv) for every hq < Hq,
 // or false when no 32-bit product does it.

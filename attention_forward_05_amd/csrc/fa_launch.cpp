@@ -3,9 +3,10 @@
 // a code object) and launches them.
 //
 // Two kernel shapes: four waves on 256-row query tiles (every D), and, for
-// D = 128 when the 512-row tiles alone give every compute unit an item,
-// eight waves (two per SIMD, alternating MFMA and softmax phases) on 512-row
-// tiles, which halves the K/V traffic into LDS per FLOP.
+// D = 128 when the 512-row tiles alone give every compute unit an item (and
+// each item with keys spans at least 3 key tiles), eight waves (two per
+// SIMD, alternating MFMA and softmax phases) on 512-row tiles, which halves
+// the K/V traffic into LDS per FLOP and streams K/V tiles across items.
 //
 // The kernels are persistent: the grid has G = min(items, compute units)
 // workgroups, one per CU, and workgroup g takes item r*G + (g or G-1-g,
@@ -20,6 +21,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "fa_kernel.h"
@@ -107,8 +109,19 @@ int64_t work_items(int B, int Sq, int Hq) {
 
 int query_tiles(int Sq) { return (Sq + kBM - 1) / kBM; }
 
-bool use_eight_waves(int B, int Sq, int Hq, int D, int cus) {
-  return D == 128 && (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq >= cus;
+bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
+  if (D != 128 || (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
+  // The eight-wave kernel streams K/V tiles across consecutive items and
+  // needs every item with a visible key to span at least 3 key tiles (more
+  // than 128 keys).  Key ranges grow with the query tile, so the first
+  // query tile with a visible key is the shortest.
+  if (!causal) return Skv > 2 * kBN;
+  const int64_t off = (int64_t)Skv - Sq;
+  for (int64_t q0 = 0; q0 < Sq; q0 += kBM8) {
+    const int64_t end = std::min<int64_t>(Skv, std::min<int64_t>(q0 + kBM8, Sq) + off);
+    if (end > 0) return end > 2 * kBN;
+  }
+  return true;
 }
 int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
 
@@ -116,7 +129,7 @@ hipError_t launch(const LaunchArgs& a) {
   DeviceKernels* dk = nullptr;
   hipError_t e = kernels_for_current_device(&dk);
   if (e != hipSuccess) return e;
-  const bool x8 = use_eight_waves(a.B, a.Sq, a.Hq, a.D, dk->cus);
+  const bool x8 = use_eight_waves(a.B, a.Sq, a.Skv, a.Hq, a.D, a.causal, dk->cus);
   const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
                          : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
   KernArgs ka;

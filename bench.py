@@ -179,7 +179,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=workloads.HEADLINE.name,
                     choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")

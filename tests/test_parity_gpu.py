@@ -155,8 +155,11 @@ X8_CASES = [
     (1, 1000, 1000, 128, 32, True, "bf16"),    # ragged second tile, GQA 4
     (2, 300, 777, 128, 16, False, "bf16"),     # ragged key tail, GQA 8
     (1, 200, 1500, 256, 32, True, "f16"),      # bottom-right mask, Sq < Skv
-    (1, 600, 100, 256, 256, True, "bf16"),     # rows with no visible key
+    (1, 1500, 1300, 128, 128, True, "bf16"),   # rows (and whole blocks) without a key
+    (1, 1600, 1000, 128, 64, True, "bf16"),    # a query tile without any key
     (1, 520, 600, 256, 64, False, "f16"),      # 8-row second query tile
+    (1, 1024, 150, 256, 32, False, "bf16"),    # 3-tile items, two per compute unit
+    (2, 2048, 200, 128, 128, False, "bf16"),   # 4-tile items, four per compute unit
 ]
 
 
