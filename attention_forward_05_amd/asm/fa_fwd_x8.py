@@ -264,10 +264,17 @@ class Gen8:
         self.emit_div(t.r(2), "s21", t.r(3), t.r(4), t.r(0), t.r(1))       # b, head slot
         em.valu(f"v_readfirstlane_b32 {ob}, {t.r(3)}", src=[t.r(3)])
         em.valu(f"v_readfirstlane_b32 {x[4]}, {t.r(4)}", src=[t.r(4)])
-        # hq: contiguous head groups over the 8 XCDs
+        # hq: contiguous head groups over the 8 XCDs.  Workgroup g runs on XCD
+        # g % 8; in odd rounds it takes slot G-1-g's item, whose slot % 8 is
+        # 7 - g % 8 (G and the pair count multiples of 8), so the group index
+        # is flipped there and every round of a workgroup stays on one group
+        # of heads (whose K/V its XCD's L2 holds)
         em.salu("s_cmp_eq_u32 s27, 0")
         em.salu(f"s_cselect_b32 {x[2]}, 0, 7")
         em.salu(f"s_and_b32 {ohq}, {x[4]}, {x[2]}")
+        em.salu(f"s_bitcmp1_b32 {rsg}, 0")
+        em.salu(f"s_cselect_b32 {x[1]}, {x[2]}, 0")
+        em.salu(f"s_xor_b32 {ohq}, {ohq}, {x[1]}")
         em.salu(f"s_mul_i32 {ohq}, {ohq}, s27")
         em.salu("s_cmp_eq_u32 s27, 0")
         em.salu(f"s_cselect_b32 {x[2]}, 0, 3")

@@ -50,7 +50,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
 # the kernels are generated from these sources; a traffic file taken on other
 # sources no longer describes the kernel
 KERNEL_SRCS = [os.path.join(ROOT, "attention_forward_05_amd", "asm", n)
-               for n in ("fa_fwd_gen.py", "regs.py")]
+               for n in ("fa_fwd_gen.py", "fa_fwd_x8.py", "regs.py")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -80,6 +80,26 @@ def measured_traffic(workload_name: str):
     if not entry:
         return None
     return entry.get("bytes_per_launch")
+
+
+def launched_kernel(w: workloads.Workload, cus: int) -> str:
+    """Name of the kernel the library launches for this workload on a device
+    with `cus` compute units (the launcher's rule: the eight-wave D = 128
+    kernel when its 512-row items cover the compute units and every item
+    with keys spans more than 128 keys)."""
+    name = f"fa_fwd_{w.dtype}_d{w.D}_gfx950"
+    if w.D != 128 or -(-w.Sq // 512) * w.B * w.Hq < cus:
+        return name
+    if not w.causal:
+        ok = w.Skv > 128
+    else:
+        ok, off = True, w.Skv - w.Sq
+        for q0 in range(0, w.Sq, 512):
+            end = min(w.Skv, min(q0 + 512, w.Sq) + off)
+            if end > 0:
+                ok = end > 128
+                break
+    return f"fa_fwd_{w.dtype}_d128_x8_gfx950" if ok else name
 
 
 def algorithmic_bytes(w: workloads.Workload) -> int:
@@ -311,7 +331,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_launch_avg_us": round(launch_avg_ms * 1e3, 2),
-            "kernel": f"fa_fwd_{w.dtype}_d{w.D}_gfx950",
+            "kernel": launched_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count),
         },
         "cpu_baseline": cpu,
     }
