@@ -160,6 +160,9 @@ X8_CASES = [
     (1, 520, 600, 256, 64, False, "f16"),      # 8-row second query tile
     (1, 1024, 150, 256, 32, False, "bf16"),    # 3-tile items, two per compute unit
     (2, 2048, 200, 128, 128, False, "bf16"),   # 4-tile items, four per compute unit
+    (22, 512, 300, 12, 4, True, "bf16"),       # Hq % 8 != 0, GQA 3, 264 items: a short last round
+    (8, 1100, 260, 32, 8, False, "f16"),       # 768 items (three rounds), ragged rows and keys
+    (1, 700, 3000, 256, 64, True, "bf16"),     # bottom-right, two query tiles of unequal length
 ]
 
 
