@@ -3,7 +3,7 @@ attention forward library.
 
 This module only marshals arguments: every step of the computation runs in
 the HIP kernel behind the C ABI declared in ``include/fa.h``.  The functions
-carry the C names (``fa_fwd``, ``fa_fwd_f16``, ``fa_strerror``) and take
+carry the C names (``fa_fwd``, ``fa_fwd_f16``, ``fa_fwd_plan``, ``fa_strerror``) and take
 either torch tensors (their device pointers are passed) or raw integer
 addresses.  PyTorch is used for device memory and streams only.
 
@@ -15,16 +15,19 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f16", "fa_strerror", "attention", "FAError",
+__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_plan", "fa_strerror", "attention", "FAError",
            "library_path", "load", "FA_OK", "FA_ERR_INVALID",
-           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "EXPORTED_SYMBOLS"]
+           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_KERNEL_FOUR_WAVE",
+           "FA_KERNEL_EIGHT_WAVE", "EXPORTED_SYMBOLS"]
 
 FA_OK = 0
 FA_ERR_INVALID = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
+FA_KERNEL_FOUR_WAVE = 0
+FA_KERNEL_EIGHT_WAVE = 1
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_strerror")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_plan", "fa_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -56,6 +59,9 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ctypes.c_float, vp]
         fn.restype = i
+    ip = ctypes.POINTER(i)
+    lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, ip, ip]
+    lib.fa_fwd_plan.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -64,6 +70,18 @@ def load():
 
 def fa_strerror(status: int) -> str:
     return load().fa_strerror(int(status)).decode()
+
+
+def fa_fwd_plan(B, Sq, Skv, Hq, D, causal, compute_units):
+    """Host-only query (see include/fa.h): returns (status, kernel,
+    key_ranges) for these sizes on a device with `compute_units` compute
+    units; kernel and key_ranges are None unless status is FA_OK."""
+    kern, ranges = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = load().fa_fwd_plan(int(B), int(Sq), int(Skv), int(Hq), int(D), int(causal),
+                            int(compute_units), ctypes.byref(kern), ctypes.byref(ranges))
+    if st != FA_OK:
+        return st, None, None
+    return st, kern.value, ranges.value
 
 
 def _addr(x):

@@ -44,12 +44,12 @@ KSLOTS = 4        # K tiles held in LDS
 VSLOTS = 5        # V tiles held in LDS
 PREFETCH = 4      # tiles loaded ahead of the tile whose keys are multiplied next
 THRESH = 32768.0  # lazy-rescale trigger: a half-row sum of p above 2^15
-KERNARG_BYTES = 80
+KERNARG_BYTES = 96
 LN2 = 0.6931471805599453
 
 # kernarg offsets
 KA = dict(q=0, k=8, v=16, o=24, lse=32, B=40, Sq=44, Skv=48, Hq=52, Hkv=56,
-          causal=60, c=64, nq_grid=68, gmagic=72, hq_xcd=76)   # nq_grid = nq | G << 16
+          causal=60, c=64, nq_grid=68, gmagic=72, hq_xcd=76, log2split=80)   # nq_grid = nq | G << 16
 
 
 def kernel_name(dtype: str, D: int) -> str:
@@ -1089,7 +1089,7 @@ VARIANTS = [("bf16", 128), ("bf16", 64), ("f16", 128), ("f16", 64)]
 
 def generate_all() -> str:
     """Every kernel of the library: the four-wave variants, then the
-    eight-wave D = 128 variants (fa_fwd_x8)."""
+    eight-wave D = 128 variants (fa_fwd_x8), whole key ranges and split."""
     from .fa_fwd_x8 import Gen8
     texts, metas = [], []
     for dt, D in VARIANTS:
@@ -1097,10 +1097,11 @@ def generate_all() -> str:
         txt, info = g.assemble_text()
         texts.append(txt)
         metas.append(info)
-    for dt in ("bf16", "f16"):
-        txt, info = Gen8(dt).assemble_text()
-        texts.append(txt)
-        metas.append(info)
+    for split in (False, True):
+        for dt in ("bf16", "f16"):
+            txt, info = Gen8(dt, split).assemble_text()
+            texts.append(txt)
+            metas.append(info)
     return "".join(texts) + metadata(metas)
 
 

@@ -50,17 +50,22 @@ AHEAD = 3         # tiles whose loads are in flight ahead of the tile in use
 THRESH = 32768.0  # slow-path trigger: a lane's 16-key partial row sum above 2^15
 
 
-def kernel_name(dtype: str) -> str:
-    return f"fa_fwd_{dtype}_d128_x8_gfx950"
+def kernel_name(dtype: str, split: bool = False) -> str:
+    return f"fa_fwd_{dtype}_d128_x8{'s' if split else ''}_gfx950"
 
 
 class Gen8:
     D = 128
 
-    def __init__(self, dtype: str):
+    def __init__(self, dtype: str, split: bool = False):
         assert dtype in ("bf16", "f16")
         self.dtype = dtype
-        self.name = kernel_name(dtype)
+        # split: every (batch, q-head, query tile) item is cut into 2^log2split
+        # key ranges (kernel argument); each writes its normalised O (fp32)
+        # and LSE to the partial buffers passed as o / lse, which a combine
+        # kernel merges
+        self.split = split
+        self.name = kernel_name(dtype, split)
         self.mfma_op = "v_mfma_f32_32x32x16_bf16" if dtype == "bf16" else "v_mfma_f32_32x32x16_f16"
         self.cvt_op = "v_cvt_pk_bf16_f32" if dtype == "bf16" else "v_cvt_pk_f16_f32"
         D = self.D
@@ -82,7 +87,7 @@ class Gen8:
 
     def lab(self, tag):
         self._lab += 1
-        return f".L{self.dtype}x8_{tag}_{self._lab}"
+        return f".L{self.dtype}x8{'s' if self.split else ''}_{tag}_{self._lab}"
 
     # ------------------------------------------------------------------------
     def alloc(self):
@@ -143,6 +148,10 @@ class Gen8:
         r["s_y"] = [t(f"y{i}", 1) for i in range(6)]
         r["s_m1"], r["s_m2"] = t("msk1", 2, 2), t("msk2", 2, 2)
         r["s_thr"] = t("thr", 1)
+        if self.split:
+            r["s_l2s"] = t("log2split", 1)     # log2 of the key ranges per item
+            r["s_sp"], r["s_nsp"] = t("sp", 1), t("nsp", 1)   # key range of the item / the next
+            r["s_kst"] = t("kstart", 1)        # first key of the item's range
         self.nsgpr = S.next
 
     # ------------------------------------------------------------------------
@@ -158,6 +167,8 @@ class Gen8:
         em.salu(f"s_mov_b32 {self.s_g}, s2")
         em.salu(f"s_mov_b32 {self.s_r}, 0")
         em.salu(f"s_mov_b32 {self.s_ring}, 0")
+        if self.split:
+            em.salu(f"s_load_dword {self.s_l2s}, s[0:1], 0x50")
         em.salu("s_waitcnt lgkmcnt(0)")
         em.salu(f"s_mov_b32 {self.s_thr}, {f32_hex(THRESH)}")
         em.salu(f"s_mul_i32 {self.s_rowb}, s22, {D * 2}")          # K/V row stride
@@ -245,7 +256,7 @@ class Gen8:
         """(b, hq, qt) of the item of round `rsg` (sgpr) into the sgprs `out`;
         branches to l_none when there is no such item.  Uses the v_t temps."""
         em, x, t = self.em, self.s_x, self.v_t
-        ob, ohq, oqt = out
+        ob, ohq, oqt = out[:3]
         em.salu(f"s_lshr_b32 {x[1]}, s25, 16")                     # G
         em.salu(f"s_mul_i32 {x[2]}, {rsg}, {x[1]}")
         em.salu(f"s_sub_u32 {x[3]}, {x[1]}, 1")
@@ -254,6 +265,8 @@ class Gen8:
         em.salu(f"s_cselect_b32 {x[3]}, {x[3]}, {self.s_g}")
         em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[3]}")                # idx
         em.salu(f"s_mul_i32 {x[4]}, s18, s21")                      # (batch, head) pairs
+        if self.split:
+            em.salu(f"s_lshl_b32 {x[4]}, {x[4]}, {self.s_l2s}")     # ... times key ranges
         em.salu(f"s_and_b32 {x[5]}, s25, 0xffff")                   # query tiles
         em.salu(f"s_mul_i32 {x[1]}, {x[4]}, {x[5]}")
         em.salu(f"s_cmp_ge_u32 {x[2]}, {x[1]}")
@@ -261,6 +274,12 @@ class Gen8:
         em.valu(f"v_mov_b32 {t.r(0)}, {x[2]}", dst=[t.r(0)])
         self.emit_div(t.r(0), x[4], t.r(1), t.r(2), t.r(3), t.r(4))        # level, within
         em.valu(f"v_readfirstlane_b32 {x[3]}, {t.r(1)}", src=[t.r(1)])
+        if self.split:
+            # within = key range * pairs + (batch, head) pair
+            em.salu(f"s_mul_i32 {x[0]}, s18, s21")
+            self.emit_div(t.r(2), x[0], t.r(3), t.r(4), t.r(0), t.r(1))    # key range, pair
+            em.valu(f"v_readfirstlane_b32 {out[3]}, {t.r(3)}", src=[t.r(3)])
+            em.valu(f"v_mov_b32 {t.r(2)}, {t.r(4)}", dst=[t.r(2)], src=[t.r(4)])
         self.emit_div(t.r(2), "s21", t.r(3), t.r(4), t.r(0), t.r(1))       # b, head slot
         em.valu(f"v_readfirstlane_b32 {ob}, {t.r(3)}", src=[t.r(3)])
         em.valu(f"v_readfirstlane_b32 {x[4]}, {t.r(4)}", src=[t.r(4)])
@@ -286,7 +305,7 @@ class Gen8:
         em.salu("s_cmp_eq_u32 s23, 0")
         em.salu(f"s_cselect_b32 {oqt}, {x[3]}, {x[5]}")
 
-    def kv_range(self, qt, nt, rowlim):
+    def kv_range(self, qt, nt, rowlim, sp=None, kst=None):
         """Key tiles of query tile qt: kv_end = causal ? min(Skv, min(512 qt + 512,
         Sq) + Skv - Sq) : Skv; nt = ceil(kv_end / 64), rowlim = min(64 nt, Skv)."""
         em, x = self.em, self.s_x
@@ -301,11 +320,26 @@ class Gen8:
         em.salu(f"s_max_i32 {x[0]}, {x[0]}, 0")
         em.salu(f"s_add_u32 {x[0]}, {x[0]}, {BN - 1}")
         em.salu(f"s_lshr_b32 {nt}, {x[0]}, 6")
-        em.salu(f"s_lshl_b32 {x[0]}, {nt}, 6")
-        em.salu(f"s_min_u32 {rowlim}, {x[0]}, s20")
+        if sp is None:
+            em.salu(f"s_lshl_b32 {x[0]}, {nt}, 6")
+            em.salu(f"s_min_u32 {rowlim}, {x[0]}, s20")
+            return
+        # key range sp of 2^log2split: tiles [sp n >> l, (sp+1) n >> l); the
+        # row limit relative to the range's first key kst = 64 * first tile
+        em.salu(f"s_mul_i32 {x[0]}, {sp}, {nt}")
+        em.salu(f"s_lshr_b32 {x[0]}, {x[0]}, {self.s_l2s}")        # first tile
+        em.salu(f"s_add_u32 {x[1]}, {sp}, 1")
+        em.salu(f"s_mul_i32 {x[1]}, {x[1]}, {nt}")
+        em.salu(f"s_lshr_b32 {x[1]}, {x[1]}, {self.s_l2s}")        # end tile
+        em.salu(f"s_sub_u32 {nt}, {x[1]}, {x[0]}")
+        em.salu(f"s_lshl_b32 {kst}, {x[0]}, 6")
+        em.salu(f"s_lshl_b32 {x[1]}, {x[1]}, 6")
+        em.salu(f"s_min_u32 {x[1]}, {x[1]}, s20")
+        em.salu(f"s_sub_u32 {rowlim}, {x[1]}, {kst}")
 
-    def kv_bases(self, b, hq, kb, vb):
-        """K and V byte bases of (b, kv-head of hq): kv-head = (hq * gmagic) >> 20."""
+    def kv_bases(self, b, hq, kb, vb, kst=None):
+        """K and V byte bases of (b, kv-head of hq) (+ kst rows): kv-head =
+        (hq * gmagic) >> 20."""
         em, x, D = self.em, self.s_x, self.D
         em.salu(f"s_mul_i32 {x[5]}, {hq}, s26")
         em.salu(f"s_lshr_b32 {x[5]}, {x[5]}, 20")
@@ -315,6 +349,11 @@ class Gen8:
         em.salu(f"s_mul_i32 {x[4]}, {x[5]}, {D * 2}")
         em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[4]}")
         em.salu(f"s_addc_u32 {x[3]}, {x[3]}, 0")
+        if kst is not None:
+            em.salu(f"s_mul_i32 {x[4]}, {kst}, {self.s_rowb}")
+            em.salu(f"s_mul_hi_u32 {x[5]}, {kst}, {self.s_rowb}")
+            em.salu(f"s_add_u32 {x[2]}, {x[2]}, {x[4]}")
+            em.salu(f"s_addc_u32 {x[3]}, {x[3]}, {x[5]}")
         em.salu(f"s_add_u32 {kb.r(0)}, s10, {x[2]}")
         em.salu(f"s_addc_u32 {kb.r(1)}, s11, {x[3]}")
         em.salu(f"s_add_u32 {vb.r(0)}, s12, {x[2]}")
@@ -330,7 +369,10 @@ class Gen8:
         em.salu(f"s_sub_u32 {self.s_rb[1]}, {x[0]}, {x[1]}")
         em.salu(f"s_add_u32 {self.s_rb[1]}, {self.s_rb[1]}, {32 * 15}")
         em.salu(f"s_sub_i32 {self.s_off}, s20, s19")              # Skv - Sq
-        self.kv_range(self.s_qt, self.s_ntiles, self.s_rowlim)
+        if self.split:
+            self.kv_range(self.s_qt, self.s_ntiles, self.s_rowlim, self.s_sp, self.s_kst)
+        else:
+            self.kv_range(self.s_qt, self.s_ntiles, self.s_rowlim)
         # block thresholds: a row's last visible key is min(row + off, Skv-1)
         # (causal) or Skv-1; fu_b = that of the block's first row - 31,
         # dl_b = that of its last row
@@ -343,7 +385,8 @@ class Gen8:
             em.salu(f"s_sub_i32 {self.s_fu[qb]}, {self.s_fu[qb]}, 31")
             em.salu(f"s_add_i32 {x[0]}, {x[0]}, 31")
             em.salu(f"s_min_i32 {self.s_dl[qb]}, {x[0]}, {x[1]}")
-        self.kv_bases(self.s_b, self.s_hq, self.s_kbase, self.s_vbase)
+        self.kv_bases(self.s_b, self.s_hq, self.s_kbase, self.s_vbase,
+                      self.s_kst if self.split else None)
         self.out_desc()
 
     def next_info(self, l_done):
@@ -352,9 +395,14 @@ class Gen8:
         em = self.em
         l_none = self.lab("nonext")
         em.salu(f"s_add_u32 {self.s_y[0]}, {self.s_r}, 1")
-        self.decode(self.s_y[0], (self.s_nb, self.s_nhq, self.s_nqt), l_none)
-        self.kv_range(self.s_nqt, self.s_nnt, self.s_nrl)
-        self.kv_bases(self.s_nb, self.s_nhq, self.s_nkb, self.s_nvb)
+        if self.split:
+            self.decode(self.s_y[0], (self.s_nb, self.s_nhq, self.s_nqt, self.s_nsp), l_none)
+            self.kv_range(self.s_nqt, self.s_nnt, self.s_nrl, self.s_nsp, self.s_y[1])
+            self.kv_bases(self.s_nb, self.s_nhq, self.s_nkb, self.s_nvb, self.s_y[1])
+        else:
+            self.decode(self.s_y[0], (self.s_nb, self.s_nhq, self.s_nqt), l_none)
+            self.kv_range(self.s_nqt, self.s_nnt, self.s_nrl)
+            self.kv_bases(self.s_nb, self.s_nhq, self.s_nkb, self.s_nvb)
         em.salu(f"s_branch {l_done}")
         em.label(l_none)
         em.salu(f"s_mov_b32 {self.s_nnt}, 0")
@@ -378,8 +426,26 @@ class Gen8:
         em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
 
     def out_desc(self):
-        """O and LSE buffer resources of the current item."""
+        """O and LSE buffer resources of the current item (with key ranges:
+        its slices of the partial buffers, O fp32 [range][B][Hq][Sq][D] and
+        LSE fp32 [range][B][Hq][Sq])."""
         em, x = self.em, self.s_x
+        if self.split:
+            D = self.D
+            em.salu(f"s_mul_i32 {x[4]}, {self.s_sp}, s18")
+            em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_b}")
+            em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s21")
+            em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
+            em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s19")                  # row index
+            for rs, base, rb in ((self.s_ro, 14, D * 4), (self.s_rl, 16, 4)):
+                em.salu(f"s_mul_i32 {x[2]}, {x[4]}, {rb}")
+                em.salu(f"s_mul_hi_u32 {x[3]}, {x[4]}, {rb}")
+                em.salu(f"s_add_u32 {rs.r(0)}, s{base}, {x[2]}")
+                em.salu(f"s_addc_u32 {rs.r(1)}, s{base + 1}, {x[3]}")
+                em.salu(f"s_and_b32 {rs.r(1)}, {rs.r(1)}, 0xffff")
+                em.salu(f"s_mul_i32 {rs.r(2)}, s19, {rb}")
+                em.salu(f"s_mov_b32 {rs.r(3)}, 0x20000")
+            return
         self.emit_qo_desc(self.s_ro, 14, self.s_b, self.s_hq)
         em.salu(f"s_mul_i32 {x[4]}, {self.s_b}, s21")
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hq}")
@@ -881,12 +947,14 @@ class Gen8:
         em.salu("s_barrier")
 
     def zero_dead_blocks(self):
-        """O^T of a query block none of whose rows sees a key (dl_b < 0, only
-        with a causal mask and Sq > Skv) is never accumulated into: clear it
+        """O^T of a query block none of whose rows sees a key of the item's
+        range (dl_b below its first key: a causal mask with Sq > Skv, or a key
+        range past the block's diagonal) is never accumulated into: clear it
         (out of line, MFMAs of zero operands)."""
         em = self.em
+        first = self.s_kst if self.split else 0
         l_z, l_back = self.lab("zero"), self.lab("zback")
-        em.salu(f"s_cmp_lt_i32 {self.s_dl[0]}, 0")
+        em.salu(f"s_cmp_lt_i32 {self.s_dl[0]}, {first}")
         em.salu(f"s_cbranch_scc1 {l_z}")
         snap = em.snapshot()
         em.label(l_back)
@@ -897,7 +965,7 @@ class Gen8:
                 em.valu(f"v_mov_b32 {Z.r(i)}, 0", dst=[Z.r(i)])
             for qb in range(2):
                 l_skip = self.lab("zskip")
-                em.salu(f"s_cmp_lt_i32 {self.s_dl[qb]}, 0")
+                em.salu(f"s_cmp_lt_i32 {self.s_dl[qb]}, {first}")
                 em.salu(f"s_cbranch_scc0 {l_skip}")
                 for db in range(self.NDB):
                     em.mfma(self.mfma_op, str(self.v_O[qb][db]), str(Z), str(Z), "0")
@@ -938,7 +1006,13 @@ class Gen8:
         u = self.v_R[2]
         em.valu(f"v_lshrrev_b32 {t.r(0)}, 5, v0", dst=[t.r(0)], src=["v0"])
         em.valu(f"v_lshlrev_b32 {t.r(3)}, 4, {t.r(0)}", dst=[t.r(3)], src=[t.r(0)])   # 16h
+        # row stride: BSHD output, or the fp32 partial rows of a key range
         em.salu(f"s_mul_i32 {self.s_x[0]}, s21, {self.D * 2}")
+        if self.split:
+            em.salu(f"s_mov_b32 {self.s_x[0]}, {self.D * 4}")
+            if empty:
+                for c in range(4):
+                    em.valu(f"v_mov_b32 {F[0].r(8 + c)}, 0", dst=[F[0].r(8 + c)])
         for qb in range(2):
             l = self.v_l.r(qb)
             if empty:
@@ -954,7 +1028,20 @@ class Gen8:
             self.row_of_block(qb, u.r(0))
             em.valu(f"v_mul_lo_u32 {t.r(2)}, {u.r(0)}, {self.s_x[0]}", dst=[t.r(2)], src=[u.r(0)])
             em.valu(f"v_add_u32 {t.r(2)}, {t.r(2)}, {t.r(3)}", dst=[t.r(2)], src=[t.r(2), t.r(3)])
-            for db in range(self.NDB):
+            for db in range(self.NDB if self.split else 0):
+                # fp32 partial O: lane (l, h) holds dims 32db + 8j + 4h .. +3 in
+                # registers 4j .. 4j+3, 16 contiguous bytes of the row
+                blk = self.v_O[qb][db]
+                for j in range(4):
+                    src = F[0].r(8, 4)
+                    if not empty:
+                        for r in range(4):
+                            x_ = blk.r(4 * j + r)
+                            em.valu(f"v_mul_f32 {x_}, {x_}, {t.r(1)}", dst=[x_], src=[x_, t.r(1)])
+                        src = blk.r(4 * j, 4)
+                    em.vmem(f"buffer_store_dwordx4 {src}, {t.r(2)}, {self.s_ro}, 0 offen "
+                            f"offset:{128 * db + 32 * j}", src=[src, t.r(2)])
+            for db in range(0 if self.split else self.NDB):
                 blk = self.v_O[qb][db]
                 for jp in range(2):
                     k = 2 * db + jp
@@ -992,11 +1079,19 @@ class Gen8:
             em.vmem(f"buffer_store_dword {u.r(2)}, {u.r(1)}, {self.s_rl}, 0 offen", src=[u.r(2), u.r(1)])
 
     # ------------------------------------------------------------------------
+    def cur_ids(self):
+        ids = (self.s_b, self.s_hq, self.s_qt)
+        return ids + (self.s_sp,) if self.split else ids
+
+    def epilogue_stores(self):
+        """Buffer stores one epilogue issues (the vmcnt accounting needs it)."""
+        return 2 * (self.NDB * 4 + 1) if self.split else 2 * (self.NDB * 2 + 1)
+
     def item_start(self):
         """Tile counters and operand bases of the (just derived) item."""
         em = self.em
         em.salu(f"s_mov_b32 {self.s_u}, 0")
-        em.salu(f"s_mov_b32 {self.s_k0}, 0")
+        em.salu(f"s_mov_b32 {self.s_k0}, {self.s_kst if self.split else 0}")
         self.set_kb(0)
         self.set_vb(0)
 
@@ -1010,7 +1105,7 @@ class Gen8:
         l_loop, l_last, l_end = self.lab("loop"), self.lab("last"), self.lab("end")
         # ---- the first item: Q and its tiles 0 .. AHEAD-1 ------------------------
         # (every item with keys has at least AHEAD tiles: the launcher checks)
-        self.decode(self.s_r, (self.s_b, self.s_hq, self.s_qt), l_exit)
+        self.decode(self.s_r, self.cur_ids(), l_exit)
         self.derive()
         em.salu(f"s_cmp_eq_u32 {self.s_ntiles}, 0")
         em.salu(f"s_cbranch_scc1 {l_empty}")
@@ -1070,13 +1165,15 @@ class Gen8:
         em.salu(f"s_mov_b32 {self.s_b}, {self.s_nb}")
         em.salu(f"s_mov_b32 {self.s_hq}, {self.s_nhq}")
         em.salu(f"s_mov_b32 {self.s_qt}, {self.s_nqt}")
+        if self.split:
+            em.salu(f"s_mov_b32 {self.s_sp}, {self.s_nsp}")
         em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
         self.derive()
         self.next_info(self.lab("nd"))
         self.item_start()
         self.zero_dead_blocks()
-        # Q of this item (its tile 2 and the previous epilogue's 18 stores came later)
-        em.salu("s_waitcnt vmcnt(22)")
+        # Q of this item (its tile 2 and the previous epilogue's stores came later)
+        em.salu(f"s_waitcnt vmcnt({4 + self.epilogue_stores()})")
         self.prefetch(self.qk_frags(0))
         em.salu("s_barrier")
         em.drain()
@@ -1090,14 +1187,14 @@ class Gen8:
         em.salu("s_barrier")
         em.label(l_g1)
         em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
-        self.decode(self.s_r, (self.s_b, self.s_hq, self.s_qt), l_exit)
+        self.decode(self.s_r, self.cur_ids(), l_exit)
         self.derive()
         em.drain()
         # ---- items without a visible key (they come after every item with keys)
         em.label(l_empty)
         self.epilogue(empty=True)
         em.salu(f"s_add_u32 {self.s_r}, {self.s_r}, 1")
-        self.decode(self.s_r, (self.s_b, self.s_hq, self.s_qt), l_exit)
+        self.decode(self.s_r, self.cur_ids(), l_exit)
         self.derive()
         em.drain()
         em.salu(f"s_branch {l_empty}")
@@ -1123,7 +1220,7 @@ class Gen8:
                f"\t.amdhsa_kernel {name}"]
         for k, v in [
             ("group_segment_fixed_size", self.LDS), ("private_segment_fixed_size", 0),
-            ("kernarg_size", 80), ("user_sgpr_count", 2),
+            ("kernarg_size", 96), ("user_sgpr_count", 2),
             ("user_sgpr_dispatch_ptr", 0), ("user_sgpr_queue_ptr", 0),
             ("user_sgpr_kernarg_segment_ptr", 1), ("user_sgpr_dispatch_id", 0),
             ("user_sgpr_kernarg_preload_length", 0), ("user_sgpr_kernarg_preload_offset", 0),

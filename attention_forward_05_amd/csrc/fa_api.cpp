@@ -121,6 +121,19 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
              stream);
 }
 
+int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int D, int causal, int compute_units,
+                int* kernel, int* key_ranges) {
+  if (!kernel || !key_ranges) return FA_ERR_INVALID;
+  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || D < 1 || compute_units < 1) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const int l2s = fa::split_log2(B, Sq, Skv, Hq, D, causal, compute_units);
+  const bool x8 = l2s > 0 || fa::use_eight_waves(B, Sq, Skv, Hq, D, causal, compute_units);
+  *kernel = x8 ? FA_KERNEL_EIGHT_WAVE : FA_KERNEL_FOUR_WAVE;
+  *key_ranges = 1 << l2s;
+  return FA_OK;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK:

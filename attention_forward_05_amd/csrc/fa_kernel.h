@@ -34,8 +34,19 @@ int key_tiles(int Skv);
 // or false when no 32-bit product does it.
 bool group_magic(int Hq, int Hkv, uint32_t* magic);
 
-// Enqueue the kernel (loading the code object on first use on the current
+// Key tiles of the shortest 512-row item with a visible key (0: none).
+int64_t min_item_tiles(int Sq, int Skv, int causal);
+// log2 of the key ranges each 512-row item is split into (0: no split).
+int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus);
+
+// Enqueue the kernel(s) (loading the code object on first use on the current
 // device); returns the launch status.
 hipError_t launch(const LaunchArgs& a);
+
+// Merge the partial results of `nsplit` key ranges (O fp32
+// [nsplit][B][Hq][Sq][128], LSE fp32 [nsplit][B][Hq][Sq]) into o (BSHD, the
+// input dtype) and lse ([B][Hq][Sq], may be null).
+hipError_t launch_combine(DType dtype, const float* part_o, const float* part_lse, void* o,
+                          float* lse, int nsplit, int B, int Hq, int Sq, hipStream_t stream);
 
 }  // namespace fa

@@ -7,6 +7,9 @@
 // each item with keys spans at least 3 key tiles), eight waves (two per
 // SIMD, alternating MFMA and softmax phases) on 512-row tiles, which halves
 // the K/V traffic into LDS per FLOP and streams K/V tiles across items.
+// When the 512-row items would leave compute units idle and the key ranges
+// are long, each item's keys are split into 2..16 ranges whose partial
+// results a combine kernel (fa_combine.hip) merges.
 //
 // The kernels are persistent: the grid has G = min(items, compute units)
 // workgroups, one per CU, and workgroup g takes item r*G + (g or G-1-g,
@@ -48,13 +51,16 @@ struct alignas(8) KernArgs {
   uint32_t nq_grid;  // query tiles | workgroups << 16
   uint32_t gmagic;  // hk = (hq * gmagic) >> 20
   uint32_t hq_xcd;  // Hq / 8 when Hq % 8 == 0, else 0
+  uint32_t log2split;  // split kernels: log2 of the key ranges per item
+  uint32_t pad[3];
 };
-static_assert(sizeof(KernArgs) == 80, "kernarg layout of the generated kernels");
+static_assert(sizeof(KernArgs) == 96, "kernarg layout of the generated kernels");
 
-constexpr int kKernels = 6;
-const char* kNames[kKernels] = {"fa_fwd_bf16_d128_gfx950", "fa_fwd_bf16_d64_gfx950",
-                                "fa_fwd_f16_d128_gfx950",  "fa_fwd_f16_d64_gfx950",
-                                "fa_fwd_bf16_d128_x8_gfx950", "fa_fwd_f16_d128_x8_gfx950"};
+constexpr int kKernels = 8;
+const char* kNames[kKernels] = {"fa_fwd_bf16_d128_gfx950",     "fa_fwd_bf16_d64_gfx950",
+                                "fa_fwd_f16_d128_gfx950",      "fa_fwd_f16_d64_gfx950",
+                                "fa_fwd_bf16_d128_x8_gfx950",  "fa_fwd_f16_d128_x8_gfx950",
+                                "fa_fwd_bf16_d128_x8s_gfx950", "fa_fwd_f16_d128_x8s_gfx950"};
 
 struct DeviceKernels {
   bool loaded = false;
@@ -103,25 +109,47 @@ bool group_magic(int Hq, int Hkv, uint32_t* magic) {
   return true;
 }
 
+hipError_t launch_kernel(DeviceKernels* dk, const LaunchArgs& a, int variant, bool x8, int l2s);
+
 int64_t work_items(int B, int Sq, int Hq) {
   return (int64_t)((Sq + kBM - 1) / kBM) * B * Hq;
 }
 
 int query_tiles(int Sq) { return (Sq + kBM - 1) / kBM; }
 
-bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
-  if (D != 128 || (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
-  // The eight-wave kernel streams K/V tiles across consecutive items and
-  // needs every item with a visible key to span at least 3 key tiles (more
-  // than 128 keys).  Key ranges grow with the query tile, so the first
-  // query tile with a visible key is the shortest.
-  if (!causal) return Skv > 2 * kBN;
+int64_t min_item_tiles(int Sq, int Skv, int causal) {
+  // Key ranges grow with the query tile, so the first 512-row query tile
+  // with a visible key is the shortest.
+  if (!causal) return key_tiles(Skv);
   const int64_t off = (int64_t)Skv - Sq;
   for (int64_t q0 = 0; q0 < Sq; q0 += kBM8) {
     const int64_t end = std::min<int64_t>(Skv, std::min<int64_t>(q0 + kBM8, Sq) + off);
-    if (end > 0) return end > 2 * kBN;
+    if (end > 0) return (end + kBN - 1) / kBN;
   }
-  return true;
+  return 0;
+}
+
+bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
+  if (D != 128 || (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
+  // The eight-wave kernel streams K/V tiles across consecutive items and
+  // needs every item with a visible key to span at least 3 key tiles.
+  const int64_t n = min_item_tiles(Sq, Skv, causal);
+  return n == 0 || n >= 3;
+}
+
+int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
+  if (D != 128) return 0;
+  const int64_t items = (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq;
+  if (items >= cus) return 0;
+  const int64_t n = min_item_tiles(Sq, Skv, causal);
+  if (n == 0) return 0;
+  // the fewest key ranges (a power of two, at most 16) that give every
+  // compute unit an item, while each range keeps at least 16 tiles (1024
+  // keys): below that the partial results' traffic outweighs the gain
+  int l = 0;
+  while (l < 4 && (items << l) < cus) ++l;
+  while (l > 0 && n < ((int64_t)16 << l)) --l;
+  return l;
 }
 int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
 
@@ -129,9 +157,36 @@ hipError_t launch(const LaunchArgs& a) {
   DeviceKernels* dk = nullptr;
   hipError_t e = kernels_for_current_device(&dk);
   if (e != hipSuccess) return e;
+  // Split key ranges when the 512-row items leave compute units idle: the
+  // partial results go to a stream-ordered temporary buffer and a combine
+  // kernel merges them into o / lse.
+  const int l2s = split_log2(a.B, a.Sq, a.Skv, a.Hq, a.D, a.causal, dk->cus);
+  if (l2s > 0) {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+    const size_t lse_bytes = (size_t)(rows << l2s) * 4;
+    const size_t o_bytes = lse_bytes * a.D;
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, o_bytes + lse_bytes, a.stream) == hipSuccess) {
+      LaunchArgs p = a;
+      p.o = ws;
+      p.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+      e = launch_kernel(dk, p, a.dtype == DType::kBF16 ? 6 : 7, true, l2s);
+      if (e == hipSuccess)
+        e = launch_combine(a.dtype, static_cast<const float*>(ws), p.lse, a.o, a.lse, 1 << l2s, a.B,
+                           a.Hq, a.Sq, a.stream);
+      const hipError_t f = hipFreeAsync(ws, a.stream);
+      return e != hipSuccess ? e : f;
+    }
+    (void)hipGetLastError();  // no temporary buffer: whole key ranges instead
+  }
   const bool x8 = use_eight_waves(a.B, a.Sq, a.Skv, a.Hq, a.D, a.causal, dk->cus);
   const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
                          : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
+  return launch_kernel(dk, a, variant, x8, 0);
+}
+
+hipError_t launch_kernel(DeviceKernels* dk, const LaunchArgs& a, int variant, bool x8, int l2s) {
+  hipError_t e;
   KernArgs ka;
   memset(&ka, 0, sizeof(ka));
   ka.q = a.q;
@@ -147,7 +202,8 @@ hipError_t launch(const LaunchArgs& a) {
   ka.causal = a.causal;
   ka.c = a.c;
   const int64_t nq = x8 ? (a.Sq + kBM8 - 1) / kBM8 : query_tiles(a.Sq);
-  const int64_t items = nq * a.B * a.Hq;
+  const int64_t items = (nq * a.B * a.Hq) << l2s;
+  ka.log2split = (uint32_t)l2s;
   const int64_t grid = items < dk->cus ? items : dk->cus;
   ka.nq_grid = (uint32_t)nq | ((uint32_t)grid << 16);
   if (!group_magic(a.Hq, a.Hkv, &ka.gmagic)) return hipErrorInvalidValue;

@@ -84,22 +84,17 @@ def measured_traffic(workload_name: str):
 
 def launched_kernel(w: workloads.Workload, cus: int) -> str:
     """Name of the kernel the library launches for this workload on a device
-    with `cus` compute units (the launcher's rule: the eight-wave D = 128
-    kernel when its 512-row items cover the compute units and every item
-    with keys spans more than 128 keys)."""
-    name = f"fa_fwd_{w.dtype}_d{w.D}_gfx950"
-    if w.D != 128 or -(-w.Sq // 512) * w.B * w.Hq < cus:
-        return name
-    if not w.causal:
-        ok = w.Skv > 128
-    else:
-        ok, off = True, w.Skv - w.Sq
-        for q0 in range(0, w.Sq, 512):
-            end = min(w.Skv, min(q0 + 512, w.Sq) + off)
-            if end > 0:
-                ok = end > 128
-                break
-    return f"fa_fwd_{w.dtype}_d128_x8_gfx950" if ok else name
+    with `cus` compute units, from the library's own plan query (with split
+    key ranges a merge kernel follows it)."""
+    import attention_forward_05_amd as fa
+    st, kern, ranges = fa.fa_fwd_plan(w.B, w.Sq, w.Skv, w.Hq, w.D, int(w.causal), cus)
+    if st != fa.FA_OK:
+        raise fa.FAError(st, "fa_fwd_plan")
+    if kern == fa.FA_KERNEL_FOUR_WAVE:
+        return f"fa_fwd_{w.dtype}_d{w.D}_gfx950"
+    if ranges == 1:
+        return f"fa_fwd_{w.dtype}_d128_x8_gfx950"
+    return f"fa_fwd_{w.dtype}_d128_x8s_gfx950 ({ranges} key ranges) + combine_kernel"
 
 
 def algorithmic_bytes(w: workloads.Workload) -> int:
@@ -201,7 +196,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=workloads.HEADLINE.name,
-                    choices=[w.name for w in workloads.WORKLOADS])
+                    choices=list(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="first copy BYTES bytes device-to-device (HBM counter calibration)")

@@ -75,10 +75,21 @@ typedef enum {
  * only state the library keeps is its kernel code: the first call on a
  * device loads the library's gfx950 code object on that device (under a
  * lock, so concurrent first calls are safe) and keeps it until the process
- * ends; a failed load returns FA_ERR_HIP.  No other memory is allocated.
- * Calls on different streams may run concurrently.  The call is
- * asynchronous: it returns once the kernel is enqueued, and o / lse are
- * valid after the stream has been synchronised.
+ * ends; a failed load returns FA_ERR_HIP.  Calls on different streams may
+ * run concurrently.  The call is asynchronous: it returns once its kernels
+ * are enqueued, and o / lse are valid after the stream has been
+ * synchronised.
+ *
+ * Split key ranges (D = 128 only): when the (batch, q-head, 512-row query
+ * tile) items are fewer than the device's compute units and every item's
+ * key range is long, each item's keys are cut into 2, 4, 8 or 16 ranges (the
+ * one-device form of the kernbench GQA prefill page's split of the key
+ * sequence over PE groups; fa_fwd_plan reports the choice).  The ranges' partial results (fp32 O and LSE, 516 bytes per
+ * query row and range) then go to a temporary device buffer taken with
+ * hipMallocAsync on `stream` and released with hipFreeAsync on it after a
+ * second kernel has merged them into o / lse (`_merge_running` on that
+ * page).  If that buffer cannot be had, the call runs unsplit instead (same
+ * result).  Every other call allocates nothing.
  *
  * Returns FA_OK or one of the error codes above.
  */
@@ -90,6 +101,28 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o,
                float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
                int causal, float scale, hipStream_t stream);
+
+/* Kernel shapes reported by fa_fwd_plan. */
+enum {
+  FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD */
+  FA_KERNEL_EIGHT_WAVE = 1  /* 512-row query tiles, two waves per SIMD (D = 128) */
+};
+
+/*
+ * fa_fwd_plan -- host-only query (no HIP call): the kernel shape and the
+ * number of key ranges per item that fa_fwd / fa_fwd_f16 use for these sizes
+ * on a device with `compute_units` compute units (256 on an MI355X).
+ *
+ *   kernel     : written, FA_KERNEL_FOUR_WAVE or FA_KERNEL_EIGHT_WAVE
+ *   key_ranges : written, 1 (whole key ranges) or 2, 4, 8, 16 (split key
+ *                ranges merged by a second kernel)
+ *
+ * Returns FA_OK, FA_ERR_INVALID (NULL output pointer, size or compute_units
+ * < 1, causal not 0/1) or FA_ERR_UNSUPPORTED (D not 64 or 128); the outputs
+ * are written only on FA_OK.  Size limits of fa_fwd are not checked here.
+ */
+int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int D, int causal, int compute_units,
+                int* kernel, int* key_ranges);
 
 /* fa_strerror -- a static, NUL-terminated description of a status code
  * (never NULL; unknown codes give "unknown fa_status"). */

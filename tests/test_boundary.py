@@ -105,3 +105,61 @@ def test_python_wrapper_raises_on_bad_tensors(lib):
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(fa.FAError):
         fa.attention(q, q, q, True, 0.125)  # CPU tensors are refused before any call
+
+
+# fa_fwd_plan: the kernel-shape rule on the host, with the expected shapes
+# worked out by hand from the rule stated in include/fa.h and the launcher:
+# eight waves (512-row items) when B*Hq*ceil(Sq/512) >= compute units and the
+# shortest item with a visible key spans >= 3 key tiles of 64; else, with
+# D = 128 and fewer items than compute units, the fewest power-of-two key
+# ranges (<= 16) that cover the compute units, reduced until every range of
+# the shortest item keeps >= 16 key tiles.
+PLAN_CASES = [
+    # B, Sq, Skv, Hq, D, causal, cus, kernel, key_ranges
+    (2, 4096, 4096, 32, 128, 1, 256, 1, 1),    # 256 items: eight waves, whole ranges
+    (4, 1024, 1024, 16, 128, 0, 256, 0, 1),    # 128 items, 16 key tiles: too short to split
+    (1, 1000, 16384, 8, 128, 1, 256, 1, 8),    # 16 items; shortest 249 tiles < 16*16
+    (1, 512, 8192, 4, 128, 0, 256, 1, 8),      # 4 items; 128 tiles = 16*8
+    (1, 512, 16384, 16, 128, 0, 256, 1, 16),   # 16 items; 256 tiles = 16*16
+    (3, 300, 4000, 5, 128, 0, 256, 1, 2),      # 15 items; 63 tiles: only 2 ranges
+    (1, 2048, 4096, 32, 128, 1, 256, 1, 2),    # 128 items: 2 ranges cover 256
+    (2, 700, 5000, 16, 128, 1, 256, 1, 4),     # 64 items; shortest 76 tiles
+    (1, 3000, 2600, 16, 128, 1, 256, 0, 1),    # first keyed tile has 2 key tiles
+    (1, 512, 8192, 4, 64, 0, 256, 0, 1),       # D = 64: four waves, never split
+    (1, 512, 8192, 4, 128, 0, 4, 1, 1),        # 4 compute units: 4 items fill them
+    (1, 200, 100, 256, 128, 1, 256, 0, 1),     # 256 items of 2 key tiles: four waves
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,D,causal,cus,kernel,ranges", PLAN_CASES)
+def test_plan(lib, B, Sq, Skv, Hq, D, causal, cus, kernel, ranges):
+    assert fa.fa_fwd_plan(B, Sq, Skv, Hq, D, causal, cus) == (fa.FA_OK, kernel, ranges)
+
+
+def test_plan_items_without_keys(lib):
+    # Sq = 600, Skv = 100, causal: rows 0..499 see no key, so the first
+    # 512-row tile reaches only keys 0..11 (1 key tile): four waves.
+    # Sq = 1200, Skv = 100: rows below 1100 see nothing, so tiles 0 and 1
+    # have no key and tile 2 ends at key 100 (2 key tiles): four waves.
+    assert fa.fa_fwd_plan(1, 600, 100, 256, 128, 1, 256) == (fa.FA_OK, 0, 1)
+    assert fa.fa_fwd_plan(1, 1200, 100, 256, 128, 1, 256) == (fa.FA_OK, 0, 1)
+    # Sq = 1200, Skv = 300: tile 0 none (rows < 900 see nothing), tile 1
+    # (rows 512..1023) ends at key min(1024 - 900, 300) = 124 (2 tiles);
+    # Skv = 1100: tile 0 ends at key 412 (7 tiles): eight waves
+    assert fa.fa_fwd_plan(1, 1200, 300, 256, 128, 1, 256) == (fa.FA_OK, 0, 1)
+    assert fa.fa_fwd_plan(1, 1200, 1100, 256, 128, 1, 256) == (fa.FA_OK, 1, 1)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), fa.FA_ERR_INVALID), (dict(Sq=0), fa.FA_ERR_INVALID),
+    (dict(Skv=-1), fa.FA_ERR_INVALID), (dict(Hq=0), fa.FA_ERR_INVALID),
+    (dict(causal=2), fa.FA_ERR_INVALID), (dict(cus=0), fa.FA_ERR_INVALID),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(lib, over, status):
+    a = dict(B=1, Sq=512, Skv=8192, Hq=4, D=128, causal=0, cus=256)
+    a.update(over)
+    assert fa.fa_fwd_plan(a["B"], a["Sq"], a["Skv"], a["Hq"], a["D"], a["causal"],
+                          a["cus"]) == (status, None, None)
+    # NULL output pointers
+    assert lib.fa_fwd_plan(1, 512, 8192, 4, 128, 0, 256, None, None) == fa.FA_ERR_INVALID

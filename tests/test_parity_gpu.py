@@ -171,6 +171,49 @@ def test_eight_wave_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype):
     full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 3 * Skv + Hkv)
 
 
+# ---------------------------------------------------------------------------
+# split key ranges: items too few for the compute units, long key ranges; the
+# eight-wave kernel writes fp32 partial (O, LSE) per range and a second
+# kernel merges them
+# ---------------------------------------------------------------------------
+
+SPLIT_CASES = [
+    # B, Sq, Skv, Hq, Hkv, causal, dtype, key ranges on 256 compute units
+    (1, 1000, 16384, 8, 2, True, "bf16", 8),    # bottom-right, ragged second query tile
+    (1, 512, 8192, 4, 4, False, "f16", 8),      # 16 key tiles per range
+    (2, 700, 5000, 16, 2, True, "bf16", 4),     # GQA 8, ragged keys, unequal items
+    (3, 300, 4000, 5, 5, False, "bf16", 2),     # Hq % 8 != 0, ragged last range
+    (1, 2048, 4096, 32, 8, True, "f16", 2),     # causal diagonal inside the last range
+    (1, 512, 16384, 16, 4, False, "bf16", 16),  # 16 ranges
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype,ranges", SPLIT_CASES)
+def test_split_key_ranges(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, ranges):
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st, kern, nr = fa.fa_fwd_plan(B, Sq, Skv, Hq, 128, int(causal), cus)
+    assert st == fa.FA_OK and kern == fa.FA_KERNEL_EIGHT_WAVE
+    if cus == 256:
+        assert nr == ranges
+    full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 7 * Skv + Hq)
+
+
+def test_split_without_lse(fa):
+    """lse = NULL on the split path: the merge still needs the partial LSEs
+    (which the kernel always writes), and O must not change."""
+    q, k, v = workloads.make_inputs(1, 1000, 16384, 8, 2, 128, "bf16", 5)
+    o1, l1 = run_gpu(fa, q, k, v, True, 0.088)
+    o2, _ = run_gpu(fa, q, k, v, True, 0.088, with_lse=False)
+    assert np.array_equal(o1, o2)
+
+
+def test_split_slow_path(fa):
+    """Key rows scaled by 8 in every range: the reference max moves inside
+    ranges, and the ranges' LSEs differ widely before the merge."""
+    full_case(fa, 1, 512, 8192, 4, 2, 128, False, "f16", seed=23, boost=0.01)
+
+
 @pytest.mark.parametrize("case", ["scale1", "kboost"])
 def test_eight_wave_slow_path(fa, case):
     """Logits large enough that the reference max moves often (the slow
@@ -204,7 +247,8 @@ def _sample_rows(w, n_random=1536, seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=[w.name for w in workloads.WORKLOADS])
+@pytest.mark.parametrize("w", workloads.WORKLOADS + workloads.SPLIT_WORKLOADS,
+                         ids=[w.name for w in workloads.WORKLOADS + workloads.SPLIT_WORKLOADS])
 def test_named_workload(fa, w):
     q, k, v = workloads.workload_inputs(w)
     o, lse = run_gpu(fa, q, k, v, w.causal, w.scale)

@@ -60,7 +60,16 @@ WORKLOADS = [
     Workload("causal_gqa_prefill_b1_hq64_hkv8_sq2048_skv32768_d128_f16_kboost",
              1, 64, 8, 2048, 32768, 128, True, "f16", 46, k_row_boost_frac=0.01),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Shapes outside the five above that exercise the split key ranges: few
+# (batch, q-head, 512-row query tile) items over long key ranges, the
+# short-prefill / long-context case of the kernbench GQA prefill page.
+SPLIT_WORKLOADS = [
+    Workload("causal_gqa_shortprefill_b1_hq8_hkv1_sq1024_skv32768_d128_bf16",
+             1, 8, 1, 1024, 32768, 128, True, "bf16", 47),
+    Workload("causal_gqa_shortprefill_b1_hq32_hkv8_sq512_skv16384_d128_bf16",
+             1, 32, 8, 512, 16384, 128, True, "bf16", 48),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + SPLIT_WORKLOADS}
 
 # The headline benchmark workload: causal, D=128, bf16, S=4096.
 HEADLINE = WORKLOADS[2]
