@@ -143,12 +143,17 @@ int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
   if (items >= cus) return 0;
   const int64_t n = min_item_tiles(Sq, Skv, causal);
   if (n == 0) return 0;
-  // the fewest key ranges (a power of two, at most 16) that give every
-  // compute unit an item, while each range keeps at least 16 tiles (1024
-  // keys): below that the partial results' traffic outweighs the gain
+  // The fewest key ranges (a power of two, at most 16) that give every
+  // compute unit an item, while each range keeps at least 16 key tiles:
+  // below that the partial results' traffic outweighs the gain.  When the
+  // four-wave kernel's 256-row items already cover the compute units, split
+  // only ranges of at least 64 key tiles: on shorter ones writing and
+  // merging the partial results costs more than the eight-wave kernel's
+  // faster loop saves.
+  const int64_t min_range = work_items(B, Sq, Hq) >= cus ? 64 : 16;
   int l = 0;
   while (l < 4 && (items << l) < cus) ++l;
-  while (l > 0 && n < ((int64_t)16 << l)) --l;
+  while (l > 0 && n < (min_range << l)) --l;
   return l;
 }
 int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }

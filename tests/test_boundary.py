@@ -113,7 +113,8 @@ def test_python_wrapper_raises_on_bad_tensors(lib):
 # shortest item with a visible key spans >= 3 key tiles of 64; else, with
 # D = 128 and fewer items than compute units, the fewest power-of-two key
 # ranges (<= 16) that cover the compute units, reduced until every range of
-# the shortest item keeps >= 16 key tiles.
+# the shortest item keeps >= 16 key tiles (>= 64 when B*Hq*ceil(Sq/256)
+# already covers the compute units).
 PLAN_CASES = [
     # B, Sq, Skv, Hq, D, causal, cus, kernel, key_ranges
     (2, 4096, 4096, 32, 128, 1, 256, 1, 1),    # 256 items: eight waves, whole ranges
@@ -122,7 +123,9 @@ PLAN_CASES = [
     (1, 512, 8192, 4, 128, 0, 256, 1, 8),      # 4 items; 128 tiles = 16*8
     (1, 512, 16384, 16, 128, 0, 256, 1, 16),   # 16 items; 256 tiles = 16*16
     (3, 300, 4000, 5, 128, 0, 256, 1, 2),      # 15 items; 63 tiles: only 2 ranges
-    (1, 2048, 4096, 32, 128, 1, 256, 1, 2),    # 128 items: 2 ranges cover 256
+    (1, 2048, 4096, 32, 128, 1, 256, 0, 1),    # 256 four-wave items; ranges would be < 64 tiles
+    (1, 2048, 32768, 32, 128, 1, 256, 1, 2),   # 256 four-wave items; 2 ranges of >= 244 tiles
+    (1, 2048, 8192, 16, 128, 1, 256, 1, 4),    # 64 items, 128 four-wave ones; 4 ranges of >= 26 tiles
     (2, 700, 5000, 16, 128, 1, 256, 1, 4),     # 64 items; shortest 76 tiles
     (1, 3000, 2600, 16, 128, 1, 256, 0, 1),    # first keyed tile has 2 key tiles
     (1, 512, 8192, 4, 64, 0, 256, 0, 1),       # D = 64: four waves, never split

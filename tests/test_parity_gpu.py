@@ -183,7 +183,7 @@ SPLIT_CASES = [
     (1, 512, 8192, 4, 4, False, "f16", 8),      # 16 key tiles per range
     (2, 700, 5000, 16, 2, True, "bf16", 4),     # GQA 8, ragged keys, unequal items
     (3, 300, 4000, 5, 5, False, "bf16", 2),     # Hq % 8 != 0, ragged last range
-    (1, 2048, 4096, 32, 8, True, "f16", 2),     # causal diagonal inside the last range
+    (1, 2048, 8192, 16, 8, True, "f16", 4),     # causal diagonal inside the last range
     (1, 512, 16384, 16, 4, False, "bf16", 16),  # 16 ranges
 ]
 
