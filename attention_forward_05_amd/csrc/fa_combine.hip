@@ -13,7 +13,9 @@
 // and a row with no visible key at all gets O = 0, LSE = -inf.  O is rounded
 // once to the output dtype (round to nearest even).
 //
-// One 64-lane wave per query row, two head dimensions per lane (D = 128).
+// Half a wave (32 lanes) per query row, four head dimensions per lane
+// (D = 128); the number of ranges is a template parameter so that every
+// range's loads are issued before the first is used.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -27,67 +29,105 @@ namespace fa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kRowsPerBlock = 4;
+constexpr int kLanesPerRow = kD / 4;
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
 
-__device__ inline void store2(__hip_bfloat16* p, float a, float b) {
-  p[0] = __float2bfloat16(a);
-  p[1] = __float2bfloat16(b);
+__device__ inline void store4(__hip_bfloat16* p, const float (&a)[4]) {
+  __hip_bfloat162 lo = __float22bfloat162_rn(make_float2(a[0], a[1]));
+  __hip_bfloat162 hi = __float22bfloat162_rn(make_float2(a[2], a[3]));
+  uint2 u;
+  u.x = *reinterpret_cast<uint32_t*>(&lo);
+  u.y = *reinterpret_cast<uint32_t*>(&hi);
+  *reinterpret_cast<uint2*>(p) = u;
 }
-__device__ inline void store2(__half* p, float a, float b) {
-  p[0] = __float2half(a);
-  p[1] = __float2half(b);
+__device__ inline void store4(__half* p, const float (&a)[4]) {
+  __half2 lo = __floats2half2_rn(a[0], a[1]);
+  __half2 hi = __floats2half2_rn(a[2], a[3]);
+  uint2 u;
+  u.x = *reinterpret_cast<uint32_t*>(&lo);
+  u.y = *reinterpret_cast<uint32_t*>(&hi);
+  *reinterpret_cast<uint2*>(p) = u;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(64 * kRowsPerBlock)
+template <typename T, int NS>
+__global__ void __launch_bounds__(kThreads)
 combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-               T* __restrict__ o, float* __restrict__ lse, int nsplit, int B, int Hq, int Sq) {
+               T* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Sq) {
   const int64_t rows = (int64_t)B * Hq * Sq;
-  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / 64;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   if (r >= rows) return;
-  const int lane = threadIdx.x % 64;
+  const int lane = threadIdx.x % kLanesPerRow;
   // row r = (b * Hq + hq) * Sq + i, the layout of the partial buffers
   const int i = (int)(r % Sq);
   const int64_t bh = r / Sq;
   const int hq = (int)(bh % Hq);
   const int b = (int)(bh / Hq);
 
+  float ls[NS];
+  float4 v[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    ls[s] = part_lse[(int64_t)s * rows + r];
+    v[s] = *reinterpret_cast<const float4*>(part_o + ((int64_t)s * rows + r) * kD + 4 * lane);
+  }
   float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[(int64_t)s * rows + r]);
-  float acc0 = 0.0f, acc1 = 0.0f, out_lse = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) m = fmaxf(m, ls[s]);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float out_lse = -INFINITY;
   if (m != -INFINITY) {
     float wsum = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ls = part_lse[(int64_t)s * rows + r];
-      const float w = expf(ls - m);          // 0 for a range without keys
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float w = expf(ls[s] - m);  // 0 for a range without keys
       wsum += w;
-      const float2 v = *reinterpret_cast<const float2*>(part_o + ((int64_t)s * rows + r) * kD + 2 * lane);
-      acc0 += w * v.x;
-      acc1 += w * v.y;
+      acc[0] += w * v[s].x;
+      acc[1] += w * v[s].y;
+      acc[2] += w * v[s].z;
+      acc[3] += w * v[s].w;
     }
     const float inv = 1.0f / wsum;
-    acc0 *= inv;
-    acc1 *= inv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] *= inv;
     out_lse = m + logf(wsum);
   }
-  store2(o + (((int64_t)b * Sq + i) * Hq + hq) * kD + 2 * lane, acc0, acc1);
+  store4(o + (((int64_t)b * Sq + i) * Hq + hq) * kD + 4 * lane, acc);
   if (lse != nullptr && lane == 0) lse[r] = out_lse;
+}
+
+template <typename T>
+hipError_t launch_t(const float* part_o, const float* part_lse, T* o, float* lse, int nsplit,
+                    int B, int Hq, int Sq, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 block(kThreads);
+  switch (nsplit) {
+    case 2:
+      hipLaunchKernelGGL((combine_kernel<T, 2>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
+      break;
+    case 4:
+      hipLaunchKernelGGL((combine_kernel<T, 4>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
+      break;
+    case 8:
+      hipLaunchKernelGGL((combine_kernel<T, 8>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
+      break;
+    case 16:
+      hipLaunchKernelGGL((combine_kernel<T, 16>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_combine(DType dtype, const float* part_o, const float* part_lse, void* o, float* lse,
                           int nsplit, int B, int Hq, int Sq, hipStream_t stream) {
-  const int64_t rows = (int64_t)B * Hq * Sq;
-  const unsigned blocks = (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  if (dtype == DType::kBF16) {
-    hipLaunchKernelGGL(combine_kernel<__hip_bfloat16>, dim3(blocks), dim3(64 * kRowsPerBlock), 0, stream,
-                       part_o, part_lse, static_cast<__hip_bfloat16*>(o), lse, nsplit, B, Hq, Sq);
-  } else {
-    hipLaunchKernelGGL(combine_kernel<__half>, dim3(blocks), dim3(64 * kRowsPerBlock), 0, stream,
-                       part_o, part_lse, static_cast<__half*>(o), lse, nsplit, B, Hq, Sq);
-  }
-  return hipGetLastError();
+  if (dtype == DType::kBF16)
+    return launch_t(part_o, part_lse, static_cast<__hip_bfloat16*>(o), lse, nsplit, B, Hq, Sq, stream);
+  return launch_t(part_o, part_lse, static_cast<__half*>(o), lse, nsplit, B, Hq, Sq, stream);
 }
 
 }  // namespace fa

@@ -67,6 +67,14 @@ struct DeviceKernels {
   hipModule_t mod = nullptr;
   hipFunction_t fn[kKernels] = {};
   int cus = 0;  // compute units of the device
+  // The split path's buffer of partial results, kept for the next call and
+  // grown when a call needs more.  `done` is recorded on the caller's stream
+  // after the merge kernel; the next call (on any stream) makes its stream
+  // wait for it before overwriting the buffer, so calls never share it at the
+  // same time and the host never waits.
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipEvent_t done = nullptr;
 };
 
 std::mutex g_mu;
@@ -89,6 +97,8 @@ hipError_t kernels_for_current_device(DeviceKernels** out) {
     e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (d.cus < 1) d.cus = 1;
+    e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
     d.loaded = true;
   }
   *out = &d;
@@ -170,19 +180,39 @@ hipError_t launch(const LaunchArgs& a) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
     const size_t lse_bytes = (size_t)(rows << l2s) * 4;
     const size_t o_bytes = lse_bytes * a.D;
-    void* ws = nullptr;
-    if (hipMallocAsync(&ws, o_bytes + lse_bytes, a.stream) == hipSuccess) {
+    // the lock also keeps the event's record order that of the calls
+    std::lock_guard<std::mutex> lock(g_mu);
+    bool have = dk->ws_bytes >= o_bytes + lse_bytes;
+    if (!have) {
+      if (dk->ws) {
+        e = hipEventSynchronize(dk->done);  // the last call's kernels are done with it
+        if (e != hipSuccess) return e;
+        e = hipFree(dk->ws);
+        if (e != hipSuccess) return e;
+        dk->ws = nullptr;
+        dk->ws_bytes = 0;
+      }
+      if (hipMalloc(&dk->ws, o_bytes + lse_bytes) == hipSuccess) {
+        dk->ws_bytes = o_bytes + lse_bytes;
+        have = true;
+      } else {
+        dk->ws = nullptr;
+        (void)hipGetLastError();  // no buffer: whole key ranges instead
+      }
+    }
+    if (have) {
+      e = hipStreamWaitEvent(a.stream, dk->done, 0);
+      if (e != hipSuccess) return e;
       LaunchArgs p = a;
-      p.o = ws;
-      p.lse = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+      p.o = dk->ws;
+      p.lse = reinterpret_cast<float*>(static_cast<char*>(dk->ws) + o_bytes);
       e = launch_kernel(dk, p, a.dtype == DType::kBF16 ? 6 : 7, true, l2s);
       if (e == hipSuccess)
-        e = launch_combine(a.dtype, static_cast<const float*>(ws), p.lse, a.o, a.lse, 1 << l2s, a.B,
-                           a.Hq, a.Sq, a.stream);
-      const hipError_t f = hipFreeAsync(ws, a.stream);
+        e = launch_combine(a.dtype, static_cast<const float*>(dk->ws), p.lse, a.o, a.lse, 1 << l2s,
+                           a.B, a.Hq, a.Sq, a.stream);
+      const hipError_t f = hipEventRecord(dk->done, a.stream);
       return e != hipSuccess ? e : f;
     }
-    (void)hipGetLastError();  // no temporary buffer: whole key ranges instead
   }
   const bool x8 = use_eight_waves(a.B, a.Sq, a.Skv, a.Hq, a.D, a.causal, dk->cus);
   const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)

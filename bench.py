@@ -47,10 +47,6 @@ import workloads  # noqa: E402
 METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 GPU"
 # Published dense MFMA peak of one MI355X for bf16 and fp16 (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
-# the kernels are generated from these sources; a traffic file taken on other
-# sources no longer describes the kernel
-KERNEL_SRCS = [os.path.join(ROOT, "attention_forward_05_amd", "asm", n)
-               for n in ("fa_fwd_gen.py", "fa_fwd_x8.py", "regs.py")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -58,26 +54,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def kernel_code_hash(kernel: str):
+    """sha256 (16 hex digits) of the generated instructions of `kernel` (its
+    assembly up to the kernel descriptor), or None for a name the generators
+    do not make.  Counter figures taken on other instructions no longer
+    describe the kernel."""
+    sys.path.insert(0, ROOT)
+    try:
+        from attention_forward_05_amd.asm.fa_fwd_gen import Gen
+        from attention_forward_05_amd.asm.fa_fwd_x8 import Gen8
+    finally:
+        sys.path.pop(0)
+    parts = kernel.split("_")   # fa_fwd_<dt>_d<D>[_x8|_x8s]_gfx950
+    if len(parts) < 5 or parts[:2] != ["fa", "fwd"] or parts[-1] != "gfx950":
+        return None
+    dt, D, shape = parts[2], int(parts[3][1:]), parts[4:-1]
+    if shape == []:
+        gen = Gen(dt, D)
+    elif shape in (["x8"], ["x8s"]):
+        gen = Gen8(dt, shape == ["x8s"])
+    else:
+        return None
+    text = gen.assemble_text()[0]
+    code = text[:text.index(".amdhsa_kernel")]
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
+def measured_traffic(workload_name: str, kernel: str):
     """Bytes per launch from the committed counter summary, or None when the
-    file is absent or was taken on a different kernel source."""
+    file is absent or its figures were taken on other instructions."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
     entry = t.get("workloads", {}).get(workload_name)
-    if not entry:
+    if not entry or entry.get("kernel") != kernel:
+        return None
+    if entry.get("kernel_code_sha256_16") != kernel_code_hash(kernel):
         return None
     return entry.get("bytes_per_launch")
 
@@ -202,19 +216,22 @@ def main():
                     help="first copy BYTES bytes device-to-device (HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--compute-units", type=int, default=256,
+                    help="with --traffic-summary: compute units of the profiled device")
     args = ap.parse_args()
 
     if args.traffic_summary:
         entry = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
                                 args.copy_bytes, args.workload)
+        kernel = launched_kernel(workloads.BY_NAME[args.workload], args.compute_units)
+        entry["kernel"] = kernel
+        entry["kernel_code_sha256_16"] = kernel_code_hash(kernel)
         try:
             with open(TRAFFIC_FILE) as f:
                 doc = json.load(f)
         except (OSError, ValueError):
             doc = {}
-        if doc.get("kernel_source_sha256_16") != kernel_source_hash():
-            doc = {"kernel_source_sha256_16": kernel_source_hash(), "workloads": {}}
-        doc["workloads"][args.workload] = entry
+        doc.setdefault("workloads", {})[args.workload] = entry
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(doc, f, indent=1, sort_keys=True)
             f.write("\n")
@@ -288,7 +305,8 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name)
+    kernel = launched_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count)
+    traffic = measured_traffic(w.name, kernel)
     log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak:.0f}); launch avg {launch_avg_ms * 1e3:.1f} us, "
         f"min {launch_ms[0] * 1e3:.1f} us, median {launch_ms[len(launch_ms) // 2] * 1e3:.1f} us")
@@ -326,7 +344,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_launch_avg_us": round(launch_avg_ms * 1e3, 2),
-            "kernel": launched_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count),
+            "kernel": kernel,
         },
         "cpu_baseline": cpu,
     }

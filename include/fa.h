@@ -84,12 +84,18 @@ typedef enum {
  * tile) items are fewer than the device's compute units and every item's
  * key range is long, each item's keys are cut into 2, 4, 8 or 16 ranges (the
  * one-device form of the kernbench GQA prefill page's split of the key
- * sequence over PE groups; fa_fwd_plan reports the choice).  The ranges' partial results (fp32 O and LSE, 516 bytes per
- * query row and range) then go to a temporary device buffer taken with
- * hipMallocAsync on `stream` and released with hipFreeAsync on it after a
- * second kernel has merged them into o / lse (`_merge_running` on that
- * page).  If that buffer cannot be had, the call runs unsplit instead (same
- * result).  Every other call allocates nothing.
+ * sequence over PE groups; fa_fwd_plan reports the choice).  The ranges'
+ * partial results (fp32 O and LSE, 516 bytes per query row and range) go to
+ * a device buffer the library keeps per device, and a second kernel merges
+ * them into o / lse (`_merge_running` on that page).  The buffer is taken
+ * with hipMalloc on the first such call and grown (hipFree of the old one
+ * after its last use, then hipMalloc) when a call needs more; it is held
+ * until the process ends (at most 516 * 512 * 2 * compute units bytes:
+ * 135 MB on 256 compute units).  Calls hand it on with a device-side event
+ * wait, so split calls on different streams run one after the other on the
+ * device, and the host never waits except when the buffer grows.  If it
+ * cannot be allocated the call runs unsplit instead (same result).  Calls
+ * that do not split allocate nothing.
  *
  * Returns FA_OK or one of the error codes above.
  */

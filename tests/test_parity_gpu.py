@@ -208,6 +208,37 @@ def test_split_without_lse(fa):
     assert np.array_equal(o1, o2)
 
 
+def test_split_streams_and_buffer_growth(fa):
+    """Split calls on two streams, queued without a host wait, the second
+    needing a larger partial buffer than the first: both give the same bits
+    as when run one at a time (the library's buffer is handed from call to
+    call by a device-side event wait)."""
+    dev = torch.device("cuda:0")
+    shapes = [(1, 512, 8192, 4, 4, False), (1, 1000, 16384, 8, 2, True), (1, 512, 8192, 4, 4, False)]
+    ins = []
+    for n, (B, Sq, Skv, Hq, Hkv, causal) in enumerate(shapes):
+        q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, 128, "bf16", 100 + n)
+        ins.append((q.to(dev), k.to(dev), v.to(dev), causal))
+    ref = []
+    for q, k, v, causal in ins:
+        o, lse = fa.attention(q, k, v, causal, 0.088)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), lse.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for n, (q, k, v, causal) in enumerate(ins):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((q.shape[0], q.shape[2], q.shape[1]), float("nan"), device=dev)
+        st = streams[n % 2]
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            fa.attention(q, k, v, causal, 0.088, out=o, lse=lse, stream=st)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    for (o, lse), (o_ref, lse_ref) in zip(outs, ref):
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+
+
 def test_split_slow_path(fa):
     """Key rows scaled by 8 in every range: the reference max moves inside
     ranges, and the ranges' LSEs differ widely before the merge."""
