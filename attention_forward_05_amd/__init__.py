@@ -3,7 +3,8 @@ attention forward library.
 
 This module only marshals arguments: every step of the computation runs in
 the HIP kernel behind the C ABI declared in ``include/fa.h``.  The functions
-carry the C names (``fa_fwd``, ``fa_fwd_f16``, ``fa_fwd_plan``, ``fa_strerror``) and take
+carry the C names (``fa_fwd``, ``fa_fwd_f16``, ``fa_fwd_ws``, ``fa_fwd_plan``,
+``fa_strerror``) and take
 either torch tensors (their device pointers are passed) or raw integer
 addresses.  PyTorch is used for device memory and streams only.
 
@@ -15,19 +16,22 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_plan", "fa_strerror", "attention", "FAError",
-           "library_path", "load", "FA_OK", "FA_ERR_INVALID",
-           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_KERNEL_FOUR_WAVE",
-           "FA_KERNEL_EIGHT_WAVE", "EXPORTED_SYMBOLS"]
+__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_plan", "fa_strerror", "attention",
+           "FAError", "library_path", "load", "FA_OK", "FA_ERR_INVALID",
+           "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_DTYPE_BF16",
+           "FA_DTYPE_F16", "FA_KERNEL_FOUR_WAVE", "FA_KERNEL_EIGHT_WAVE", "EXPORTED_SYMBOLS"]
 
 FA_OK = 0
 FA_ERR_INVALID = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
+FA_ERR_WORKSPACE = -4
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F16 = 1
 FA_KERNEL_FOUR_WAVE = 0
 FA_KERNEL_EIGHT_WAVE = 1
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_plan", "fa_strerror")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_plan", "fa_strerror")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -59,8 +63,12 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ctypes.c_float, vp]
         fn.restype = i
+    sz = ctypes.c_size_t
+    lib.fa_fwd_ws.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ctypes.c_float, vp,
+                              sz, vp]
+    lib.fa_fwd_ws.restype = i
     ip = ctypes.POINTER(i)
-    lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, ip, ip]
+    lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, i, ip, ip, ctypes.POINTER(sz)]
     lib.fa_fwd_plan.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
@@ -72,16 +80,19 @@ def fa_strerror(status: int) -> str:
     return load().fa_strerror(int(status)).decode()
 
 
-def fa_fwd_plan(B, Sq, Skv, Hq, D, causal, compute_units):
+def fa_fwd_plan(B, Sq, Skv, Hq, Hkv, D, causal, compute_units, with_workspace=False):
     """Host-only query (see include/fa.h): returns (status, kernel,
-    key_ranges) for these sizes on a device with `compute_units` compute
-    units; kernel and key_ranges are None unless status is FA_OK."""
-    kern, ranges = ctypes.c_int(-1), ctypes.c_int(-1)
-    st = load().fa_fwd_plan(int(B), int(Sq), int(Skv), int(Hq), int(D), int(causal),
-                            int(compute_units), ctypes.byref(kern), ctypes.byref(ranges))
+    key_ranges, workspace_bytes) for these sizes on a device with
+    `compute_units` compute units, for fa_fwd (with_workspace False) or
+    fa_fwd_ws with a large enough workspace (True); the last three are None
+    unless status is FA_OK."""
+    kern, ranges, ws = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_size_t(0)
+    st = load().fa_fwd_plan(int(B), int(Sq), int(Skv), int(Hq), int(Hkv), int(D), int(causal),
+                            int(compute_units), int(bool(with_workspace)), ctypes.byref(kern),
+                            ctypes.byref(ranges), ctypes.byref(ws))
     if st != FA_OK:
-        return st, None, None
-    return st, kern.value, ranges.value
+        return st, None, None, None
+    return st, kern.value, ranges.value, ws.value
 
 
 def _addr(x):
@@ -123,12 +134,27 @@ def fa_fwd_f16(q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale, stream=No
     return _call("fa_fwd_f16", q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale, stream)
 
 
+def fa_fwd_ws(dtype, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale, workspace,
+              workspace_bytes, stream=None) -> int:
+    """Forward with a caller-owned workspace for split key ranges (see
+    include/fa.h); dtype is FA_DTYPE_BF16 or FA_DTYPE_F16.  Returns the
+    status code."""
+    st = load().fa_fwd_ws(int(dtype), _addr(q), _addr(k), _addr(v), _addr(o), _addr(lse),
+                          int(B), int(Sq), int(Skv), int(Hq), int(Hkv), int(D), int(causal),
+                          float(scale), _addr(workspace), int(workspace_bytes),
+                          _stream(stream) if stream != 0 else None)
+    return st
+
+
 def attention(q, k, v, causal: bool, scale: float, with_lse: bool = True, out=None,
-              lse=None, stream=None):
+              lse=None, stream=None, split: bool = False):
     """Convenience wrapper on torch tensors: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]
     (bf16 or fp16, contiguous, on the GPU).  Allocates O (and the fp32 LSE
     [B,Hq,Sq]) with torch unless given, calls the entry point for the dtype
-    and raises FAError on a non-zero status.  Returns (o, lse or None)."""
+    and raises FAError on a non-zero status.  With split=True the call goes
+    through fa_fwd_ws with a torch-allocated workspace of the size
+    fa_fwd_plan reports, so that key ranges may be split.  Returns
+    (o, lse or None)."""
     import torch
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise FAError(FA_ERR_INVALID, "attention: q, k and v dtypes differ")
@@ -144,13 +170,26 @@ def attention(q, k, v, causal: bool, scale: float, with_lse: bool = True, out=No
     if with_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if q.dtype == torch.bfloat16:
-        fn = fa_fwd
+        fn, dt = fa_fwd, FA_DTYPE_BF16
     elif q.dtype == torch.float16:
-        fn = fa_fwd_f16
+        fn, dt = fa_fwd_f16, FA_DTYPE_F16
     else:
         raise FAError(FA_ERR_UNSUPPORTED, f"attention: dtype {q.dtype}")
-    st = fn(q, k, v, out, lse if with_lse else None, B, Sq, Skv, Hq, Hkv, D,
-            int(bool(causal)), scale, stream)
+    lse_arg = lse if with_lse else None
+    if split:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        st, _, _, nbytes = fa_fwd_plan(B, Sq, Skv, Hq, Hkv, D, int(bool(causal)), cus, True)
+        if st != FA_OK:
+            raise FAError(st, "attention: fa_fwd_plan")
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
+        if ws is not None and isinstance(stream, torch.cuda.Stream):
+            # torch's allocator may hand the block out again once this
+            # function returns: tie its reuse to the stream the call runs on
+            ws.record_stream(stream)
+        st = fa_fwd_ws(dt, q, k, v, out, lse_arg, B, Sq, Skv, Hq, Hkv, D, int(bool(causal)),
+                       scale, ws, nbytes, stream)
+    else:
+        st = fn(q, k, v, out, lse_arg, B, Sq, Skv, Hq, Hkv, D, int(bool(causal)), scale, stream)
     if st != FA_OK:
         raise FAError(st, "attention")
     return out, (lse if with_lse else None)

@@ -31,9 +31,13 @@ bool overlap(const void* p, uint64_t bytes, const void* r, uint64_t rbytes) {
   return a < b + rbytes && b < a + bytes;
 }
 
-int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o,
-        float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,
-        float scale, hipStream_t stream) {
+}  // namespace
+
+namespace fa {
+
+int check_fwd_args(DType dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
+                   hipStream_t stream, LaunchArgs* out) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID;
   if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1) return FA_ERR_INVALID;
   if (Hq % Hkv != 0) return FA_ERR_INVALID;
@@ -84,7 +88,7 @@ int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o,
   if (!(c >= FLT_MIN)) c = FLT_MIN;
   if (!isfinite(c)) return FA_ERR_UNSUPPORTED;
 
-  fa::LaunchArgs a;
+  LaunchArgs& a = *out;
   a.dtype = dtype;
   a.q = q;
   a.k = k;
@@ -100,7 +104,42 @@ int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o,
   a.causal = causal;
   a.c = c;
   a.stream = stream;
-  return fa::launch(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  a.ws = nullptr;
+  a.ws_bytes = 0;
+  return FA_OK;
+}
+
+}  // namespace fa
+
+namespace {
+
+// bytes of q/o and of k/v (valid after check_fwd_args succeeded)
+void tensor_bytes(const fa::LaunchArgs& a, uint64_t* qb, uint64_t* kvb, uint64_t* lseb) {
+  *qb = (uint64_t)a.B * a.Sq * a.Hq * a.D * 2;
+  *kvb = (uint64_t)a.B * a.Skv * a.Hkv * a.D * 2;
+  *lseb = (uint64_t)a.B * a.Hq * a.Sq * 4;
+}
+
+int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+        int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale, void* ws,
+        size_t ws_bytes, hipStream_t stream) {
+  fa::LaunchArgs a;
+  int st = fa::check_fwd_args(dtype, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale,
+                              stream, &a);
+  if (st != FA_OK) return st;
+  if (ws) {
+    // the workspace: 16-byte aligned, overlapping none of the tensors
+    if (!aligned16(ws) || ws_bytes == 0) return FA_ERR_INVALID;
+    uint64_t qb, kvb, lseb;
+    tensor_bytes(a, &qb, &kvb, &lseb);
+    if (overlap(ws, ws_bytes, q, qb) || overlap(ws, ws_bytes, k, kvb) ||
+        overlap(ws, ws_bytes, v, kvb) || overlap(ws, ws_bytes, o, qb) ||
+        (lse && overlap(ws, ws_bytes, lse, lseb)))
+      return FA_ERR_INVALID;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+  }
+  return fa::launch(a);
 }
 
 }  // namespace
@@ -110,27 +149,39 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
            int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
            hipStream_t stream) {
-  return fwd(fa::DType::kBF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale,
-             stream);
+  return fwd(fa::DType::kBF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale, nullptr,
+             0, stream);
 }
 
 int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
                hipStream_t stream) {
-  return fwd(fa::DType::kF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale,
-             stream);
+  return fwd(fa::DType::kF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale, nullptr,
+             0, stream);
 }
 
-int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int D, int causal, int compute_units,
-                int* kernel, int* key_ranges) {
-  if (!kernel || !key_ranges) return FA_ERR_INVALID;
-  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || D < 1 || compute_units < 1) return FA_ERR_INVALID;
+int fa_fwd_ws(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID;
+  return fwd(dtype == FA_DTYPE_BF16 ? fa::DType::kBF16 : fa::DType::kF16, q, k, v, o, lse, B, Sq,
+             Skv, Hq, Hkv, D, causal, scale, workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, int compute_units,
+                int with_workspace, int* kernel, int* key_ranges, size_t* workspace_bytes) {
+  if (!kernel || !key_ranges || !workspace_bytes) return FA_ERR_INVALID;
+  if (B < 1 || Sq < 1 || Skv < 1 || Hq < 1 || Hkv < 1 || D < 1 || compute_units < 1)
+    return FA_ERR_INVALID;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (with_workspace != 0 && with_workspace != 1) return FA_ERR_INVALID;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  const int l2s = fa::split_log2(B, Sq, Skv, Hq, D, causal, compute_units);
-  const bool x8 = l2s > 0 || fa::use_eight_waves(B, Sq, Skv, Hq, D, causal, compute_units);
-  *kernel = x8 ? FA_KERNEL_EIGHT_WAVE : FA_KERNEL_FOUR_WAVE;
-  *key_ranges = 1 << l2s;
+  const fa::Plan p =
+      fa::make_plan(B, Sq, Skv, Hq, Hkv, D, causal, compute_units, with_workspace != 0);
+  *kernel = p.kernel;
+  *key_ranges = 1 << p.log2_ranges;
+  *workspace_bytes = p.ws_bytes;
   return FA_OK;
 }
 
@@ -144,6 +195,8 @@ const char* fa_strerror(int status) {
       return "unsupported argument (D must be 64 or 128, scale >= 0, sizes within the kernel's limits)";
     case FA_ERR_HIP:
       return "HIP runtime error at kernel launch";
+    case FA_ERR_WORKSPACE:
+      return "workspace too small for the split key ranges of this call (fa_fwd_plan gives the size)";
     default:
       return "unknown fa_status";
   }

@@ -102,23 +102,17 @@ hipError_t launch_t(const float* part_o, const float* part_lse, T* o, float* lse
   const int64_t rows = (int64_t)B * Hq * Sq;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   const dim3 block(kThreads);
+  const void* fn;
   switch (nsplit) {
-    case 2:
-      hipLaunchKernelGGL((combine_kernel<T, 2>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
-      break;
-    case 4:
-      hipLaunchKernelGGL((combine_kernel<T, 4>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
-      break;
-    case 8:
-      hipLaunchKernelGGL((combine_kernel<T, 8>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
-      break;
-    case 16:
-      hipLaunchKernelGGL((combine_kernel<T, 16>), grid, block, 0, stream, part_o, part_lse, o, lse, B, Hq, Sq);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 2: fn = reinterpret_cast<const void*>(&combine_kernel<T, 2>); break;
+    case 4: fn = reinterpret_cast<const void*>(&combine_kernel<T, 4>); break;
+    case 8: fn = reinterpret_cast<const void*>(&combine_kernel<T, 8>); break;
+    case 16: fn = reinterpret_cast<const void*>(&combine_kernel<T, 16>); break;
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  void* args[] = {&part_o, &part_lse, &o, &lse, &B, &Hq, &Sq};
+  // the launch's own status (an unrelated earlier error is not reported)
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace

@@ -2,11 +2,23 @@
 // gfx950 kernel launcher (not installed, not part of the public ABI).
 #pragma once
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fa {
 
 enum class DType { kBF16, kF16 };
+
+// Kernel shapes (the values of FA_KERNEL_* in fa.h).
+enum Kernel : int { kFourWave = 0, kEightWave = 1 };
+
+// The launch plan for one call: kernel shape, key ranges per item and the
+// bytes of partial results the split needs (0 without a split).
+struct Plan {
+  int kernel;
+  int log2_ranges;
+  size_t ws_bytes;
+};
 
 struct LaunchArgs {
   DType dtype;
@@ -18,6 +30,11 @@ struct LaunchArgs {
   int B, Sq, Skv, Hq, Hkv, D, causal;
   float c;  // scale * log2(e), clamped to >= FLT_MIN
   hipStream_t stream;
+  // Device memory for the partial results of split key ranges, owned by the
+  // caller (nullptr: never split).  The launch fails with FA_ERR_WORKSPACE
+  // when the plan splits and ws_bytes is less than it needs.
+  void* ws;
+  size_t ws_bytes;
 };
 
 // (batch, q-head, 256-row query tile) items of these sizes; the persistent
@@ -38,15 +55,27 @@ bool group_magic(int Hq, int Hkv, uint32_t* magic);
 int64_t min_item_tiles(int Sq, int Skv, int causal);
 // log2 of the key ranges each 512-row item is split into (0: no split).
 int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus);
+// Bytes of fp32 partial results (O and LSE) of 2^l2s key ranges.
+size_t split_ws_bytes(int B, int Sq, int Hq, int D, int l2s);
+// The plan for these sizes on a device with `cus` compute units; with
+// allow_split false (no workspace) key ranges are never split.
+Plan make_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, int cus,
+               bool allow_split);
 
 // Enqueue the kernel(s) (loading the code object on first use on the current
-// device); returns the launch status.
-hipError_t launch(const LaunchArgs& a);
+// device); returns an fa_status (FA_OK, FA_ERR_WORKSPACE, FA_ERR_HIP).
+int launch(const LaunchArgs& a);
 
 // Merge the partial results of `nsplit` key ranges (O fp32
 // [nsplit][B][Hq][Sq][128], LSE fp32 [nsplit][B][Hq][Sq]) into o (BSHD, the
 // input dtype) and lse ([B][Hq][Sq], may be null).
 hipError_t launch_combine(DType dtype, const float* part_o, const float* part_lse, void* o,
                           float* lse, int nsplit, int B, int Hq, int Sq, hipStream_t stream);
+
+// Argument checks shared by every forward entry point (no HIP call); on
+// FA_OK fills `a` (everything but ws / ws_bytes).
+int check_fwd_args(DType dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
+                   hipStream_t stream, LaunchArgs* a);
 
 }  // namespace fa

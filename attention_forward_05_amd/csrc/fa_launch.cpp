@@ -7,9 +7,10 @@
 // each item with keys spans at least 3 key tiles), eight waves (two per
 // SIMD, alternating MFMA and softmax phases) on 512-row tiles, which halves
 // the K/V traffic into LDS per FLOP and streams K/V tiles across items.
-// When the 512-row items would leave compute units idle and the key ranges
-// are long, each item's keys are split into 2..16 ranges whose partial
-// results a combine kernel (fa_combine.hip) merges.
+// When the 512-row items would leave compute units idle, the key ranges are
+// long and the caller passed a workspace, each item's keys are split into
+// 2..16 ranges whose partial results (in that workspace) a combine kernel
+// (fa_combine.hip) merges.  The library itself allocates no device memory.
 //
 // The kernels are persistent: the grid has G = min(items, compute units)
 // workgroups, one per CU, and workgroup g takes item r*G + (g or G-1-g,
@@ -27,6 +28,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "fa.h"
 #include "fa_kernel.h"
 
 extern "C" const unsigned char fa_hsaco_data[];
@@ -67,14 +69,6 @@ struct DeviceKernels {
   hipModule_t mod = nullptr;
   hipFunction_t fn[kKernels] = {};
   int cus = 0;  // compute units of the device
-  // The split path's buffer of partial results, kept for the next call and
-  // grown when a call needs more.  `done` is recorded on the caller's stream
-  // after the merge kernel; the next call (on any stream) makes its stream
-  // wait for it before overwriting the buffer, so calls never share it at the
-  // same time and the host never waits.
-  void* ws = nullptr;
-  size_t ws_bytes = 0;
-  hipEvent_t done = nullptr;
 };
 
 std::mutex g_mu;
@@ -97,8 +91,6 @@ hipError_t kernels_for_current_device(DeviceKernels** out) {
     e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (d.cus < 1) d.cus = 1;
-    e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
-    if (e != hipSuccess) return e;
     d.loaded = true;
   }
   *out = &d;
@@ -168,60 +160,49 @@ int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
 }
 int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
 
-hipError_t launch(const LaunchArgs& a) {
+size_t split_ws_bytes(int B, int Sq, int Hq, int D, int l2s) {
+  if (l2s <= 0) return 0;
+  const size_t rows = ((size_t)B * Hq * Sq) << l2s;
+  return rows * 4 * (size_t)(D + 1);
+}
+
+Plan make_plan(int B, int Sq, int Skv, int Hq, int /*Hkv*/, int D, int causal, int cus,
+               bool allow_split) {
+  Plan p;
+  p.log2_ranges = allow_split ? split_log2(B, Sq, Skv, Hq, D, causal, cus) : 0;
+  p.ws_bytes = split_ws_bytes(B, Sq, Hq, D, p.log2_ranges);
+  p.kernel = (p.log2_ranges > 0 || use_eight_waves(B, Sq, Skv, Hq, D, causal, cus)) ? kEightWave
+                                                                                    : kFourWave;
+  return p;
+}
+
+int launch(const LaunchArgs& a) {
   DeviceKernels* dk = nullptr;
-  hipError_t e = kernels_for_current_device(&dk);
-  if (e != hipSuccess) return e;
-  // Split key ranges when the 512-row items leave compute units idle: the
-  // partial results go to a stream-ordered temporary buffer and a combine
-  // kernel merges them into o / lse.
-  const int l2s = split_log2(a.B, a.Sq, a.Skv, a.Hq, a.D, a.causal, dk->cus);
-  if (l2s > 0) {
-    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-    const size_t lse_bytes = (size_t)(rows << l2s) * 4;
-    const size_t o_bytes = lse_bytes * a.D;
-    // the lock also keeps the event's record order that of the calls
-    std::lock_guard<std::mutex> lock(g_mu);
-    bool have = dk->ws_bytes >= o_bytes + lse_bytes;
-    if (!have) {
-      if (dk->ws) {
-        e = hipEventSynchronize(dk->done);  // the last call's kernels are done with it
-        if (e != hipSuccess) return e;
-        e = hipFree(dk->ws);
-        if (e != hipSuccess) return e;
-        dk->ws = nullptr;
-        dk->ws_bytes = 0;
-      }
-      if (hipMalloc(&dk->ws, o_bytes + lse_bytes) == hipSuccess) {
-        dk->ws_bytes = o_bytes + lse_bytes;
-        have = true;
-      } else {
-        dk->ws = nullptr;
-        (void)hipGetLastError();  // no buffer: whole key ranges instead
-      }
-    }
-    if (have) {
-      e = hipStreamWaitEvent(a.stream, dk->done, 0);
-      if (e != hipSuccess) return e;
-      LaunchArgs p = a;
-      p.o = dk->ws;
-      p.lse = reinterpret_cast<float*>(static_cast<char*>(dk->ws) + o_bytes);
-      e = launch_kernel(dk, p, a.dtype == DType::kBF16 ? 6 : 7, true, l2s);
-      if (e == hipSuccess)
-        e = launch_combine(a.dtype, static_cast<const float*>(dk->ws), p.lse, a.o, a.lse, 1 << l2s,
-                           a.B, a.Hq, a.Sq, a.stream);
-      const hipError_t f = hipEventRecord(dk->done, a.stream);
-      return e != hipSuccess ? e : f;
-    }
+  if (kernels_for_current_device(&dk) != hipSuccess) return FA_ERR_HIP;
+  const Plan p = make_plan(a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.D, a.causal, dk->cus, a.ws != nullptr);
+  hipError_t e;
+  if (p.log2_ranges > 0) {
+    // Split key ranges: the partial results go to the caller's workspace and
+    // the combine kernel merges them into o / lse on the same stream.
+    if (a.ws_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    const size_t lse_bytes = p.ws_bytes / (size_t)(a.D + 1);
+    LaunchArgs s = a;
+    s.o = a.ws;
+    s.lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + lse_bytes * a.D);
+    e = launch_kernel(dk, s, a.dtype == DType::kBF16 ? 6 : 7, true, p.log2_ranges);
+    if (e == hipSuccess)
+      e = launch_combine(a.dtype, static_cast<const float*>(s.o), s.lse, a.o, a.lse,
+                         1 << p.log2_ranges, a.B, a.Hq, a.Sq, a.stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
-  const bool x8 = use_eight_waves(a.B, a.Sq, a.Skv, a.Hq, a.D, a.causal, dk->cus);
+  const bool x8 = p.kernel == kEightWave;
   const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
                          : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
-  return launch_kernel(dk, a, variant, x8, 0);
+  e = launch_kernel(dk, a, variant, x8, 0);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 hipError_t launch_kernel(DeviceKernels* dk, const LaunchArgs& a, int variant, bool x8, int l2s) {
-  hipError_t e;
   KernArgs ka;
   memset(&ka, 0, sizeof(ka));
   ka.q = a.q;
@@ -246,10 +227,10 @@ hipError_t launch_kernel(DeviceKernels* dk, const LaunchArgs& a, int variant, bo
   size_t size = sizeof(ka);
   void* config[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &ka, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
                     HIP_LAUNCH_PARAM_END};
-  e = hipModuleLaunchKernel(dk->fn[variant], (unsigned)grid, 1, 1, x8 ? 512 : 256, 1, 1, 0,
-                            a.stream, nullptr, config);
-  if (e != hipSuccess) return e;
-  return hipGetLastError();
+  // the launch's own status: an earlier, unrelated error left in the
+  // runtime's last-error slot is neither reported nor cleared here
+  return hipModuleLaunchKernel(dk->fn[variant], (unsigned)grid, 1, 1, x8 ? 512 : 256, 1, 1, 0,
+                               a.stream, nullptr, config);
 }
 
 }  // namespace fa

@@ -45,7 +45,9 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 GPU"
-# Published dense MFMA peak of one MI355X for bf16 and fp16 (TFLOP/s).
+# Published dense MFMA peak of one MI355X for bf16 and fp16 (TFLOP/s).  The
+# bench also prints the peak that the device's own compute-unit count and
+# peak clock give (device_peak), beside this one.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -101,7 +103,8 @@ def launched_kernel(w: workloads.Workload, cus: int) -> str:
     with `cus` compute units, from the library's own plan query (with split
     key ranges a merge kernel follows it)."""
     import attention_forward_05_amd as fa
-    st, kern, ranges = fa.fa_fwd_plan(w.B, w.Sq, w.Skv, w.Hq, w.D, int(w.causal), cus)
+    st, kern, ranges, _ = fa.fa_fwd_plan(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D, int(w.causal), cus,
+                                         True)
     if st != fa.FA_OK:
         raise fa.FAError(st, "fa_fwd_plan")
     if kern == fa.FA_KERNEL_FOUR_WAVE:
@@ -109,6 +112,33 @@ def launched_kernel(w: workloads.Workload, cus: int) -> str:
     if ranges == 1:
         return f"fa_fwd_{w.dtype}_d128_x8_gfx950"
     return f"fa_fwd_{w.dtype}_d128_x8s_gfx950 ({ranges} key ranges) + combine_kernel"
+
+
+def device_peak(dtype: str):
+    """Compute units and peak shader clock of device 0, read from the HIP
+    runtime torch has loaded, and the dense MFMA peak they give
+    (4096 bf16/fp16 FLOP per clock per compute unit: 4 SIMDs x 1024)."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        return None
+    hip = ctypes.CDLL(path)
+    val = ctypes.c_int(0)
+    # hipDeviceAttributeClockRate = 5 (kHz), hipDeviceAttributeMultiprocessorCount = 63
+    if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) != 0:
+        return None
+    khz = val.value
+    if hip.hipDeviceGetAttribute(ctypes.byref(val), 63, 0) != 0:
+        return None
+    cus = val.value
+    flop_per_clk_cu = 4096 if dtype in ("bf16", "f16") else None
+    return {"compute_units": cus, "max_sclk_mhz": khz / 1e3,
+            "peak_tflops_from_clock": round(cus * flop_per_clk_cu * khz * 1e3 / 1e12, 1)}
 
 
 def algorithmic_bytes(w: workloads.Workload) -> int:
@@ -264,15 +294,20 @@ def main():
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     od = torch.empty_like(qd)
     lsed = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
-    entry = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f16
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # the workspace for split key ranges, allocated before the timed region
+    _, _, _, ws_bytes = fa.fa_fwd_plan(w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D, int(w.causal), cus,
+                                       True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F16
 
     def step():
-        st = entry(qd, kd, vd, od, lsed, w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D,
-                   int(w.causal), w.scale, sh)
+        st = fa.fa_fwd_ws(dt, qd, kd, vd, od, lsed, w.B, w.Sq, w.Skv, w.Hq, w.Hkv, w.D,
+                          int(w.causal), w.scale, ws, ws_bytes, sh)
         if st != fa.FA_OK:
-            raise fa.FAError(st, "fa_fwd")
+            raise fa.FAError(st, "fa_fwd_ws")
 
     for _ in range(args.warmup):
         step()
@@ -305,7 +340,8 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    kernel = launched_kernel(w, torch.cuda.get_device_properties(0).multi_processor_count)
+    kernel = launched_kernel(w, cus)
+    dev_peak = device_peak(w.dtype)
     traffic = measured_traffic(w.name, kernel)
     log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak:.0f}); launch avg {launch_avg_ms * 1e3:.1f} us, "
@@ -344,7 +380,9 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_launch_avg_us": round(launch_avg_ms * 1e3, 2),
+            "timing": f"HIP events around each of {args.steps} launches on the launch stream",
             "kernel": kernel,
+            "device": dev_peak,
         },
         "cpu_baseline": cpu,
     }

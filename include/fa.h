@@ -36,6 +36,7 @@
 #define LIBFA_FA_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -47,15 +48,21 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID = -1,     /* bad argument: NULL pointer, size < 1, Hq % Hkv != 0,
                               causal not 0/1, scale not finite, pointer not
-                              16-byte aligned, o overlapping q/k/v, size overflow */
+                              16-byte aligned, o overlapping q/k/v, a workspace
+                              overlapping a tensor, size overflow, unknown dtype */
   FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64 or 128,
                               scale < 0, sizes beyond the kernel's limits
                               (ceil(Sq/256) at most 65535, B*Hq*ceil(Sq/256)
                               below 2^24, ceil(Skv/64) below 65536,
                               Sq*Hq*D*2 bytes, B*Sq*Hq and B*Skv below 2^31) */
-  FA_ERR_HIP = -3          /* the HIP runtime reported an error loading the
+  FA_ERR_HIP = -3,         /* the HIP runtime reported an error loading the
                               kernels or at launch */
+  FA_ERR_WORKSPACE = -4    /* the call splits its key ranges and the workspace
+                              given is smaller than fa_fwd_plan reports */
 } fa_status;
+
+/* Element types of q, k, v and o for the entry points that take a dtype. */
+enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F16 = 1 };
 
 /*
  * fa_fwd -- bf16 inputs and output.
@@ -72,30 +79,16 @@ typedef enum {
  *   stream : HIP stream to enqueue on (NULL = the default stream)
  *
  * All pointers are owned by the caller and must be 16-byte aligned.  The
- * only state the library keeps is its kernel code: the first call on a
+ * library allocates no device memory.  The only state it keeps is its
+ * kernel code and the device's compute-unit count: the first call on a
  * device loads the library's gfx950 code object on that device (under a
  * lock, so concurrent first calls are safe) and keeps it until the process
  * ends; a failed load returns FA_ERR_HIP.  Calls on different streams may
- * run concurrently.  The call is asynchronous: it returns once its kernels
- * are enqueued, and o / lse are valid after the stream has been
- * synchronised.
+ * run concurrently.  The call is asynchronous: it returns once its kernel is
+ * enqueued, and o / lse are valid after the stream has been synchronised.
  *
- * Split key ranges (D = 128 only): when the (batch, q-head, 512-row query
- * tile) items are fewer than the device's compute units and every item's
- * key range is long, each item's keys are cut into 2, 4, 8 or 16 ranges (the
- * one-device form of the kernbench GQA prefill page's split of the key
- * sequence over PE groups; fa_fwd_plan reports the choice).  The ranges'
- * partial results (fp32 O and LSE, 516 bytes per query row and range) go to
- * a device buffer the library keeps per device, and a second kernel merges
- * them into o / lse (`_merge_running` on that page).  The buffer is taken
- * with hipMalloc on the first such call and grown (hipFree of the old one
- * after its last use, then hipMalloc) when a call needs more; it is held
- * until the process ends (at most 516 * 512 * 2 * compute units bytes:
- * 135 MB on 256 compute units).  Calls hand it on with a device-side event
- * wait, so split calls on different streams run one after the other on the
- * device, and the host never waits except when the buffer grows.  If it
- * cannot be allocated the call runs unsplit instead (same result).  Calls
- * that do not split allocate nothing.
+ * fa_fwd never splits an item's key range (it has no memory for partial
+ * results); fa_fwd_ws does, given a workspace.
  *
  * Returns FA_OK or one of the error codes above.
  */
@@ -108,6 +101,36 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o,
                float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
                int causal, float scale, hipStream_t stream);
 
+/*
+ * fa_fwd_ws -- the forward pass with a caller-owned workspace for split key
+ * ranges; dtype is FA_DTYPE_BF16 or FA_DTYPE_F16, the other arguments are
+ * those of fa_fwd.
+ *
+ * When the (batch, q-head, 512-row query tile) items are fewer than the
+ * device's compute units and every item's key range is long (D = 128), each
+ * item's keys are cut into 2, 4, 8 or 16 ranges: the one-device form of the
+ * kernbench GQA prefill page's split of the key sequence over PE groups.
+ * Each range's partial result (fp32 O normalised over the range's keys and
+ * the range's LSE, 4*(D+1) bytes per query row and range) goes to the
+ * workspace, and a second kernel on the same stream merges them into o and
+ * lse (that page's `_merge_running`).  fa_fwd_plan reports the number of
+ * ranges and the workspace bytes the call needs.
+ *
+ *   workspace       : device memory, 16-byte aligned, overlapping no tensor
+ *                     of the call; or NULL: then the call never splits and
+ *                     behaves exactly as fa_fwd / fa_fwd_f16.
+ *   workspace_bytes : its size in bytes (> 0 when workspace is not NULL).
+ *
+ * The workspace's contents are undefined after the call; it is in use until
+ * the stream passes the call, so calls that run concurrently need distinct
+ * workspaces.  A call that splits with workspace_bytes smaller than it needs
+ * returns FA_ERR_WORKSPACE before enqueueing anything.
+ */
+int fa_fwd_ws(int dtype, const void* q, const void* k, const void* v, void* o,
+              float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
+              int causal, float scale, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
 /* Kernel shapes reported by fa_fwd_plan. */
 enum {
   FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD */
@@ -115,20 +138,25 @@ enum {
 };
 
 /*
- * fa_fwd_plan -- host-only query (no HIP call): the kernel shape and the
- * number of key ranges per item that fa_fwd / fa_fwd_f16 use for these sizes
- * on a device with `compute_units` compute units (256 on an MI355X).
+ * fa_fwd_plan -- host-only query (no HIP call): what a forward call of these
+ * sizes does on a device with `compute_units` compute units (256 on an
+ * MI355X).  with_workspace = 0 gives the plan of fa_fwd / fa_fwd_f16 (and of
+ * fa_fwd_ws without a workspace), 1 that of fa_fwd_ws with a large enough
+ * workspace.
  *
- *   kernel     : written, FA_KERNEL_FOUR_WAVE or FA_KERNEL_EIGHT_WAVE
- *   key_ranges : written, 1 (whole key ranges) or 2, 4, 8, 16 (split key
- *                ranges merged by a second kernel)
+ *   kernel          : written, FA_KERNEL_FOUR_WAVE or FA_KERNEL_EIGHT_WAVE
+ *   key_ranges      : written, 1 (whole key ranges) or 2, 4, 8, 16 (split
+ *                     key ranges merged by a second kernel)
+ *   workspace_bytes : written, the workspace the split needs (0 without one)
  *
  * Returns FA_OK, FA_ERR_INVALID (NULL output pointer, size or compute_units
- * < 1, causal not 0/1) or FA_ERR_UNSUPPORTED (D not 64 or 128); the outputs
- * are written only on FA_OK.  Size limits of fa_fwd are not checked here.
+ * < 1, Hq % Hkv != 0, causal or with_workspace not 0/1) or
+ * FA_ERR_UNSUPPORTED (D not 64 or 128); the outputs are written only on
+ * FA_OK.  Size limits of fa_fwd are not checked here.
  */
-int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int D, int causal, int compute_units,
-                int* kernel, int* key_ranges);
+int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,
+                int compute_units, int with_workspace, int* kernel,
+                int* key_ranges, size_t* workspace_bytes);
 
 /* fa_strerror -- a static, NUL-terminated description of a status code
  * (never NULL; unknown codes give "unknown fa_status"). */

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_strerror(lib):
     assert fa.fa_strerror(fa.FA_OK) == "success"
-    for code in (fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+    for code in (fa.FA_ERR_INVALID, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, fa.FA_ERR_WORKSPACE):
         s = fa.fa_strerror(code)
         assert s and s != "unknown fa_status"
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -111,10 +111,11 @@ def test_python_wrapper_raises_on_bad_tensors(lib):
 # worked out by hand from the rule stated in include/fa.h and the launcher:
 # eight waves (512-row items) when B*Hq*ceil(Sq/512) >= compute units and the
 # shortest item with a visible key spans >= 3 key tiles of 64; else, with
-# D = 128 and fewer items than compute units, the fewest power-of-two key
-# ranges (<= 16) that cover the compute units, reduced until every range of
-# the shortest item keeps >= 16 key tiles (>= 64 when B*Hq*ceil(Sq/256)
-# already covers the compute units).
+# D = 128, a workspace and fewer items than compute units, the fewest
+# power-of-two key ranges (<= 16) that cover the compute units, reduced until
+# every range of the shortest item keeps >= 16 key tiles (>= 64 when
+# B*Hq*ceil(Sq/256) already covers the compute units).  The workspace of a
+# split is ranges * B*Hq*Sq rows * (D + 1) * 4 bytes.
 PLAN_CASES = [
     # B, Sq, Skv, Hq, D, causal, cus, kernel, key_ranges
     (2, 4096, 4096, 32, 128, 1, 256, 1, 1),    # 256 items: eight waves, whole ranges
@@ -136,7 +137,20 @@ PLAN_CASES = [
 
 @pytest.mark.parametrize("B,Sq,Skv,Hq,D,causal,cus,kernel,ranges", PLAN_CASES)
 def test_plan(lib, B, Sq, Skv, Hq, D, causal, cus, kernel, ranges):
-    assert fa.fa_fwd_plan(B, Sq, Skv, Hq, D, causal, cus) == (fa.FA_OK, kernel, ranges)
+    ws = 0 if ranges == 1 else ranges * B * Hq * Sq * (D + 1) * 4
+    assert fa.fa_fwd_plan(B, Sq, Skv, Hq, 1, D, causal, cus, True) == (fa.FA_OK, kernel, ranges, ws)
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,D,causal,cus,kernel,ranges", PLAN_CASES)
+def test_plan_without_workspace_never_splits(lib, B, Sq, Skv, Hq, D, causal, cus, kernel, ranges):
+    """fa_fwd has no memory for partial results: whole key ranges, on the
+    eight-wave kernel only where its 512-row items cover the compute units."""
+    st, kern, nr, ws = fa.fa_fwd_plan(B, Sq, Skv, Hq, 1, D, causal, cus, False)
+    assert (st, nr, ws) == (fa.FA_OK, 1, 0)
+    if ranges == 1:
+        assert kern == kernel
+    else:
+        assert kern == fa.FA_KERNEL_FOUR_WAVE  # split cases have too few 512-row items
 
 
 def test_plan_items_without_keys(lib):
@@ -144,25 +158,64 @@ def test_plan_items_without_keys(lib):
     # 512-row tile reaches only keys 0..11 (1 key tile): four waves.
     # Sq = 1200, Skv = 100: rows below 1100 see nothing, so tiles 0 and 1
     # have no key and tile 2 ends at key 100 (2 key tiles): four waves.
-    assert fa.fa_fwd_plan(1, 600, 100, 256, 128, 1, 256) == (fa.FA_OK, 0, 1)
-    assert fa.fa_fwd_plan(1, 1200, 100, 256, 128, 1, 256) == (fa.FA_OK, 0, 1)
+    assert fa.fa_fwd_plan(1, 600, 100, 256, 256, 128, 1, 256, True) == (fa.FA_OK, 0, 1, 0)
+    assert fa.fa_fwd_plan(1, 1200, 100, 256, 256, 128, 1, 256, True) == (fa.FA_OK, 0, 1, 0)
     # Sq = 1200, Skv = 300: tile 0 none (rows < 900 see nothing), tile 1
     # (rows 512..1023) ends at key min(1024 - 900, 300) = 124 (2 tiles);
     # Skv = 1100: tile 0 ends at key 412 (7 tiles): eight waves
-    assert fa.fa_fwd_plan(1, 1200, 300, 256, 128, 1, 256) == (fa.FA_OK, 0, 1)
-    assert fa.fa_fwd_plan(1, 1200, 1100, 256, 128, 1, 256) == (fa.FA_OK, 1, 1)
+    assert fa.fa_fwd_plan(1, 1200, 300, 256, 256, 128, 1, 256, True) == (fa.FA_OK, 0, 1, 0)
+    assert fa.fa_fwd_plan(1, 1200, 1100, 256, 256, 128, 1, 256, True) == (fa.FA_OK, 1, 1, 0)
 
 
 @pytest.mark.parametrize("over,status", [
     (dict(B=0), fa.FA_ERR_INVALID), (dict(Sq=0), fa.FA_ERR_INVALID),
     (dict(Skv=-1), fa.FA_ERR_INVALID), (dict(Hq=0), fa.FA_ERR_INVALID),
+    (dict(Hkv=0), fa.FA_ERR_INVALID), (dict(Hkv=3), fa.FA_ERR_INVALID),
     (dict(causal=2), fa.FA_ERR_INVALID), (dict(cus=0), fa.FA_ERR_INVALID),
-    (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=2), fa.FA_ERR_INVALID), (dict(ws=-1), fa.FA_ERR_INVALID),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(D=32), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(lib, over, status):
-    a = dict(B=1, Sq=512, Skv=8192, Hq=4, D=128, causal=0, cus=256)
+    a = dict(B=1, Sq=512, Skv=8192, Hq=4, Hkv=2, D=128, causal=0, cus=256, ws=1)
     a.update(over)
-    assert fa.fa_fwd_plan(a["B"], a["Sq"], a["Skv"], a["Hq"], a["D"], a["causal"],
-                          a["cus"]) == (status, None, None)
+    kern, ranges, ws = ctypes.c_int(-7), ctypes.c_int(-7), ctypes.c_size_t(7)
+    st = lib.fa_fwd_plan(a["B"], a["Sq"], a["Skv"], a["Hq"], a["Hkv"], a["D"], a["causal"],
+                         a["cus"], a["ws"], ctypes.byref(kern), ctypes.byref(ranges),
+                         ctypes.byref(ws))
+    assert st == status
+    assert (kern.value, ranges.value, ws.value) == (-7, -7, 7)  # untouched on error
     # NULL output pointers
-    assert lib.fa_fwd_plan(1, 512, 8192, 4, 128, 0, 256, None, None) == fa.FA_ERR_INVALID
+    assert lib.fa_fwd_plan(1, 512, 8192, 4, 2, 128, 0, 256, 1, None, None, None) == fa.FA_ERR_INVALID
+
+
+# fa_fwd_ws: the same checks as fa_fwd, plus the dtype and the workspace
+WS = 6 << 40
+
+
+def _call_ws(dtype=0, ws=WS, ws_bytes=1 << 20, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.fa_fwd_ws(dtype, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Sq"],
+                        a["Skv"], a["Hq"], a["Hkv"], a["D"], a["causal"], a["scale"], ws,
+                        ws_bytes, 0)
+
+
+@pytest.mark.parametrize("over", INVALID, ids=[str(x) for x in INVALID])
+def test_ws_invalid_arguments(lib, over):
+    assert _call_ws(**over) == fa.FA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", UNSUPPORTED, ids=[str(x) for x in UNSUPPORTED])
+def test_ws_unsupported_arguments(lib, over):
+    assert _call_ws(**over) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("args", [
+    dict(dtype=2), dict(dtype=-1),                     # unknown dtype
+    dict(ws=WS + 8), dict(ws=WS + 1),                  # workspace not 16-byte aligned
+    dict(ws_bytes=0),                                  # a workspace of no bytes
+    dict(ws=Q), dict(ws=K - 64), dict(ws=V + 4096),    # overlapping q, k, v
+    dict(ws=O + 16), dict(ws=L - 16),                  # overlapping o, lse
+])
+def test_ws_rejects_bad_workspace(lib, args):
+    assert _call_ws(**args) == fa.FA_ERR_INVALID

@@ -3,8 +3,9 @@
 The oracle is only trusted once it agrees with things that do not come from
 itself: closed forms, invariants of the online-softmax merge, special cases
 that reduce to a textbook result, and two independent library formulations
-(a NumPy einsum transcription of the JAX page's ``attention_reference`` and
-PyTorch's CPU ``scaled_dot_product_attention`` in float64).  The cases are
+(the softmax definition evaluated on whole matrices with SciPy's
+``logsumexp``, and PyTorch's CPU ``scaled_dot_product_attention`` in
+float64).  The cases are
 chosen so that a dropped term, a wrong sign, a wrong index or a transposed
 operand in ``oracle.c`` fails at least one of them; ``test_oracle_mutants.py``
 checks that claim by compiling broken copies of the oracle.
@@ -291,35 +292,45 @@ def test_gqa_contiguous_grouping():
 # independent library formulations
 # --------------------------------------------------------------------------
 
-def _jax_page_reference(q, k, v, causal):
-    """The JAX page's `attention_reference`, transcribed into NumPy (it applies
-    no scale and a top-left mask, so it is called with Sq == Skv and the
-    scale folded into q by the caller).  Returns out and the page's base-2 lse
-    in [B, Hq, Sq]."""
-    B, Sq, Hq, D = q.shape
-    Skv, Hkv = k.shape[1], k.shape[2]
-    qr = q.reshape(B, Sq, Hkv, Hq // Hkv, D)
-    logits = np.einsum("bqHhc,bkHc->bqHhk", qr, k)
+def _softmax_definition(q, k, v, causal, scale, Hq, Hkv):
+    """Masked softmax attention evaluated from its definition on whole
+    matrices: the weights of a row are exp(s_j - LSE) over its visible keys,
+    with LSE = logsumexp of the row's visible logits (SciPy's routine), and O
+    is the weighted sum of the V rows.  Returns O [B,Sq,Hq,D] and the
+    natural-log LSE [B,Hq,Sq]."""
+    from scipy.special import logsumexp
+    s = _logits(q, k, scale, Hq, Hkv)                     # [B, Hq, Sq, Skv]
     if causal:
-        mask = np.arange(Sq)[:, None] >= np.arange(Skv)[None, :]
-        logits = np.where(mask[:, None, None, :], logits, -np.inf)
-    m = logits.max(axis=-1, keepdims=True)
-    un = np.exp(logits - m)
-    l = un.sum(axis=-1, keepdims=True)
-    out = np.einsum("bqHhk,bkHc->bqHhc", un / l, v).reshape(q.shape)
-    lse2 = (m * math.log2(math.e) + np.log2(l)).reshape(B, Sq, Hq)
-    return out, lse2.transpose(0, 2, 1)
+        s = np.where(_bottom_right_mask(s.shape[2], s.shape[3]), s, -np.inf)
+    lse = logsumexp(s, axis=-1)                           # [B, Hq, Sq]
+    w = np.exp(s - lse[..., None])
+    v_rep = np.repeat(_f64(v), Hq // Hkv, axis=2)         # [B, Skv, Hq, D]
+    o = np.einsum("bhij,bjhd->bihd", w, v_rep)
+    return o, lse
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_against_jax_page_reference(causal):
+def test_against_softmax_definition(causal):
     B, S, Hq, Hkv, D = 2, 24, 4, 2, 64
     q, k, v = _inputs(B, S, S, Hq, Hkv, D, seed=12)
     o, lse = oracle.attn_fwd(q, k, v, causal, 1.0)
-    o_ref, lse2_ref = _jax_page_reference(_f64(q), _f64(k), _f64(v), causal)
+    o_ref, lse_ref = _softmax_definition(q, k, v, causal, 1.0, Hq, Hkv)
     np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
-    # base-2 residual of the page = natural-log LSE * log2(e)
-    np.testing.assert_allclose(lse * math.log2(math.e), lse2_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_base2_residual_identity():
+    """The JAX page keeps a base-2 residual: row max (in natural-log units)
+    times log2(e) plus log2 of the row's sum of exp(s_j - max).  The oracle's
+    natural-log LSE times log2(e) must equal it."""
+    B, S, Hq, Hkv, D = 1, 20, 2, 1, 64
+    q, k, v = _inputs(B, S, S, Hq, Hkv, D, seed=16)
+    _, lse = oracle.attn_fwd(q, k, v, True, 0.3)
+    s = _logits(q, k, 0.3, Hq, Hkv)
+    s = np.where(_bottom_right_mask(S, S), s, -np.inf)
+    m = s.max(axis=-1)
+    resid2 = m * math.log2(math.e) + np.log2(np.exp(s - m[..., None]).sum(axis=-1))
+    np.testing.assert_allclose(lse * math.log2(math.e), resid2, rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,D,causal,scale", [

@@ -43,7 +43,7 @@ PIN_CALLS = [
     lambda: pins.test_merge_of_partials_equals_one_shot(True),
     lambda: pins.test_merge_identity_commutes_and_associates(),
     lambda: pins.test_gqa_contiguous_grouping(),
-    lambda: pins.test_against_jax_page_reference(True),
+    lambda: pins.test_against_softmax_definition(True),
     lambda: pins.test_against_torch_sdpa_float64(2, 9, 31, 4, 2, 64, True, 0.0884),
 ]
 

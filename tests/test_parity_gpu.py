@@ -3,11 +3,14 @@
 Bar (per element, O widened to fp64): max |dO| <= 2e-2, mean |dO| <= 2e-3,
 max |dLSE| <= 1e-3, both sides reading the same rounded input bits.
 
-* Small and ragged shapes are compared element by element on every output.
-* The five named workloads run at full size in the launch configuration the
-  benchmark times; the oracle checks sampled rows (first/last rows, rows
-  around every 256-row tile edge of the kernel, random rows), and a
-  property that holds at any size (V = 1 gives O = 1) covers every output.
+* Every case is compared element by element on every output, the five
+  named workloads included: they run at full size in the launch
+  configuration the benchmark times, and the oracle evaluates all their
+  rows (a few minutes of host time for the largest).  A property that holds
+  at any size (V = 1 gives O = 1) is checked on them as well.
+* Split key ranges run through fa_fwd_ws with a workspace of the size
+  fa_fwd_plan reports; decode-shaped calls (a few query rows over long key
+  ranges) among them.
 """
 import math
 
@@ -32,17 +35,26 @@ def fa():
     return m
 
 
-def run_gpu(fa, q, k, v, causal, scale, with_lse=True, stream=None):
+def run_gpu(fa, q, k, v, causal, scale, with_lse=True, stream=None, split=False):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o, lse = fa.attention(qd, kd, vd, causal, scale, with_lse=with_lse, stream=stream)
+    o, lse = fa.attention(qd, kd, vd, causal, scale, with_lse=with_lse, stream=stream,
+                          split=split)
     torch.cuda.synchronize()
     return o.cpu().double().numpy(), (lse.cpu().double().numpy() if with_lse else None)
 
 
-def check(o, lse, o_ref, lse_ref, what=""):
+def check(o, lse, o_ref, lse_ref, what="", figures=None):
     assert np.all(np.isfinite(o)), f"{what}: non-finite O"
     do = np.abs(o - o_ref)
+    if figures is not None:
+        dl_all = 0.0
+        if lse is not None:
+            live = ~np.isneginf(lse_ref)
+            if live.any():
+                dl_all = float(np.abs(lse[live] - lse_ref[live]).max())
+        figures.append(f"{what}: max|dO| {do.max():.3e}  mean|dO| {do.mean():.3e}  "
+                       f"max|dLSE| {dl_all:.3e}  ({o.size} O elements)")
     assert do.max() <= MAX_DO, f"{what}: max|dO| {do.max():.3e}"
     assert do.mean() <= MEAN_DO, f"{what}: mean|dO| {do.mean():.3e}"
     if lse is not None:
@@ -55,13 +67,24 @@ def check(o, lse, o_ref, lse_ref, what=""):
 
 
 def full_case(fa, B, Sq, Skv, Hq, Hkv, D, causal, dtype="bf16", seed=0, scale=None, dist="normal",
-              boost=0.0):
+              boost=0.0, split=False):
     q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, D, dtype, seed, k_row_boost_frac=boost, dist=dist)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    o, lse = run_gpu(fa, q, k, v, causal, scale)
+    o, lse = run_gpu(fa, q, k, v, causal, scale, split=split)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale)
     return check(o, lse, o_ref, lse_ref, f"B{B} Sq{Sq} Skv{Skv} Hq{Hq} Hkv{Hkv} D{D} c{causal} {dtype}")
+
+
+def compute_units():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def plan(fa, B, Sq, Skv, Hq, Hkv, D, causal, with_ws):
+    st, kern, ranges, ws = fa.fa_fwd_plan(B, Sq, Skv, Hq, Hkv, D, int(causal), compute_units(),
+                                          with_ws)
+    assert st == fa.FA_OK
+    return kern, ranges, ws
 
 
 # ---------------------------------------------------------------------------
@@ -79,10 +102,18 @@ def test_ragged_shapes_bf16(fa, Sq, Skv, causal, D):
     full_case(fa, 1, Sq, Skv, 2, 1, D, causal, "bf16", seed=Sq * 7 + Skv)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Sq,Skv", [(300, 300), (17, 1000), (1000, 17), (257, 513)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ragged_shapes_f16(fa, Sq, Skv, causal):
-    full_case(fa, 2, Sq, Skv, 4, 2, 128, causal, "f16", seed=Sq + Skv)
+def test_ragged_shapes_f16(fa, Sq, Skv, causal, D):
+    full_case(fa, 2, Sq, Skv, 4, 2, D, causal, "f16", seed=Sq + Skv + D)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_d64_long_keys_and_gqa(fa, dtype):
+    """D = 64 (the four-wave kernel's second head size) over long, ragged key
+    ranges with GQA 4, causal bottom-right."""
+    full_case(fa, 2, 700, 3001, 16, 4, 64, True, dtype, seed=31)
 
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
@@ -168,7 +199,19 @@ X8_CASES = [
 
 @pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype", X8_CASES)
 def test_eight_wave_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype):
+    if compute_units() == 256:
+        for with_ws in (False, True):
+            assert plan(fa, B, Sq, Skv, Hq, Hkv, 128, causal, with_ws) == (
+                fa.FA_KERNEL_EIGHT_WAVE, 1, 0)
     full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 3 * Skv + Hkv)
+
+
+def test_eight_wave_slow_path_bf16(fa):
+    """bf16 on the eight-wave kernel with 1% of the key rows scaled by 8: the
+    reference max moves (the slow path) in bf16 as well."""
+    if compute_units() == 256:
+        assert plan(fa, 1, 256, 1024, 256, 8, 128, True, False)[0] == fa.FA_KERNEL_EIGHT_WAVE
+    full_case(fa, 1, 256, 1024, 256, 8, 128, True, "bf16", seed=24, boost=0.01)
 
 
 # ---------------------------------------------------------------------------
@@ -190,29 +233,65 @@ SPLIT_CASES = [
 
 @pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype,ranges", SPLIT_CASES)
 def test_split_key_ranges(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, ranges):
-    import torch
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    st, kern, nr = fa.fa_fwd_plan(B, Sq, Skv, Hq, 128, int(causal), cus)
-    assert st == fa.FA_OK and kern == fa.FA_KERNEL_EIGHT_WAVE
-    if cus == 256:
-        assert nr == ranges
-    full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 7 * Skv + Hq)
+    kern, nr, ws = plan(fa, B, Sq, Skv, Hq, Hkv, 128, causal, True)
+    assert kern == fa.FA_KERNEL_EIGHT_WAVE
+    if compute_units() == 256:
+        assert nr == ranges and ws == ranges * B * Hq * Sq * 129 * 4
+    full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 7 * Skv + Hq, split=True)
+
+
+def test_split_shape_without_workspace(fa):
+    """fa_fwd on a shape fa_fwd_ws would split: whole key ranges, same bar."""
+    assert plan(fa, 1, 1000, 16384, 8, 2, 128, True, False)[1] == 1
+    full_case(fa, 1, 1000, 16384, 8, 2, 128, True, "bf16", seed=5)
+
+
+# decode-shaped calls: a few query rows (Sq <= 64) over long key ranges,
+# GQA 4 and 8, with a workspace (split key ranges)
+DECODE_CASES = [
+    # B, Sq, Skv, Hq, Hkv, causal, dtype
+    (1, 1, 16384, 32, 8, False, "bf16"),
+    (1, 1, 32768, 64, 8, True, "f16"),
+    (2, 4, 16384, 32, 8, True, "bf16"),
+    (1, 16, 32768, 32, 4, False, "bf16"),
+    (1, 16, 16384, 16, 4, True, "f16"),
+    (1, 64, 16384, 32, 8, True, "bf16"),
+    (1, 64, 32768, 64, 8, False, "f16"),
+    (3, 7, 20000, 24, 3, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype", DECODE_CASES)
+def test_decode_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, parity_figures):
+    q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, 128, dtype, 200 + Sq + Hq)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_gpu(fa, q, k, v, causal, scale, split=True)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale)
+    check(o, lse, o_ref, lse_ref, f"decode B{B} Sq{Sq} Skv{Skv} Hq{Hq} Hkv{Hkv} c{causal} {dtype}",
+          figures=parity_figures)
+    # and without a workspace: whole key ranges, same bar
+    o2, lse2 = run_gpu(fa, q, k, v, causal, scale)
+    check(o2, lse2, o_ref, lse_ref, "decode (no workspace)")
+
+
+def test_long_key_range_few_rows(fa):
+    """A key range of about a million keys (16384 key tiles, the ragged last
+    one with 63 keys) for three query rows."""
+    full_case(fa, 1, 3, (1 << 20) - 1, 8, 2, 128, True, "bf16", seed=41, split=True)
 
 
 def test_split_without_lse(fa):
     """lse = NULL on the split path: the merge still needs the partial LSEs
     (which the kernel always writes), and O must not change."""
     q, k, v = workloads.make_inputs(1, 1000, 16384, 8, 2, 128, "bf16", 5)
-    o1, l1 = run_gpu(fa, q, k, v, True, 0.088)
-    o2, _ = run_gpu(fa, q, k, v, True, 0.088, with_lse=False)
+    o1, l1 = run_gpu(fa, q, k, v, True, 0.088, split=True)
+    o2, _ = run_gpu(fa, q, k, v, True, 0.088, with_lse=False, split=True)
     assert np.array_equal(o1, o2)
 
 
-def test_split_streams_and_buffer_growth(fa):
-    """Split calls on two streams, queued without a host wait, the second
-    needing a larger partial buffer than the first: both give the same bits
-    as when run one at a time (the library's buffer is handed from call to
-    call by a device-side event wait)."""
+def test_split_streams_own_workspaces(fa):
+    """Split calls on two streams, queued without a host wait, each with a
+    workspace of its own: the same bits as when run one at a time."""
     dev = torch.device("cuda:0")
     shapes = [(1, 512, 8192, 4, 4, False), (1, 1000, 16384, 8, 2, True), (1, 512, 8192, 4, 4, False)]
     ins = []
@@ -221,28 +300,52 @@ def test_split_streams_and_buffer_growth(fa):
         ins.append((q.to(dev), k.to(dev), v.to(dev), causal))
     ref = []
     for q, k, v, causal in ins:
-        o, lse = fa.attention(q, k, v, causal, 0.088)
+        o, lse = fa.attention(q, k, v, causal, 0.088, split=True)
         torch.cuda.synchronize()
         ref.append((o.clone(), lse.clone()))
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
-    outs = []
+    outs, keep = [], []
     for n, (q, k, v, causal) in enumerate(ins):
+        B, Sq, Hq, D = q.shape
+        Skv, Hkv = k.shape[1], k.shape[2]
+        _, _, nr, nbytes = fa.fa_fwd_plan(B, Sq, Skv, Hq, Hkv, D, int(causal), compute_units(), True)
+        assert nr > 1
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         o = torch.full_like(q, float("nan"))
-        lse = torch.full((q.shape[0], q.shape[2], q.shape[1]), float("nan"), device=dev)
+        lse = torch.full((B, Hq, Sq), float("nan"), device=dev)
         st = streams[n % 2]
         st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            fa.attention(q, k, v, causal, 0.088, out=o, lse=lse, stream=st)
+        assert fa.fa_fwd_ws(fa.FA_DTYPE_BF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D,
+                            int(causal), 0.088, ws, nbytes, st) == fa.FA_OK
         outs.append((o, lse))
+        keep.append(ws)
     torch.cuda.synchronize()
     for (o, lse), (o_ref, lse_ref) in zip(outs, ref):
         assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
 
 
+def test_split_workspace_too_small(fa):
+    """A workspace one byte short of what fa_fwd_plan reports: FA_ERR_WORKSPACE,
+    nothing enqueued (the outputs keep their contents)."""
+    dev = torch.device("cuda:0")
+    B, Sq, Skv, Hq, Hkv = 1, 512, 8192, 4, 4
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(B, Sq, Skv, Hq, Hkv, 128, "bf16", 3))
+    _, _, nr, nbytes = fa.fa_fwd_plan(B, Sq, Skv, Hq, Hkv, 128, 0, compute_units(), True)
+    assert nr > 1
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((B, Hq, Sq), 7.0, device=dev)
+    st = fa.fa_fwd_ws(fa.FA_DTYPE_BF16, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, 128, 0, 0.088,
+                      ws, nbytes - 16, None)
+    torch.cuda.synchronize()
+    assert st == fa.FA_ERR_WORKSPACE
+    assert torch.all(o == 7.0) and torch.all(lse == 7.0)
+
+
 def test_split_slow_path(fa):
     """Key rows scaled by 8 in every range: the reference max moves inside
     ranges, and the ranges' LSEs differ widely before the merge."""
-    full_case(fa, 1, 512, 8192, 4, 2, 128, False, "f16", seed=23, boost=0.01)
+    full_case(fa, 1, 512, 8192, 4, 2, 128, False, "f16", seed=23, boost=0.01, split=True)
 
 
 @pytest.mark.parametrize("case", ["scale1", "kboost"])
@@ -261,38 +364,17 @@ def test_eight_wave_slow_path(fa, case):
 # the five named workloads at full size
 # ---------------------------------------------------------------------------
 
-def _sample_rows(w, n_random=1536, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set()
-    ii = {0, 1, w.Sq - 1, w.Sq - 2}
-    for t in range(0, w.Sq, 256):
-        ii.update({t, t + 63, t + 64, t + 255})
-    ii = sorted(i for i in ii if 0 <= i < w.Sq)
-    heads = sorted({0, w.Hq - 1, w.Hq // 2})
-    for b in {0, w.B - 1}:
-        for hq in heads:
-            for i in ii:
-                rows.add((b, hq, i))
-    for _ in range(n_random):
-        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.Sq))))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("w", workloads.WORKLOADS + workloads.SPLIT_WORKLOADS,
                          ids=[w.name for w in workloads.WORKLOADS + workloads.SPLIT_WORKLOADS])
-def test_named_workload(fa, w):
+def test_named_workload(fa, w, parity_figures):
+    """Every output element of the workload at full size against the oracle
+    over all B*Hq*Sq rows (the split workloads through fa_fwd_ws, as the
+    benchmark runs them)."""
     q, k, v = workloads.workload_inputs(w)
-    o, lse = run_gpu(fa, q, k, v, w.causal, w.scale)
-    small = w.B * w.Hq * w.Sq * w.Skv <= 4 * 16 * 1024 * 1024
-    if small:
-        o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale)
-        check(o, lse, o_ref, lse_ref, w.name)
-        return
-    rows = _sample_rows(w)
-    o_ref, lse_ref = oracle.attn_rows(q, k, v, w.causal, w.scale, rows)
-    b, hq, i = rows[:, 0], rows[:, 1], rows[:, 2]
-    check(o[b, i, hq], lse[b, hq, i], o_ref, lse_ref, w.name)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    o, lse = run_gpu(fa, q, k, v, w.causal, w.scale, split=w in workloads.SPLIT_WORKLOADS)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale)
+    check(o, lse, o_ref, lse_ref, w.name, figures=parity_figures)
 
 
 @pytest.mark.parametrize("w", workloads.WORKLOADS[2:], ids=[w.name for w in workloads.WORKLOADS[2:]])
