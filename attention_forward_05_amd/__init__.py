@@ -19,7 +19,8 @@ import os
 __all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_plan", "fa_strerror", "attention",
            "FAError", "library_path", "load", "FA_OK", "FA_ERR_INVALID",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_DTYPE_BF16",
-           "FA_DTYPE_F16", "FA_KERNEL_FOUR_WAVE", "FA_KERNEL_EIGHT_WAVE", "EXPORTED_SYMBOLS"]
+           "FA_DTYPE_F16", "FA_KERNEL_FOUR_WAVE", "FA_KERNEL_EIGHT_WAVE",
+           "FA_KERNEL_TILE_ROWS", "FA_KERNEL_TILE_KEYS", "EXPORTED_SYMBOLS"]
 
 FA_OK = 0
 FA_ERR_INVALID = -1
@@ -30,6 +31,8 @@ FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_KERNEL_FOUR_WAVE = 0
 FA_KERNEL_EIGHT_WAVE = 1
+FA_KERNEL_TILE_ROWS = 2
+FA_KERNEL_TILE_KEYS = 3
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_plan", "fa_strerror")
 

@@ -1,5 +1,5 @@
-// fa_combine.hip -- merges the per-key-range partial results of the split
-// attention kernel into O and LSE.
+// fa_combine.hip -- merges the per-key-range partial results of split
+// attention kernels into O and LSE.
 //
 // Key range s of a query row left O_s (normalised over its own keys, fp32)
 // and LSE_s (natural log-sum-exp of its scaled logits; -inf when the range
@@ -13,9 +13,9 @@
 // and a row with no visible key at all gets O = 0, LSE = -inf.  O is rounded
 // once to the output dtype (round to nearest even).
 //
-// Half a wave (32 lanes) per query row, four head dimensions per lane
-// (D = 128); the number of ranges is a template parameter so that every
-// range's loads are issued before the first is used.
+// D/4 lanes per query row, four head dimensions per lane; the ranges are
+// visited in groups of eight whose loads are all issued before the first is
+// used.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -28,10 +28,8 @@
 namespace fa {
 namespace {
 
-constexpr int kD = 128;
-constexpr int kLanesPerRow = kD / 4;
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
+constexpr int kGroup = 8;  // ranges whose loads are issued together
 
 __device__ inline void store4(__hip_bfloat16* p, const float (&a)[4]) {
   __hip_bfloat162 lo = __float22bfloat162_rn(make_float2(a[0], a[1]));
@@ -50,10 +48,12 @@ __device__ inline void store4(__half* p, const float (&a)[4]) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
-template <typename T, int NS>
+template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-               T* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Sq) {
+               T* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Sq, int ns) {
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
   const int64_t rows = (int64_t)B * Hq * Sq;
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   if (r >= rows) return;
@@ -64,64 +64,81 @@ combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_
   const int hq = (int)(bh % Hq);
   const int b = (int)(bh / Hq);
 
-  float ls[NS];
-  float4 v[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    ls[s] = part_lse[(int64_t)s * rows + r];
-    v[s] = *reinterpret_cast<const float4*>(part_o + ((int64_t)s * rows + r) * kD + 4 * lane);
-  }
   float m = -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += kGroup) {
+    float ls[kGroup];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) m = fmaxf(m, ls[s]);
+    for (int j = 0; j < kGroup; ++j)
+      ls[j] = (s0 + j < ns) ? part_lse[(int64_t)(s0 + j) * rows + r] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) m = fmaxf(m, ls[j]);
+  }
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float out_lse = -INFINITY;
   if (m != -INFINITY) {
     float wsum = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += kGroup) {
+      float ls[kGroup];
+      float4 v[kGroup];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float w = expf(ls[s] - m);  // 0 for a range without keys
-      wsum += w;
-      acc[0] += w * v[s].x;
-      acc[1] += w * v[s].y;
-      acc[2] += w * v[s].z;
-      acc[3] += w * v[s].w;
+      for (int j = 0; j < kGroup; ++j) {
+        const bool ok = s0 + j < ns;
+        ls[j] = ok ? part_lse[(int64_t)(s0 + j) * rows + r] : -INFINITY;
+        v[j] = ok ? *reinterpret_cast<const float4*>(part_o + ((int64_t)(s0 + j) * rows + r) * D +
+                                                     4 * lane)
+                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const float w = expf(ls[j] - m);  // 0 for a range without keys
+        wsum += w;
+        acc[0] += w * v[j].x;
+        acc[1] += w * v[j].y;
+        acc[2] += w * v[j].z;
+        acc[3] += w * v[j].w;
+      }
     }
     const float inv = 1.0f / wsum;
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] *= inv;
     out_lse = m + logf(wsum);
   }
-  store4(o + (((int64_t)b * Sq + i) * Hq + hq) * kD + 4 * lane, acc);
+  store4(o + (((int64_t)b * Sq + i) * Hq + hq) * D + 4 * lane, acc);
   if (lse != nullptr && lane == 0) lse[r] = out_lse;
+}
+
+template <typename T, int D>
+hipError_t launch_d(const float* part_o, const float* part_lse, T* o, float* lse, int nsplit,
+                    int B, int Hq, int Sq, hipStream_t stream) {
+  constexpr int kRowsPerBlock = kThreads / (D / 4);
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  void* args[] = {&part_o, &part_lse, &o, &lse, &B, &Hq, &Sq, &nsplit};
+  // the launch's own status (an unrelated earlier error is not reported)
+  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel<T, D>), grid,
+                         dim3(kThreads), args, 0, stream);
 }
 
 template <typename T>
 hipError_t launch_t(const float* part_o, const float* part_lse, T* o, float* lse, int nsplit,
-                    int B, int Hq, int Sq, hipStream_t stream) {
-  const int64_t rows = (int64_t)B * Hq * Sq;
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  const dim3 block(kThreads);
-  const void* fn;
-  switch (nsplit) {
-    case 2: fn = reinterpret_cast<const void*>(&combine_kernel<T, 2>); break;
-    case 4: fn = reinterpret_cast<const void*>(&combine_kernel<T, 4>); break;
-    case 8: fn = reinterpret_cast<const void*>(&combine_kernel<T, 8>); break;
-    case 16: fn = reinterpret_cast<const void*>(&combine_kernel<T, 16>); break;
+                    int B, int Hq, int Sq, int D, hipStream_t stream) {
+  if (nsplit < 1) return hipErrorInvalidValue;
+  switch (D) {
+    case 64: return launch_d<T, 64>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
+    case 128: return launch_d<T, 128>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
+    case 256: return launch_d<T, 256>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
     default: return hipErrorInvalidValue;
   }
-  void* args[] = {&part_o, &part_lse, &o, &lse, &B, &Hq, &Sq};
-  // the launch's own status (an unrelated earlier error is not reported)
-  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_combine(DType dtype, const float* part_o, const float* part_lse, void* o, float* lse,
-                          int nsplit, int B, int Hq, int Sq, hipStream_t stream) {
+                          int nsplit, int B, int Hq, int Sq, int D, hipStream_t stream) {
   if (dtype == DType::kBF16)
-    return launch_t(part_o, part_lse, static_cast<__hip_bfloat16*>(o), lse, nsplit, B, Hq, Sq, stream);
-  return launch_t(part_o, part_lse, static_cast<__half*>(o), lse, nsplit, B, Hq, Sq, stream);
+    return launch_t(part_o, part_lse, static_cast<__hip_bfloat16*>(o), lse, nsplit, B, Hq, Sq, D,
+                    stream);
+  return launch_t(part_o, part_lse, static_cast<__half*>(o), lse, nsplit, B, Hq, Sq, D, stream);
 }
 
 }  // namespace fa

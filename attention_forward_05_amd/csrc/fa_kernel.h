@@ -10,13 +10,15 @@ namespace fa {
 enum class DType { kBF16, kF16 };
 
 // Kernel shapes (the values of FA_KERNEL_* in fa.h).
-enum Kernel : int { kFourWave = 0, kEightWave = 1 };
+enum Kernel : int { kFourWave = 0, kEightWave = 1, kTileRows = 2, kTileKeys = 3 };
 
-// The launch plan for one call: kernel shape, key ranges per item and the
-// bytes of partial results the split needs (0 without a split).
+// The launch plan for one call: kernel shape, key ranges per item, whether
+// the q-heads of a kv-head are packed into one block of rows (tile kernels),
+// and the bytes of partial results the split needs (0 without a split).
 struct Plan {
   int kernel;
-  int log2_ranges;
+  int ranges;
+  bool packed;
   size_t ws_bytes;
 };
 
@@ -55,8 +57,8 @@ bool group_magic(int Hq, int Hkv, uint32_t* magic);
 int64_t min_item_tiles(int Sq, int Skv, int causal);
 // log2 of the key ranges each 512-row item is split into (0: no split).
 int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus);
-// Bytes of fp32 partial results (O and LSE) of 2^l2s key ranges.
-size_t split_ws_bytes(int B, int Sq, int Hq, int D, int l2s);
+// Bytes of fp32 partial results (O and LSE) of `ranges` key ranges.
+size_t split_ws_bytes(int B, int Sq, int Hq, int D, int ranges);
 // The plan for these sizes on a device with `cus` compute units; with
 // allow_split false (no workspace) key ranges are never split.
 Plan make_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, int cus,
@@ -67,10 +69,17 @@ Plan make_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, int c
 int launch(const LaunchArgs& a);
 
 // Merge the partial results of `nsplit` key ranges (O fp32
-// [nsplit][B][Hq][Sq][128], LSE fp32 [nsplit][B][Hq][Sq]) into o (BSHD, the
-// input dtype) and lse ([B][Hq][Sq], may be null).
+// [nsplit][B][Hq][Sq][D], LSE fp32 [nsplit][B][Hq][Sq]) into o (BSHD, the
+// input dtype) and lse ([B][Hq][Sq], may be null); D = 64, 128 or 256.
 hipError_t launch_combine(DType dtype, const float* part_o, const float* part_lse, void* o,
-                          float* lse, int nsplit, int B, int Hq, int Sq, hipStream_t stream);
+                          float* lse, int nsplit, int B, int Hq, int Sq, int D,
+                          hipStream_t stream);
+
+// Enqueue a tile kernel (fa_tile.hip): rows or keys split over its four
+// waves, q-heads of a kv-head packed or not, `nsplit` key ranges per item
+// (partial results to part_o / part_lse when nsplit > 1, else to o / lse).
+hipError_t launch_tile(const LaunchArgs& a, bool keys, bool packed, int nsplit, float* part_o,
+                       float* part_lse);
 
 // Argument checks shared by every forward entry point (no HIP call); on
 // FA_OK fills `a` (everything but ws / ws_bytes).

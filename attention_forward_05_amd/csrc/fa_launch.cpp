@@ -160,19 +160,69 @@ int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
 }
 int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
 
-size_t split_ws_bytes(int B, int Sq, int Hq, int D, int l2s) {
-  if (l2s <= 0) return 0;
-  const size_t rows = ((size_t)B * Hq * Sq) << l2s;
+size_t split_ws_bytes(int B, int Sq, int Hq, int D, int ranges) {
+  if (ranges <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * Sq * (size_t)ranges;
   return rows * 4 * (size_t)(D + 1);
 }
 
-Plan make_plan(int B, int Sq, int Skv, int Hq, int /*Hkv*/, int D, int causal, int cus,
+namespace {
+
+// Tile kernels: rows per item and keys per tile.
+int tile_rows(bool keys) { return keys ? 32 : 128; }
+int tile_keys(bool keys, int D) { return keys ? 128 : (D == 256 ? 32 : 64); }
+
+// Key tiles of the tile kernel's shortest item with a visible key (0: none).
+int64_t tile_min_tiles(int Sq, int Skv, int causal, int gp, int rows, int tk) {
+  if (!causal) return (Skv + tk - 1) / tk;
+  const int64_t off = (int64_t)Skv - Sq;
+  const int64_t nrows = (int64_t)Sq * gp;
+  for (int64_t n0 = 0; n0 < nrows; n0 += rows) {
+    const int64_t last_i = (std::min<int64_t>(n0 + rows, nrows) - 1) / gp;
+    const int64_t end = std::min<int64_t>(Skv, last_i + 1 + off);
+    if (end > 0) return (end + tk - 1) / tk;
+  }
+  return 0;
+}
+
+}  // namespace
+
+Plan make_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, int cus,
                bool allow_split) {
   Plan p;
-  p.log2_ranges = allow_split ? split_log2(B, Sq, Skv, Hq, D, causal, cus) : 0;
-  p.ws_bytes = split_ws_bytes(B, Sq, Hq, D, p.log2_ranges);
-  p.kernel = (p.log2_ranges > 0 || use_eight_waves(B, Sq, Skv, Hq, D, causal, cus)) ? kEightWave
-                                                                                    : kFourWave;
+  p.packed = false;
+  const int g = Hq / Hkv;
+  // Decode-shaped calls (a few query rows): the q-heads of a kv-head share
+  // one block of rows, so K and V are read once per kv-head; with at most 32
+  // such rows the four waves split the keys instead of the rows.  Head
+  // dimension 256 has only the tile kernel.
+  const bool decode = D != 256 && Sq <= 64;
+  if (D == 256 || decode) {
+    p.packed = decode;
+    const int gp = decode ? g : 1;
+    const bool keys = decode && (int64_t)Sq * g <= 32;
+    p.kernel = keys ? kTileKeys : kTileRows;
+    const int rows = tile_rows(keys), tk = tile_keys(keys, D);
+    const int64_t heads = decode ? Hkv : Hq;
+    const int64_t items = (int64_t)B * heads * (((int64_t)Sq * gp + rows - 1) / rows);
+    const int64_t n = tile_min_tiles(Sq, Skv, causal, gp, rows, tk);
+    // Split key ranges (with a workspace) until the items cover the compute
+    // units (twice over for the memory-bound key split), keeping at least 4
+    // (keys) or 8 (rows) key tiles per range; at most 64 ranges.
+    const int64_t target = keys ? 2 * (int64_t)cus : cus;
+    const int64_t min_tiles = keys ? 4 : 8;
+    int ns = 1;
+    if (allow_split)
+      while (ns < 64 && items * ns < target && n >= min_tiles * 2 * ns) ns *= 2;
+    p.ranges = ns;
+    p.ws_bytes = split_ws_bytes(B, Sq, Hq, D, ns);
+    return p;
+  }
+  const int l2s = allow_split ? split_log2(B, Sq, Skv, Hq, D, causal, cus) : 0;
+  p.ranges = 1 << l2s;
+  p.ws_bytes = split_ws_bytes(B, Sq, Hq, D, p.ranges);
+  p.kernel = (l2s > 0 || use_eight_waves(B, Sq, Skv, Hq, D, causal, cus)) ? kEightWave
+                                                                          : kFourWave;
   return p;
 }
 
@@ -180,25 +230,35 @@ int launch(const LaunchArgs& a) {
   DeviceKernels* dk = nullptr;
   if (kernels_for_current_device(&dk) != hipSuccess) return FA_ERR_HIP;
   const Plan p = make_plan(a.B, a.Sq, a.Skv, a.Hq, a.Hkv, a.D, a.causal, dk->cus, a.ws != nullptr);
-  hipError_t e;
-  if (p.log2_ranges > 0) {
-    // Split key ranges: the partial results go to the caller's workspace and
-    // the combine kernel merges them into o / lse on the same stream.
-    if (a.ws_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
-    const size_t lse_bytes = p.ws_bytes / (size_t)(a.D + 1);
-    LaunchArgs s = a;
-    s.o = a.ws;
-    s.lse = reinterpret_cast<float*>(static_cast<char*>(a.ws) + lse_bytes * a.D);
-    e = launch_kernel(dk, s, a.dtype == DType::kBF16 ? 6 : 7, true, p.log2_ranges);
-    if (e == hipSuccess)
-      e = launch_combine(a.dtype, static_cast<const float*>(s.o), s.lse, a.o, a.lse,
-                         1 << p.log2_ranges, a.B, a.Hq, a.Sq, a.stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (p.ranges > 1 && a.ws_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+  // Split key ranges: the partial results go to the caller's workspace (O
+  // [ranges][B][Hq][Sq][D], then LSE [ranges][B][Hq][Sq], fp32) and the
+  // combine kernel merges them into o / lse on the same stream.
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (p.ranges > 1) {
+    part_o = static_cast<float*>(a.ws);
+    part_lse = part_o + (size_t)a.B * a.Hq * a.Sq * p.ranges * a.D;
   }
-  const bool x8 = p.kernel == kEightWave;
-  const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
-                         : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
-  e = launch_kernel(dk, a, variant, x8, 0);
+  hipError_t e;
+  if (p.kernel == kTileRows || p.kernel == kTileKeys) {
+    e = launch_tile(a, p.kernel == kTileKeys, p.packed, p.ranges, part_o, part_lse);
+  } else if (p.ranges > 1) {
+    LaunchArgs s = a;
+    s.o = part_o;
+    s.lse = part_lse;
+    int l2s = 0;
+    while ((1 << l2s) < p.ranges) ++l2s;
+    e = launch_kernel(dk, s, a.dtype == DType::kBF16 ? 6 : 7, true, l2s);
+  } else {
+    const bool x8 = p.kernel == kEightWave;
+    const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
+                           : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
+    e = launch_kernel(dk, a, variant, x8, 0);
+  }
+  if (e == hipSuccess && p.ranges > 1)
+    e = launch_combine(a.dtype, part_o, part_lse, a.o, a.lse, p.ranges, a.B, a.Hq, a.Sq, a.D,
+                       a.stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

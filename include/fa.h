@@ -50,7 +50,7 @@ typedef enum {
                               causal not 0/1, scale not finite, pointer not
                               16-byte aligned, o overlapping q/k/v, a workspace
                               overlapping a tensor, size overflow, unknown dtype */
-  FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64 or 128,
+  FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64, 128 or 256,
                               scale < 0, sizes beyond the kernel's limits
                               (ceil(Sq/256) at most 65535, B*Hq*ceil(Sq/256)
                               below 2^24, ceil(Skv/64) below 65536,
@@ -72,7 +72,7 @@ enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F16 = 1 };
  *   o    : device pointer, [B, Sq, Hq, D] bf16, written; must not overlap q, k or v
  *   lse  : device pointer, [B, Hq, Sq] fp32, written; may be NULL (not written)
  *   B, Sq, Skv, Hq, Hkv : sizes >= 1, Hq a multiple of Hkv
- *   D    : head dimension, 64 or 128
+ *   D    : head dimension, 64, 128 or 256
  *   causal : 0 (no mask) or 1 (bottom-right aligned causal mask)
  *   scale  : multiplies the logits before the softmax; finite and >= 0
  *            (usually 1/sqrt(D))
@@ -106,10 +106,10 @@ int fa_fwd_f16(const void* q, const void* k, const void* v, void* o,
  * ranges; dtype is FA_DTYPE_BF16 or FA_DTYPE_F16, the other arguments are
  * those of fa_fwd.
  *
- * When the (batch, q-head, 512-row query tile) items are fewer than the
- * device's compute units and every item's key range is long (D = 128), each
- * item's keys are cut into 2, 4, 8 or 16 ranges: the one-device form of the
- * kernbench GQA prefill page's split of the key sequence over PE groups.
+ * When a call's work items are fewer than the device's compute units and
+ * every item's key range is long, each item's keys are cut into 2, 4, 8, 16,
+ * 32 or 64 ranges: the one-device form of the kernbench GQA prefill page's
+ * split of the key sequence over PE groups.
  * Each range's partial result (fp32 O normalised over the range's keys and
  * the range's LSE, 4*(D+1) bytes per query row and range) goes to the
  * workspace, and a second kernel on the same stream merges them into o and
@@ -133,9 +133,16 @@ int fa_fwd_ws(int dtype, const void* q, const void* k, const void* v, void* o,
 
 /* Kernel shapes reported by fa_fwd_plan. */
 enum {
-  FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD */
-  FA_KERNEL_EIGHT_WAVE = 1  /* 512-row query tiles, two waves per SIMD (D = 128) */
+  FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD (D = 64, 128) */
+  FA_KERNEL_EIGHT_WAVE = 1, /* 512-row query tiles, two waves per SIMD (D = 128) */
+  FA_KERNEL_TILE_ROWS = 2,  /* 128-row blocks, four waves over the rows: D = 256,
+                               and calls with Sq <= 64 whose q-heads of one
+                               kv-head make more than 32 rows together */
+  FA_KERNEL_TILE_KEYS = 3   /* one 32-row block, four waves over the keys: calls
+                               with Sq <= 64 and Sq * Hq / Hkv <= 32 (decode) */
 };
+/* With Sq <= 64 (and D = 64 or 128) the rows of an item are (query, q-head)
+ * pairs of the q-heads of one kv-head, so K and V are read once per kv-head. */
 
 /*
  * fa_fwd_plan -- host-only query (no HIP call): what a forward call of these
@@ -144,14 +151,14 @@ enum {
  * fa_fwd_ws without a workspace), 1 that of fa_fwd_ws with a large enough
  * workspace.
  *
- *   kernel          : written, FA_KERNEL_FOUR_WAVE or FA_KERNEL_EIGHT_WAVE
- *   key_ranges      : written, 1 (whole key ranges) or 2, 4, 8, 16 (split
- *                     key ranges merged by a second kernel)
+ *   kernel          : written, one of FA_KERNEL_*
+ *   key_ranges      : written, 1 (whole key ranges) or 2 .. 64, a power of
+ *                     two (split key ranges merged by a second kernel)
  *   workspace_bytes : written, the workspace the split needs (0 without one)
  *
  * Returns FA_OK, FA_ERR_INVALID (NULL output pointer, size or compute_units
  * < 1, Hq % Hkv != 0, causal or with_workspace not 0/1) or
- * FA_ERR_UNSUPPORTED (D not 64 or 128); the outputs are written only on
+ * FA_ERR_UNSUPPORTED (D not 64, 128 or 256); the outputs are written only on
  * FA_OK.  Size limits of fa_fwd are not checked here.
  */
 int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,

@@ -84,7 +84,7 @@ def test_invalid_arguments(lib, entry, over):
     assert _call(getattr(fa, entry), **over) == fa.FA_ERR_INVALID
 
 
-UNSUPPORTED = [dict(D=96), dict(D=256), dict(D=32), dict(D=16), dict(scale=-0.1),
+UNSUPPORTED = [dict(D=96), dict(D=512), dict(D=32), dict(D=16), dict(scale=-0.1),
                dict(scale=3e38),
                # 2^24 (batch, q-head, query tile) items: beyond the item decoding
                dict(B=16384, Sq=1, Skv=1, Hq=1024, Hkv=1),
@@ -153,6 +153,35 @@ def test_plan_without_workspace_never_splits(lib, B, Sq, Skv, Hq, D, causal, cus
         assert kern == fa.FA_KERNEL_FOUR_WAVE  # split cases have too few 512-row items
 
 
+# The tile kernels (include/fa.h): head dimension 256, and calls with Sq <= 64
+# whose q-heads of one kv-head are packed into rows (keys split over the four
+# waves when those rows number at most 32).  With a workspace, key ranges
+# double while items * ranges stays below the compute units (twice over for
+# the key split) and the shortest item keeps >= 4 (keys) / 8 (rows) tiles of
+# 128 / 64 keys (32 keys at D = 256) per range, at most 64 ranges.
+TILE_PLAN_CASES = [
+    # B, Sq, Skv, Hq, Hkv, D, causal, kernel, ranges
+    # decode, g = 4: 4 rows, 8 items, 128 tiles of 128 keys -> 32 ranges (256 < 512)
+    (1, 1, 16384, 32, 8, 128, 0, 3, 32),
+    # Sq 64, g = 4: 256 packed rows, 2 row blocks x 8 kv-heads = 16 items; the
+    # first block's last query 31 sees 16352 keys = 256 tiles of 64 -> 16 ranges
+    (1, 64, 16384, 32, 8, 128, 1, 2, 16),
+    # D = 256, 8 blocks of 128 rows x 8 heads = 64 items, first block 4 tiles: no split
+    (1, 1000, 1000, 8, 8, 256, 1, 2, 1),
+    # D = 256, 8 items, 256 tiles of 32 keys -> 32 ranges (8 * 32 = 256)
+    (1, 256, 8192, 4, 4, 256, 0, 2, 32),
+    # D = 64 decode, g = 8: 4 items, 32 tiles -> 8 ranges (32 < 4 * 2 * 8)
+    (2, 1, 4096, 16, 2, 64, 1, 3, 8),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,D,causal,kernel,ranges", TILE_PLAN_CASES)
+def test_plan_tile_kernels(lib, B, Sq, Skv, Hq, Hkv, D, causal, kernel, ranges):
+    ws = 0 if ranges == 1 else ranges * B * Hq * Sq * (D + 1) * 4
+    assert fa.fa_fwd_plan(B, Sq, Skv, Hq, Hkv, D, causal, 256, True) == (fa.FA_OK, kernel, ranges, ws)
+    assert fa.fa_fwd_plan(B, Sq, Skv, Hq, Hkv, D, causal, 256, False) == (fa.FA_OK, kernel, 1, 0)
+
+
 def test_plan_items_without_keys(lib):
     # Sq = 600, Skv = 100, causal: rows 0..499 see no key, so the first
     # 512-row tile reaches only keys 0..11 (1 key tile): four waves.
@@ -174,6 +203,7 @@ def test_plan_items_without_keys(lib):
     (dict(causal=2), fa.FA_ERR_INVALID), (dict(cus=0), fa.FA_ERR_INVALID),
     (dict(ws=2), fa.FA_ERR_INVALID), (dict(ws=-1), fa.FA_ERR_INVALID),
     (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(D=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=512), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(lib, over, status):
     a = dict(B=1, Sq=512, Skv=8192, Hq=4, Hkv=2, D=128, causal=0, cus=256, ws=1)

@@ -206,12 +206,34 @@ def test_eight_wave_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype):
     full_case(fa, B, Sq, Skv, Hq, Hkv, 128, causal, dtype, seed=Sq + 3 * Skv + Hkv)
 
 
+def rounding_bound(o, o_ref, v, dtype):
+    """Elementwise bound of the two roundings the kernel does (P and O to the
+    input dtype, unit roundoff u = 2^-8 for bf16, 2^-11 for fp16): P rounded
+    moves O by at most u * sum_j w_j |V_j| <= u * max|V|, and the final
+    rounding by u * |O|.  Returns the largest ratio |dO| / bound (<= 1)."""
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    vmax = float(np.abs(v.double().numpy()).max())
+    bound = u * (np.abs(o_ref) + vmax) * (1 + u) + 1e-5
+    return float((np.abs(o - o_ref) / bound).max())
+
+
 def test_eight_wave_slow_path_bf16(fa):
     """bf16 on the eight-wave kernel with 1% of the key rows scaled by 8: the
-    reference max moves (the slow path) in bf16 as well."""
+    reference max moves (the slow path) in bf16 as well.  The softmax is
+    nearly one-hot here, so |O| reaches |V| (about 4.5) and bf16 rounding of
+    O alone can exceed the 2e-2 bar of the N(0,1) workloads: the bar is the
+    rounding bound instead, with the mean and LSE bars unchanged."""
     if compute_units() == 256:
         assert plan(fa, 1, 256, 1024, 256, 8, 128, True, False)[0] == fa.FA_KERNEL_EIGHT_WAVE
-    full_case(fa, 1, 256, 1024, 256, 8, 128, True, "bf16", seed=24, boost=0.01)
+    B, Sq, Skv, Hq, Hkv, D = 1, 256, 1024, 256, 8, 128
+    q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, D, "bf16", 24, k_row_boost_frac=0.01)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(fa, q, k, v, True, scale)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, True, scale)
+    assert rounding_bound(o, o_ref, v, "bf16") <= 1.0
+    do = np.abs(o - o_ref)
+    assert do.mean() <= MEAN_DO
+    assert np.abs(lse - lse_ref).max() <= MAX_DLSE
 
 
 # ---------------------------------------------------------------------------
@@ -272,6 +294,48 @@ def test_decode_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, parity_figures):
     # and without a workspace: whole key ranges, same bar
     o2, lse2 = run_gpu(fa, q, k, v, causal, scale)
     check(o2, lse2, o_ref, lse_ref, "decode (no workspace)")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Sq,Hq,Hkv,causal", [(1, 16, 2, True), (3, 12, 4, False),
+                                               (20, 8, 1, True), (64, 4, 4, False)])
+def test_decode_tile_kernels(fa, D, Sq, Hq, Hkv, causal):
+    """The packed tile kernels with and without split key ranges: keys over
+    the waves (Sq * Hq / Hkv <= 32) or rows (more), bf16 and fp16."""
+    kern, _, _ = plan(fa, 2, Sq, 5000, Hq, Hkv, D, causal, True)
+    assert kern == (fa.FA_KERNEL_TILE_KEYS if Sq * (Hq // Hkv) <= 32 else fa.FA_KERNEL_TILE_ROWS)
+    for dtype, split in (("bf16", True), ("f16", False)):
+        full_case(fa, 2, Sq, 5000, Hq, Hkv, D, causal, dtype, seed=Sq + Hq + D, split=split)
+
+
+# head dimension 256: the tile kernel, four waves over 128-row blocks
+D256_CASES = [
+    # B, Sq, Skv, Hq, Hkv, causal, dtype, split
+    (1, 128, 128, 1, 1, True, "bf16", False),
+    (2, 300, 300, 4, 2, True, "bf16", False),     # ragged rows and keys, GQA 2
+    (1, 100, 1000, 8, 2, True, "f16", False),     # bottom-right, GQA 4
+    (1, 1000, 100, 2, 1, True, "bf16", False),    # rows with no visible key
+    (2, 513, 777, 3, 3, False, "f16", False),     # ragged, Hq % 8 != 0
+    (1, 256, 8192, 4, 4, False, "bf16", True),    # 32 key ranges merged
+    (1, 200, 6000, 6, 2, True, "f16", True),      # split, bottom-right, GQA 3
+    (1, 40, 3000, 8, 1, True, "bf16", True),      # few rows (not packed at D = 256)
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype,split", D256_CASES)
+def test_head_dim_256(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, split):
+    assert plan(fa, B, Sq, Skv, Hq, Hkv, 256, causal, split)[0] == fa.FA_KERNEL_TILE_ROWS
+    full_case(fa, B, Sq, Skv, Hq, Hkv, 256, causal, dtype, seed=Sq + Skv + 256, split=split)
+
+
+def test_head_dim_256_large_logits(fa):
+    """D = 256 with scale 1 on N(0, 1) inputs (nearly one-hot softmax, the
+    running max moves often), fp16: within the rounding bound."""
+    q, k, v = workloads.make_inputs(1, 200, 700, 2, 1, 256, "f16", 77)
+    o, lse = run_gpu(fa, q, k, v, True, 1.0)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, True, 1.0)
+    assert rounding_bound(o, o_ref, v, "f16") <= 1.0
+    assert np.abs(lse - lse_ref).max() <= MAX_DLSE
 
 
 def test_long_key_range_few_rows(fa):
