@@ -98,6 +98,8 @@ def _configure(lib):
     lib.oracle_merge.argtypes = [_i64, _i64, _dp, _dp, _dp, _dp, _dp, _dp,
                                  _dp, _dp, _dp]
     lib.oracle_merge.restype = None
+    lib.oracle_attn_bwd.argtypes = [_dp] * 7 + [_i64] * 6 + [ctypes.c_int, ctypes.c_double]
+    lib.oracle_attn_bwd.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_threads.restype = None
     lib.oracle_threads.argtypes = []
@@ -147,6 +149,27 @@ def attn_fwd(q, k, v, causal: bool, scale: float):
     if rc != 0:
         raise ValueError(f"oracle_attn_fwd failed ({rc})")
     return o, lse
+
+
+def attn_bwd(q, k, v, dout, causal: bool, scale: float):
+    """Gradients of the forward pass for an upstream gradient dout = dL/dO
+    [B,Sq,Hq,D] -> (dq [B,Sq,Hq,D], dk [B,Skv,Hkv,D], dv [B,Skv,Hkv,D]) in
+    float64.  The textbook softmax gradient with the JAX page's
+    delta = rowsum(O * dO) (see oracle.c, oracle_attn_bwd); dK and dV of a
+    kv-head are summed over its q-heads."""
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Skv, Hq, Hkv, D = _dims(q, k)
+    if v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("v must match k and dout must match q")
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                             B, Sq, Skv, Hq, Hkv, D, int(bool(causal)), float(scale))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd failed ({rc})")
+    return dq, dk, dv
 
 
 def attn_rows(q, k, v, causal: bool, scale: float, rows):

@@ -276,3 +276,148 @@ void oracle_merge(int64_t n, int64_t D, const double* m1, const double* l1,
     m_out[r] = m;
   }
 }
+
+/*
+ * Backward pass: the gradients of a scalar loss L with respect to q, k and v,
+ * given dout = dL/dO, for the same forward definition as oracle_attn_fwd.
+ *
+ * The textbook softmax gradient, following the backward of the JAX Pallas
+ * FlashAttention3 page (`_attention_bwd`: delta = rowsum(O * dO); dP = dO.V^T;
+ * dS = P * (dP - delta); dQ = dS.K; dK = dS^T.Q; dV = P^T.dO, the dK and dV of
+ * a kv-head summed over the q-heads of its group) with the scale applied to
+ * the logits, so that dQ and dK carry one factor of scale:
+ *
+ *   P[i,j]  = exp(s[i,j] - LSE[i])        over the visible keys j of row i
+ *   delta_i = sum_j P[i,j] * (dO_i . V_j)      (= dO_i . O_i)
+ *   dS[i,j] = P[i,j] * (dO_i . V_j - delta_i)
+ *   dQ_i    = scale * sum_j dS[i,j] * K_j
+ *   dK_j    = scale * sum_{q-heads of j's kv-head} sum_i dS[i,j] * Q_i
+ *   dV_j    =         sum_{q-heads of j's kv-head} sum_i P[i,j]  * dO_i
+ *
+ * Three passes, each a plain sum per output element so that no two threads
+ * write one element: (1) per row, LSE and delta from the logits; (2) per
+ * row, dQ; (3) per key row of a kv-head, dK and dV over every (q-head, row)
+ * that sees it.  Rows without a visible key contribute nothing.
+ *
+ * dq [B,Sq,Hq,D]; dk, dv [B,Skv,Hkv,D].  Returns 0, -1 on a bad shape, -2 if
+ * scratch cannot be allocated.
+ */
+int oracle_attn_bwd(const double* q, const double* k, const double* v,
+                    const double* dout, double* dq, double* dk, double* dv,
+                    int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                    int64_t D, int causal, double scale) {
+  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
+  const int64_t group = Hq / Hkv;
+  const int64_t rows = B * Hq * Sq;
+  double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
+  if (!lse || !delta) {
+    free(lse);
+    free(delta);
+    return -2;
+  }
+  int failed = 0;
+
+  /* pass 1: LSE and delta of every row (b, hq, i), row index (b*Hq+hq)*Sq+i */
+#pragma omp parallel num_threads(oracle_threads())
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!s || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / (Hq * Sq);
+        int64_t hq = (r / Sq) % Hq;
+        int64_t i = r % Sq;
+        double m, l;
+        row_partial(q, k, v, b, hq, i, Sq, Skv, Hq, Hkv, D, causal, scale, 0,
+                    Skv, s, &m, &l, acc);
+        const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
+        if (l > 0.0) {
+          lse[r] = m + log(l);
+          double dl = 0.0; /* dO . O, with O = acc / l */
+          for (int64_t d = 0; d < D; ++d) dl += dorow[d] * (acc[d] / l);
+          delta[r] = dl;
+        } else {
+          lse[r] = -INFINITY;
+          delta[r] = 0.0;
+        }
+      }
+    }
+    free(s);
+    free(acc);
+  }
+  if (failed) {
+    free(lse);
+    free(delta);
+    return -2;
+  }
+
+  /* pass 2: dQ of every row */
+#pragma omp parallel for schedule(dynamic, 16) num_threads(oracle_threads())
+  for (int64_t r = 0; r < rows; ++r) {
+    int64_t b = r / (Hq * Sq);
+    int64_t hq = (r / Sq) % Hq;
+    int64_t i = r % Sq;
+    int64_t hk = hq / group;
+    const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
+    const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
+    double* dqrow = dq + ((b * Sq + i) * Hq + hq) * D;
+    for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
+    int64_t end = visible_end(i, Sq, Skv, causal);
+    for (int64_t j = 0; j < end; ++j) {
+      const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
+      const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
+      double dot = 0.0, dp = 0.0;
+      for (int64_t d = 0; d < D; ++d) {
+        dot += qrow[d] * krow[d];
+        dp += dorow[d] * vrow[d];
+      }
+      double p = exp(scale * dot - lse[r]);
+      double ds = p * (dp - delta[r]);
+      for (int64_t d = 0; d < D; ++d) dqrow[d] += scale * ds * krow[d];
+    }
+  }
+
+  /* pass 3: dK and dV of every key row (b, j, hk) */
+  const int64_t krows = B * Skv * Hkv;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(oracle_threads())
+  for (int64_t kr = 0; kr < krows; ++kr) {
+    int64_t b = kr / (Skv * Hkv);
+    int64_t j = (kr / Hkv) % Skv;
+    int64_t hk = kr % Hkv;
+    const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
+    const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
+    double* dkrow = dk + ((b * Skv + j) * Hkv + hk) * D;
+    double* dvrow = dv + ((b * Skv + j) * Hkv + hk) * D;
+    for (int64_t d = 0; d < D; ++d) {
+      dkrow[d] = 0.0;
+      dvrow[d] = 0.0;
+    }
+    for (int64_t hq = hk * group; hq < (hk + 1) * group; ++hq) {
+      for (int64_t i = 0; i < Sq; ++i) {
+        if (j >= visible_end(i, Sq, Skv, causal)) continue;
+        int64_t r = (b * Hq + hq) * Sq + i;
+        const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
+        const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
+        double dot = 0.0, dp = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+          dot += qrow[d] * krow[d];
+          dp += dorow[d] * vrow[d];
+        }
+        double p = exp(scale * dot - lse[r]);
+        double ds = p * (dp - delta[r]);
+        for (int64_t d = 0; d < D; ++d) {
+          dkrow[d] += scale * ds * qrow[d];
+          dvrow[d] += p * dorow[d];
+        }
+      }
+    }
+  }
+  free(lse);
+  free(delta);
+  return 0;
+}
