@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_plan", "fa_strerror", "attention",
+__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_plan", "fa_strerror", "attention",
            "FAError", "library_path", "load", "FA_OK", "FA_ERR_INVALID",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_DTYPE_BF16",
            "FA_DTYPE_F16", "FA_KERNEL_FOUR_WAVE", "FA_KERNEL_EIGHT_WAVE",
@@ -34,7 +34,10 @@ FA_KERNEL_EIGHT_WAVE = 1
 FA_KERNEL_TILE_ROWS = 2
 FA_KERNEL_TILE_KEYS = 3
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_plan", "fa_strerror")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_plan",
+                    "fa_strerror")
+# bytes of the scratch buffer fa_fwd_noalloc keeps on each device
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -70,6 +73,8 @@ def load():
     lib.fa_fwd_ws.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ctypes.c_float, vp,
                               sz, vp]
     lib.fa_fwd_ws.restype = i
+    lib.fa_fwd_noalloc.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ctypes.c_float, vp]
+    lib.fa_fwd_noalloc.restype = i
     ip = ctypes.POINTER(i)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, i, ip, ip, ctypes.POINTER(sz)]
     lib.fa_fwd_plan.restype = i
@@ -147,6 +152,17 @@ def fa_fwd_ws(dtype, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale, wor
                           float(scale), _addr(workspace), int(workspace_bytes),
                           _stream(stream) if stream != 0 else None)
     return st
+
+
+def fa_fwd_noalloc(dtype, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale,
+                   stream=None) -> int:
+    """Forward with the library's fixed per-device scratch buffer in place of
+    a workspace, for callers that cannot allocate (see include/fa.h).
+    Returns the status code."""
+    return load().fa_fwd_noalloc(int(dtype), _addr(q), _addr(k), _addr(v), _addr(o), _addr(lse),
+                                 int(B), int(Sq), int(Skv), int(Hq), int(Hkv), int(D),
+                                 int(causal), float(scale),
+                                 _stream(stream) if stream != 0 else None)
 
 
 def attention(q, k, v, causal: bool, scale: float, with_lse: bool = True, out=None,

@@ -196,7 +196,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_HIP:
       return "HIP runtime error at kernel launch";
     case FA_ERR_WORKSPACE:
-      return "workspace too small for the split key ranges of this call (fa_fwd_plan gives the size)";
+      return "workspace too small for the split key ranges of this call: fa_fwd_ws's workspace, or "
+             "fa_fwd_noalloc's fixed 64 MiB scratch buffer (fa_fwd_plan gives the bytes needed)";
     default:
       return "unknown fa_status";
   }

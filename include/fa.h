@@ -58,7 +58,8 @@ typedef enum {
   FA_ERR_HIP = -3,         /* the HIP runtime reported an error loading the
                               kernels or at launch */
   FA_ERR_WORKSPACE = -4    /* the call splits its key ranges and the workspace
-                              given is smaller than fa_fwd_plan reports */
+                              given (or fa_fwd_noalloc's scratch buffer) is
+                              smaller than fa_fwd_plan reports */
 } fa_status;
 
 /* Element types of q, k, v and o for the entry points that take a dtype. */
@@ -130,6 +131,35 @@ int fa_fwd_ws(int dtype, const void* q, const void* k, const void* v, void* o,
               float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
               int causal, float scale, void* workspace, size_t workspace_bytes,
               hipStream_t stream);
+
+/* Bytes of the scratch buffer fa_fwd_noalloc keeps on each device (64 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * fa_fwd_noalloc -- for callers that cannot allocate device memory around
+ * the call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the forward pass of fa_fwd_ws, with the library's own
+ * scratch buffer of FA_NOALLOC_SCRATCH_BYTES in place of a caller workspace.
+ * dtype and the other arguments are those of fa_fwd_ws.
+ *
+ * The buffer is a device array of the library, one per device, held from the
+ * load of the library's device code until the process ends.  The call
+ * allocates nothing.  The first call of any entry point on a device loads the
+ * library's kernel code there (the HIP runtime allocates for that), so make
+ * one call on each device before code that must not allocate.
+ *
+ * Calls that split their key ranges use the buffer for the partial results
+ * and return FA_ERR_WORKSPACE, before enqueueing anything, when the split
+ * needs more than FA_NOALLOC_SCRATCH_BYTES (fa_fwd_plan with
+ * with_workspace = 1 reports the bytes).  All calls on one device share its
+ * buffer, whose contents persist from call to call: two split calls whose
+ * kernels overlap on one device (different streams, no ordering between
+ * them) race on it and give undefined results.  Calls on one stream are
+ * ordered and safe.
+ */
+int fa_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
+                   int causal, float scale, hipStream_t stream);
 
 /* Kernel shapes reported by fa_fwd_plan. */
 enum {

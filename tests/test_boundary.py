@@ -240,6 +240,24 @@ def test_ws_unsupported_arguments(lib, over):
     assert _call_ws(**over) == fa.FA_ERR_UNSUPPORTED
 
 
+def _call_noalloc(dtype=0, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.fa_fwd_noalloc(dtype, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Sq"],
+                             a["Skv"], a["Hq"], a["Hkv"], a["D"], a["causal"], a["scale"], 0)
+
+
+@pytest.mark.parametrize("over", INVALID + [dict(dtype=2), dict(dtype=-1)],
+                         ids=[str(x) for x in INVALID + [dict(dtype=2), dict(dtype=-1)]])
+def test_noalloc_invalid_arguments(lib, over):
+    assert _call_noalloc(**over) == fa.FA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over", UNSUPPORTED, ids=[str(x) for x in UNSUPPORTED])
+def test_noalloc_unsupported_arguments(lib, over):
+    assert _call_noalloc(**over) == fa.FA_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("args", [
     dict(dtype=2), dict(dtype=-1),                     # unknown dtype
     dict(ws=WS + 8), dict(ws=WS + 1),                  # workspace not 16-byte aligned
