@@ -16,7 +16,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_plan", "fa_strerror", "attention",
+__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_plan", "fa_bwd",
+           "attention_bwd", "fa_strerror", "attention",
            "FAError", "library_path", "load", "FA_OK", "FA_ERR_INVALID",
            "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_DTYPE_BF16",
            "FA_DTYPE_F16", "FA_KERNEL_FOUR_WAVE", "FA_KERNEL_EIGHT_WAVE",
@@ -35,7 +36,7 @@ FA_KERNEL_TILE_ROWS = 2
 FA_KERNEL_TILE_KEYS = 3
 
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f16", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_plan",
-                    "fa_strerror")
+                    "fa_bwd", "fa_strerror")
 # bytes of the scratch buffer fa_fwd_noalloc keeps on each device
 FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -75,6 +76,8 @@ def load():
     lib.fa_fwd_ws.restype = i
     lib.fa_fwd_noalloc.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, ctypes.c_float, vp]
     lib.fa_fwd_noalloc.restype = i
+    lib.fa_bwd.argtypes = [i] + [vp] * 9 + [i] * 7 + [ctypes.c_float, vp, sz, vp]
+    lib.fa_bwd.restype = i
     ip = ctypes.POINTER(i)
     lib.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, i, ip, ip, ctypes.POINTER(sz)]
     lib.fa_fwd_plan.restype = i
@@ -163,6 +166,43 @@ def fa_fwd_noalloc(dtype, q, k, v, o, lse, B, Sq, Skv, Hq, Hkv, D, causal, scale
                                  int(B), int(Sq), int(Skv), int(Hq), int(Hkv), int(D),
                                  int(causal), float(scale),
                                  _stream(stream) if stream != 0 else None)
+
+
+def fa_bwd(dtype, q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Skv, Hq, Hkv, D, causal, scale,
+           workspace, workspace_bytes, stream=None) -> int:
+    """Backward pass (see include/fa.h).  Returns the status code."""
+    return load().fa_bwd(int(dtype), _addr(q), _addr(k), _addr(v), _addr(o), _addr(lse),
+                         _addr(dout), _addr(dq), _addr(dk), _addr(dv), int(B), int(Sq), int(Skv),
+                         int(Hq), int(Hkv), int(D), int(causal), float(scale), _addr(workspace),
+                         int(workspace_bytes), _stream(stream) if stream != 0 else None)
+
+
+def attention_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, stream=None):
+    """Convenience wrapper: gradients (dq, dk, dv) of the forward on torch
+    tensors (q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o and dout like q, lse
+    [B,Hq,Sq] fp32 from the forward), allocated with torch together with the
+    4*B*Hq*Sq-byte workspace.  Raises FAError on a non-zero status."""
+    import torch
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if q.dtype == torch.bfloat16:
+        dt = FA_DTYPE_BF16
+    elif q.dtype == torch.float16:
+        dt = FA_DTYPE_F16
+    else:
+        raise FAError(FA_ERR_UNSUPPORTED, f"attention_bwd: dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise FAError(FA_ERR_INVALID, f"attention_bwd: {name} must be a contiguous GPU tensor")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(4 * B * Hq * Sq, 16), dtype=torch.uint8, device=q.device)
+    if isinstance(stream, torch.cuda.Stream):
+        ws.record_stream(stream)
+    st = fa_bwd(dt, q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Skv, Hq, Hkv, D, int(bool(causal)),
+                scale, ws, ws.numel(), stream)
+    if st != FA_OK:
+        raise FAError(st, "attention_bwd")
+    return dq, dk, dv
 
 
 def attention(q, k, v, causal: bool, scale: float, with_lse: bool = True, out=None,

@@ -142,9 +142,79 @@ int fwd(fa::DType dtype, const void* q, const void* k, const void* v, void* o, f
   return fa::launch(a);
 }
 
+int bwd(fa::DType dtype, const void* q, const void* k, const void* v, const void* o,
+        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int Sq, int Skv,
+        int Hq, int Hkv, int D, int causal, float scale, void* ws, size_t ws_bytes,
+        hipStream_t stream) {
+  // the shape, scale and size checks of the forward pass, on q/k/v with dq
+  // as its output (dq must not overlap q, k or v)
+  fa::LaunchArgs a;
+  int st = fa::check_fwd_args(dtype, q, k, v, dq, nullptr, B, Sq, Skv, Hq, Hkv, D, causal, scale,
+                              stream, &a);
+  if (st != FA_OK) return st;
+  if (!o || !lse || !dout || !dk || !dv) return FA_ERR_INVALID;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return FA_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return FA_ERR_INVALID;
+  uint64_t qb, kvb, lseb;
+  tensor_bytes(a, &qb, &kvb, &lseb);
+  // outputs (dq, dk, dv) overlap neither each other nor any input
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const uint64_t in_bytes[6] = {qb, kvb, kvb, qb, lseb, qb};
+  void* outs[3] = {dq, dk, dv};
+  const uint64_t out_bytes[3] = {qb, kvb, kvb};
+  for (int x = 0; x < 3; ++x) {
+    for (int y = 0; y < 6; ++y)
+      if (overlap(outs[x], out_bytes[x], ins[y], in_bytes[y])) return FA_ERR_INVALID;
+    for (int y = x + 1; y < 3; ++y)
+      if (overlap(outs[x], out_bytes[x], outs[y], out_bytes[y])) return FA_ERR_INVALID;
+  }
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  // the workspace holds delta, one fp32 per query row: [B][Hq][Sq]
+  if (!ws || ws_bytes < lseb) return FA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return FA_ERR_INVALID;
+  for (int y = 0; y < 6; ++y)
+    if (overlap(ws, lseb, ins[y], in_bytes[y])) return FA_ERR_INVALID;
+  for (int x = 0; x < 3; ++x)
+    if (overlap(ws, lseb, outs[x], out_bytes[x])) return FA_ERR_INVALID;
+
+  fa::BwdLaunchArgs b;
+  b.dtype = dtype;
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.o = o;
+  b.lse = lse;
+  b.dout = dout;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.delta = static_cast<float*>(ws);
+  b.B = B;
+  b.Sq = Sq;
+  b.Skv = Skv;
+  b.Hq = Hq;
+  b.Hkv = Hkv;
+  b.D = D;
+  b.causal = causal;
+  b.scale = scale;
+  b.c = a.c;
+  b.stream = stream;
+  return fa::launch_bwd(b) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int Sq,
+           int Skv, int Hq, int Hkv, int D, int causal, float scale, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_INVALID;
+  return bwd(dtype == FA_DTYPE_BF16 ? fa::DType::kBF16 : fa::DType::kF16, q, k, v, o, lse, dout,
+             dq, dk, dv, B, Sq, Skv, Hq, Hkv, D, causal, scale, workspace, workspace_bytes,
+             stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
            int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,

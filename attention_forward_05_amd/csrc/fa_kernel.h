@@ -81,6 +81,27 @@ hipError_t launch_combine(DType dtype, const float* part_o, const float* part_ls
 hipError_t launch_tile(const LaunchArgs& a, bool keys, bool packed, int nsplit, float* part_o,
                        float* part_lse);
 
+// The backward pass (fa_bwd.hip).
+struct BwdLaunchArgs {
+  DType dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: [B][Hq][Sq] fp32
+  int B, Sq, Skv, Hq, Hkv, D, causal;
+  float scale;
+  float c;  // scale * log2(e), clamped to >= FLT_MIN
+  hipStream_t stream;
+};
+// Enqueue the three backward kernels (delta, dK/dV, dQ) on a.stream.
+hipError_t launch_bwd(const BwdLaunchArgs& a);
+
 // Argument checks shared by every forward entry point (no HIP call); on
 // FA_OK fills `a` (everything but ws / ws_bytes).
 int check_fwd_args(DType dtype, const void* q, const void* k, const void* v, void* o, float* lse,

@@ -44,61 +44,12 @@
 #include <stdint.h>
 
 #include "fa_kernel.h"
+#include "fa_mfma.h"
 
 namespace fa {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-
-struct BF16 {
-  static __device__ __forceinline__ f32x16 mma(s16x8 a, s16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  // round to nearest even
-  static __device__ __forceinline__ short cvt(float x) {
-    return __builtin_bit_cast(short, static_cast<__bf16>(x));
-  }
-};
-
-struct F16 {
-  static __device__ __forceinline__ f32x16 mma(s16x8 a, s16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ short cvt(float x) {
-    return __builtin_bit_cast(short, static_cast<_Float16>(x));
-  }
-};
-
-// 16-byte chunk swizzle of an LDS tile with rows of D 16-bit elements.
-// Row reads (16 consecutive rows at one chunk) and transposing reads (4
-// consecutive rows x 4 consecutive chunks per 16 lanes) both hit distinct
-// banks.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 64) return ((r >> 1) & 7) ^ (((r >> 1) & 1) << 2);
-  else return (r & 15) ^ ((r & 3) << 2);
-}
-template <int D>
-__device__ __forceinline__ int lds_off(int r, int chunk) {
-  return r * (2 * D) + ((chunk ^ swz<D>(r)) << 4);
-}
-
-// ds_read_b64_tr_b16 on a generic pointer into LDS
-__device__ __forceinline__ s16x4 read_tr(const char* p) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
+using namespace mfma;
 
 __device__ __forceinline__ float wave_max32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 

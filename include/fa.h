@@ -161,6 +161,45 @@ int fa_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, void*
                    float* lse, int B, int Sq, int Skv, int Hq, int Hkv, int D,
                    int causal, float scale, hipStream_t stream);
 
+/*
+ * fa_bwd -- the backward pass: the gradients dQ, dK, dV of a scalar loss
+ * given its gradient dO with respect to the forward output, for the
+ * forward these arguments describe.  It follows the JAX Pallas
+ * FlashAttention3 page's backward (`_attention_bwd`: delta = rowsum(O * dO);
+ * `kernel_dq`: P = exp(scale*q.k - LSE), dP = dO.V^T, dS = P * (dP - delta),
+ * dQ = scale * dS.K; `kernel_dkv`: dK = scale * dS^T.Q, dV = P^T.dO, dK and
+ * dV of a kv-head summed over the q-heads of its group), with this
+ * library's scale and natural-log LSE.  P and dS are rounded to the input
+ * dtype before the products that read them, as that page casts them; the
+ * gradients are accumulated in fp32 and rounded once.  With causal = 1 the
+ * forward's bottom-right mask applies (masked pairs have P = 0); that page
+ * has no causal backward.
+ *
+ *   dtype       : FA_DTYPE_BF16 or FA_DTYPE_F16 (q, k, v, o, dout, dq, dk, dv)
+ *   q, k, v     : the forward's inputs (layouts as in fa_fwd)
+ *   o, lse      : the forward's outputs, o [B,Sq,Hq,D], lse [B,Hq,Sq] fp32
+ *                 (natural log, as fa_fwd writes it; -inf for rows without a
+ *                 visible key, which then get dQ = 0)
+ *   dout        : dL/dO, [B,Sq,Hq,D]
+ *   dq          : written, [B,Sq,Hq,D]
+ *   dk, dv      : written, [B,Skv,Hkv,D]
+ *   B .. scale  : as in fa_fwd; D = 64 or 128
+ *   workspace   : device memory of at least 4*B*Hq*Sq bytes, 16-byte aligned
+ *                 (one fp32 delta per query row); contents undefined after
+ *   stream      : HIP stream to enqueue on
+ *
+ * dq, dk, dv and the workspace must overlap neither each other nor any
+ * input.  Asynchronous like fa_fwd; the library allocates nothing.  Returns
+ * FA_OK, FA_ERR_INVALID (as fa_fwd, plus NULL o/lse/dout/dk/dv and the
+ * overlaps above), FA_ERR_UNSUPPORTED (D not 64 or 128, and fa_fwd's
+ * limits), FA_ERR_WORKSPACE (workspace NULL or smaller than 4*B*Hq*Sq
+ * bytes) or FA_ERR_HIP.
+ */
+int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+           int Sq, int Skv, int Hq, int Hkv, int D, int causal, float scale,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Kernel shapes reported by fa_fwd_plan. */
 enum {
   FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD (D = 64, 128) */

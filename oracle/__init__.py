@@ -100,6 +100,9 @@ def _configure(lib):
     lib.oracle_merge.restype = None
     lib.oracle_attn_bwd.argtypes = [_dp] * 7 + [_i64] * 6 + [ctypes.c_int, ctypes.c_double]
     lib.oracle_attn_bwd.restype = ctypes.c_int
+    lib.oracle_attn_bwd_rows.argtypes = [_dp] * 4 + [_i64] * 6 + [ctypes.c_int, ctypes.c_double,
+                                          _lp, _i64, _dp, _lp, _i64, _dp, _dp]
+    lib.oracle_attn_bwd_rows.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_threads.restype = None
     lib.oracle_threads.argtypes = []
@@ -169,6 +172,28 @@ def attn_bwd(q, k, v, dout, causal: bool, scale: float):
                              B, Sq, Skv, Hq, Hkv, D, int(bool(causal)), float(scale))
     if rc != 0:
         raise ValueError(f"oracle_attn_bwd failed ({rc})")
+    return dq, dk, dv
+
+
+def attn_bwd_rows(q, k, v, dout, causal: bool, scale: float, qrows, krows):
+    """Selected gradients: dQ of the query rows qrows (int [nq, 3] of
+    (b, hq, i)) and dK, dV of the key rows krows (int [nk, 3] of (b, hk, j))
+    -> (dq [nq, D], dk [nk, D], dv [nk, D]) in float64, the same arithmetic
+    as attn_bwd."""
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Skv, Hq, Hkv, D = _dims(q, k)
+    qrows = np.ascontiguousarray(np.asarray(qrows, dtype=np.int64).reshape(-1, 3))
+    krows = np.ascontiguousarray(np.asarray(krows, dtype=np.int64).reshape(-1, 3))
+    nq, nk = qrows.shape[0], krows.shape[0]
+    dq = np.empty((nq, D), np.float64)
+    dk = np.empty((nk, D), np.float64)
+    dv = np.empty((nk, D), np.float64)
+    rc = lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, Sq, Skv, Hq, Hkv, D,
+                                  int(bool(causal)), float(scale), qrows.ctypes.data_as(_lp), nq,
+                                  _ptr(dq), krows.ctypes.data_as(_lp), nk, _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd_rows failed ({rc})")
     return dq, dk, dv
 
 

@@ -294,31 +294,19 @@ void oracle_merge(int64_t n, int64_t D, const double* m1, const double* l1,
  *   dK_j    = scale * sum_{q-heads of j's kv-head} sum_i dS[i,j] * Q_i
  *   dV_j    =         sum_{q-heads of j's kv-head} sum_i P[i,j]  * dO_i
  *
- * Three passes, each a plain sum per output element so that no two threads
+ * Three steps, each a plain sum per output element so that no two threads
  * write one element: (1) per row, LSE and delta from the logits; (2) per
  * row, dQ; (3) per key row of a kv-head, dK and dV over every (q-head, row)
  * that sees it.  Rows without a visible key contribute nothing.
- *
- * dq [B,Sq,Hq,D]; dk, dv [B,Skv,Hkv,D].  Returns 0, -1 on a bad shape, -2 if
- * scratch cannot be allocated.
  */
-int oracle_attn_bwd(const double* q, const double* k, const double* v,
-                    const double* dout, double* dq, double* dk, double* dv,
-                    int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
-                    int64_t D, int causal, double scale) {
-  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
-  const int64_t group = Hq / Hkv;
-  const int64_t rows = B * Hq * Sq;
-  double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
-  double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
-  if (!lse || !delta) {
-    free(lse);
-    free(delta);
-    return -2;
-  }
-  int failed = 0;
 
-  /* pass 1: LSE and delta of every row (b, hq, i), row index (b*Hq+hq)*Sq+i */
+/* Step 1 for every row (b, hq, i), row index (b*Hq+hq)*Sq+i.  0 or -2. */
+static int bwd_lse_delta(const double* q, const double* k, const double* v,
+                         const double* dout, int64_t B, int64_t Sq, int64_t Skv,
+                         int64_t Hq, int64_t Hkv, int64_t D, int causal,
+                         double scale, double* lse, double* delta) {
+  const int64_t rows = B * Hq * Sq;
+  int failed = 0;
 #pragma omp parallel num_threads(oracle_threads())
   {
     double* s = (double*)malloc(sizeof(double) * (size_t)Skv);
@@ -350,27 +338,56 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v,
     free(s);
     free(acc);
   }
-  if (failed) {
-    free(lse);
-    free(delta);
-    return -2;
-  }
+  return failed ? -2 : 0;
+}
 
-  /* pass 2: dQ of every row */
-#pragma omp parallel for schedule(dynamic, 16) num_threads(oracle_threads())
-  for (int64_t r = 0; r < rows; ++r) {
-    int64_t b = r / (Hq * Sq);
-    int64_t hq = (r / Sq) % Hq;
-    int64_t i = r % Sq;
-    int64_t hk = hq / group;
-    const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
-    const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
-    double* dqrow = dq + ((b * Sq + i) * Hq + hq) * D;
-    for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
-    int64_t end = visible_end(i, Sq, Skv, causal);
-    for (int64_t j = 0; j < end; ++j) {
-      const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
-      const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
+/* Step 2: dQ of row (b, hq, i) into dqrow[D]. */
+static void bwd_dq_row(const double* q, const double* k, const double* v,
+                       const double* dout, const double* lse,
+                       const double* delta, int64_t b, int64_t hq, int64_t i,
+                       int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                       int64_t D, int causal, double scale, double* dqrow) {
+  const int64_t group = Hq / Hkv;
+  const int64_t hk = hq / group;
+  const int64_t r = (b * Hq + hq) * Sq + i;
+  const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
+  const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
+  for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
+  int64_t end = visible_end(i, Sq, Skv, causal);
+  for (int64_t j = 0; j < end; ++j) {
+    const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
+    const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
+    double dot = 0.0, dp = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+      dot += qrow[d] * krow[d];
+      dp += dorow[d] * vrow[d];
+    }
+    double p = exp(scale * dot - lse[r]);
+    double ds = p * (dp - delta[r]);
+    for (int64_t d = 0; d < D; ++d) dqrow[d] += scale * ds * krow[d];
+  }
+}
+
+/* Step 3: dK and dV of key row (b, j, hk) into dkrow[D], dvrow[D]. */
+static void bwd_dkdv_key(const double* q, const double* k, const double* v,
+                         const double* dout, const double* lse,
+                         const double* delta, int64_t b, int64_t hk, int64_t j,
+                         int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                         int64_t D, int causal, double scale, double* dkrow,
+                         double* dvrow) {
+  const int64_t group = Hq / Hkv;
+  const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
+  const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
+  for (int64_t d = 0; d < D; ++d) {
+    dkrow[d] = 0.0;
+    dvrow[d] = 0.0;
+  }
+  for (int64_t hq = hk * group; hq < (hk + 1) * group; ++hq) {
+    for (int64_t i = 0; i < Sq; ++i) {
+      if (j >= visible_end(i, Sq, Skv, causal)) continue;
+      int64_t r = (b * Hq + hq) * Sq + i;
+      const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
+      const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
       double dot = 0.0, dp = 0.0;
       for (int64_t d = 0; d < D; ++d) {
         dot += qrow[d] * krow[d];
@@ -378,46 +395,93 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v,
       }
       double p = exp(scale * dot - lse[r]);
       double ds = p * (dp - delta[r]);
-      for (int64_t d = 0; d < D; ++d) dqrow[d] += scale * ds * krow[d];
+      for (int64_t d = 0; d < D; ++d) {
+        dkrow[d] += scale * ds * qrow[d];
+        dvrow[d] += p * dorow[d];
+      }
     }
   }
+}
 
-  /* pass 3: dK and dV of every key row (b, j, hk) */
-  const int64_t krows = B * Skv * Hkv;
+/*
+ * Every gradient: dq [B,Sq,Hq,D]; dk, dv [B,Skv,Hkv,D].  Returns 0, -1 on a
+ * bad shape, -2 if scratch cannot be allocated.
+ */
+int oracle_attn_bwd(const double* q, const double* k, const double* v,
+                    const double* dout, double* dq, double* dk, double* dv,
+                    int64_t B, int64_t Sq, int64_t Skv, int64_t Hq, int64_t Hkv,
+                    int64_t D, int causal, double scale) {
+  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
+  const int64_t rows = B * Hq * Sq;
+  double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
+  int rc = (!lse || !delta) ? -2
+                            : bwd_lse_delta(q, k, v, dout, B, Sq, Skv, Hq, Hkv,
+                                            D, causal, scale, lse, delta);
+  if (rc == 0) {
 #pragma omp parallel for schedule(dynamic, 16) num_threads(oracle_threads())
-  for (int64_t kr = 0; kr < krows; ++kr) {
-    int64_t b = kr / (Skv * Hkv);
-    int64_t j = (kr / Hkv) % Skv;
-    int64_t hk = kr % Hkv;
-    const double* krow = k + ((b * Skv + j) * Hkv + hk) * D;
-    const double* vrow = v + ((b * Skv + j) * Hkv + hk) * D;
-    double* dkrow = dk + ((b * Skv + j) * Hkv + hk) * D;
-    double* dvrow = dv + ((b * Skv + j) * Hkv + hk) * D;
-    for (int64_t d = 0; d < D; ++d) {
-      dkrow[d] = 0.0;
-      dvrow[d] = 0.0;
+    for (int64_t r = 0; r < rows; ++r) {
+      int64_t b = r / (Hq * Sq), hq = (r / Sq) % Hq, i = r % Sq;
+      bwd_dq_row(q, k, v, dout, lse, delta, b, hq, i, Sq, Skv, Hq, Hkv, D,
+                 causal, scale, dq + ((b * Sq + i) * Hq + hq) * D);
     }
-    for (int64_t hq = hk * group; hq < (hk + 1) * group; ++hq) {
-      for (int64_t i = 0; i < Sq; ++i) {
-        if (j >= visible_end(i, Sq, Skv, causal)) continue;
-        int64_t r = (b * Hq + hq) * Sq + i;
-        const double* qrow = q + ((b * Sq + i) * Hq + hq) * D;
-        const double* dorow = dout + ((b * Sq + i) * Hq + hq) * D;
-        double dot = 0.0, dp = 0.0;
-        for (int64_t d = 0; d < D; ++d) {
-          dot += qrow[d] * krow[d];
-          dp += dorow[d] * vrow[d];
-        }
-        double p = exp(scale * dot - lse[r]);
-        double ds = p * (dp - delta[r]);
-        for (int64_t d = 0; d < D; ++d) {
-          dkrow[d] += scale * ds * qrow[d];
-          dvrow[d] += p * dorow[d];
-        }
-      }
+    const int64_t krows = B * Skv * Hkv;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(oracle_threads())
+    for (int64_t kr = 0; kr < krows; ++kr) {
+      int64_t b = kr / (Skv * Hkv), j = (kr / Hkv) % Skv, hk = kr % Hkv;
+      bwd_dkdv_key(q, k, v, dout, lse, delta, b, hk, j, Sq, Skv, Hq, Hkv, D,
+                   causal, scale, dk + ((b * Skv + j) * Hkv + hk) * D,
+                   dv + ((b * Skv + j) * Hkv + hk) * D);
     }
   }
   free(lse);
   free(delta);
-  return 0;
+  return rc;
+}
+
+/*
+ * Selected gradients, for checks at sizes where every gradient is too slow:
+ * dQ of the nq query rows qrows (triples b, hq, i) into dq_rows [nq, D], and
+ * dK, dV of the nk key rows krows (triples b, hk, j) into dk_rows, dv_rows
+ * [nk, D].  Step 1 still runs over every row.  Returns 0, -1 on a bad shape
+ * or index, -2 if scratch cannot be allocated.
+ */
+int oracle_attn_bwd_rows(const double* q, const double* k, const double* v,
+                         const double* dout, int64_t B, int64_t Sq, int64_t Skv,
+                         int64_t Hq, int64_t Hkv, int64_t D, int causal,
+                         double scale, const int64_t* qrows, int64_t nq,
+                         double* dq_rows, const int64_t* krows, int64_t nk,
+                         double* dk_rows, double* dv_rows) {
+  if (check_shape(B, Sq, Skv, Hq, Hkv, D)) return -1;
+  for (int64_t n = 0; n < nq; ++n) {
+    const int64_t* t = qrows + 3 * n;
+    if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= Hq || t[2] < 0 || t[2] >= Sq) return -1;
+  }
+  for (int64_t n = 0; n < nk; ++n) {
+    const int64_t* t = krows + 3 * n;
+    if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= Hkv || t[2] < 0 || t[2] >= Skv) return -1;
+  }
+  const int64_t rows = B * Hq * Sq;
+  double* lse = (double*)malloc(sizeof(double) * (size_t)rows);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)rows);
+  int rc = (!lse || !delta) ? -2
+                            : bwd_lse_delta(q, k, v, dout, B, Sq, Skv, Hq, Hkv,
+                                            D, causal, scale, lse, delta);
+  if (rc == 0) {
+#pragma omp parallel for schedule(dynamic, 4) num_threads(oracle_threads())
+    for (int64_t n = 0; n < nq; ++n) {
+      const int64_t* t = qrows + 3 * n;
+      bwd_dq_row(q, k, v, dout, lse, delta, t[0], t[1], t[2], Sq, Skv, Hq, Hkv,
+                 D, causal, scale, dq_rows + n * D);
+    }
+#pragma omp parallel for schedule(dynamic, 4) num_threads(oracle_threads())
+    for (int64_t n = 0; n < nk; ++n) {
+      const int64_t* t = krows + 3 * n;
+      bwd_dkdv_key(q, k, v, dout, lse, delta, t[0], t[1], t[2], Sq, Skv, Hq,
+                   Hkv, D, causal, scale, dk_rows + n * D, dv_rows + n * D);
+    }
+  }
+  free(lse);
+  free(delta);
+  return rc;
 }

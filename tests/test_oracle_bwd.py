@@ -176,3 +176,18 @@ def test_against_torch_autograd_float64(B, Sq, Skv, Hq, Hkv, D, causal, scale):
     np.testing.assert_allclose(dq, rq, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(dk, rk, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(dv, rv, rtol=1e-10, atol=1e-12)
+
+
+def test_rows_equal_full():
+    """The selected-rows entry gives the same numbers as the full backward."""
+    B, Sq, Skv, Hq, Hkv, D = 2, 11, 17, 4, 2, 16
+    q, k, v, do = _inputs(B, Sq, Skv, Hq, Hkv, D, seed=8)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, True, 0.3)
+    qrows = np.array([[0, 0, 0], [1, 3, 10], [0, 2, 5]])
+    krows = np.array([[0, 0, 0], [1, 1, 16], [1, 0, 7]])
+    dq_r, dk_r, dv_r = oracle.attn_bwd_rows(q, k, v, do, True, 0.3, qrows, krows)
+    for n, (b, hq, i) in enumerate(qrows):
+        np.testing.assert_array_equal(dq_r[n], dq[b, i, hq])
+    for n, (b, hk, j) in enumerate(krows):
+        np.testing.assert_array_equal(dk_r[n], dk[b, j, hk])
+        np.testing.assert_array_equal(dv_r[n], dv[b, j, hk])

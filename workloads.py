@@ -69,7 +69,22 @@ SPLIT_WORKLOADS = [
     Workload("causal_gqa_shortprefill_b1_hq32_hkv8_sq512_skv16384_d128_bf16",
              1, 32, 8, 512, 16384, 128, True, "bf16", 48),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS + SPLIT_WORKLOADS}
+# Decode-shaped calls: one query row per sequence over a long key range, the
+# q-heads of each kv-head packed into one block of rows (memory-bound: K and V
+# are read once).
+DECODE_WORKLOADS = [
+    Workload("decode_gqa_b16_hq32_hkv8_sq1_skv32768_d128_bf16",
+             16, 32, 8, 1, 32768, 128, True, "bf16", 49),
+    Workload("decode_gqa_b1_hq64_hkv8_sq1_skv32768_d128_bf16",
+             1, 64, 8, 1, 32768, 128, True, "bf16", 50),
+]
+# The other head dimensions the JAX Pallas FlashAttention3 page's `main`
+# sweeps (64, 256) at its B = 1, 16 heads, S = 4096 causal shape.
+HEAD_DIM_WORKLOADS = [
+    Workload("causal_b1_h16_s4096_d64_bf16", 1, 16, 16, 4096, 4096, 64, True, "bf16", 51),
+    Workload("causal_b1_h16_s4096_d256_bf16", 1, 16, 16, 4096, 4096, 256, True, "bf16", 52),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + SPLIT_WORKLOADS + DECODE_WORKLOADS + HEAD_DIM_WORKLOADS}
 
 # The headline benchmark workload: causal, D=128, bf16, S=4096.
 HEADLINE = WORKLOADS[2]
