@@ -45,6 +45,11 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 GPU"
+METRIC_BWD = ("attention bwd TFLOP/s (causal-adjusted, 2.5x the forward's FLOPs: five products) "
+              "and % of bf16 MFMA peak, 1 GPU")
+# Published HBM3E bandwidth of one MI355X (GB/s): the bound of memory-bound
+# (decode-shaped) calls, whose FLOPs per byte sit below the ridge.
+PEAK_HBM_GBS = 8000.0
 # Published dense MFMA peak of one MI355X for bf16 and fp16 (TFLOP/s).  The
 # bench also prints the peak that the device's own compute-unit count and
 # peak clock give (device_peak), beside this one.
@@ -58,15 +63,23 @@ def log(*a):
 
 def kernel_code_hash(kernel: str):
     """sha256 (16 hex digits) of the generated instructions of `kernel` (its
-    assembly up to the kernel descriptor), or None for a name the generators
-    do not make.  Counter figures taken on other instructions no longer
-    describe the kernel."""
+    assembly up to the kernel descriptor; for the HIP C++ tile kernels, their
+    source files), or None for a name neither makes.  Counter figures taken
+    on other instructions no longer describe the kernel."""
     sys.path.insert(0, ROOT)
     try:
         from attention_forward_05_amd.asm.fa_fwd_gen import Gen
         from attention_forward_05_amd.asm.fa_fwd_x8 import Gen8
     finally:
         sys.path.pop(0)
+    if "tile_kernel" in kernel:
+        # the HIP C++ tile kernels (and the merge after a split): their sources
+        srcs = ["fa_tile.hip", "fa_mfma.h", "fa_combine.hip"]
+        h = hashlib.sha256()
+        for s in srcs:
+            with open(os.path.join(ROOT, "attention_forward_05_amd", "csrc", s), "rb") as f:
+                h.update(f.read())
+        return h.hexdigest()[:16]
     parts = kernel.split("_")   # fa_fwd_<dt>_d<D>[_x8|_x8s]_gfx950
     if len(parts) < 5 or parts[:2] != ["fa", "fwd"] or parts[-1] != "gfx950":
         return None
@@ -107,11 +120,16 @@ def launched_kernel(w: workloads.Workload, cus: int) -> str:
                                          True)
     if st != fa.FA_OK:
         raise fa.FAError(st, "fa_fwd_plan")
+    merge = f" ({ranges} key ranges) + combine_kernel" if ranges > 1 else ""
+    if kern == fa.FA_KERNEL_TILE_ROWS:
+        return f"fwd_tile_kernel<{w.dtype}, D={w.D}, rows>{merge}"
+    if kern == fa.FA_KERNEL_TILE_KEYS:
+        return f"fwd_tile_kernel<{w.dtype}, D={w.D}, keys>{merge}"
     if kern == fa.FA_KERNEL_FOUR_WAVE:
         return f"fa_fwd_{w.dtype}_d{w.D}_gfx950"
     if ranges == 1:
         return f"fa_fwd_{w.dtype}_d128_x8_gfx950"
-    return f"fa_fwd_{w.dtype}_d128_x8s_gfx950 ({ranges} key ranges) + combine_kernel"
+    return f"fa_fwd_{w.dtype}_d128_x8s_gfx950{merge}"
 
 
 def device_peak(dtype: str):
@@ -171,8 +189,11 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload_na
         for name, did, val in rows:
             per.setdefault((name, did), 0.0)
             per[(name, did)] += val
-        fa_vals = [v for (n, _), v in per.items() if n.startswith("fa_fwd_")]
-        others = [(v, n) for (n, _), v in per.items() if not n.startswith("fa_fwd_")]
+        def is_attn(n):
+            return n.startswith("fa_fwd_") or "fwd_tile_kernel" in n
+
+        fa_vals = [v for (n, _), v in per.items() if is_attn(n)]
+        others = [(v, n) for (n, _), v in per.items() if not is_attn(n) and "combine" not in n]
         if not fa_vals or not others:
             raise SystemExit(f"{path}: no attention or no copy dispatch found")
         copy_kib, copy_name = max(others)
@@ -191,6 +212,80 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload_na
         "fetch": res["fetch"],
         "write": res["write"],
     }
+
+
+def counter_summary(csv_path: str, w: workloads.Workload, which: str = "fwd"):
+    """Per-dispatch averages of the counters in a rocprofv3 counter-collection
+    CSV for the attention kernels, and the figures derived from them:
+    MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES summed over all instances / (GPU
+    clocks x SIMDs), the GPU clocks being GRBM_GUI_ACTIVE summed over its
+    one-per-XCD instances / XCDs (counts from the run's agent info); LDS
+    bank-conflict cycles per LDS-active cycle; GPU clock = GRBM_GUI_ACTIVE /
+    dispatch duration;
+    executed MFMA FLOPs = MOPS x 512 against the algorithmic count; and
+    transcendental instructions x 64 lanes against the exponentials the
+    method needs (one per visible (query, key) pair)."""
+    import csv
+    per = {}
+    names = {}
+    durations = {}
+    for row in csv.DictReader(open(csv_path, newline="")):
+        name = row["Kernel_Name"]
+        if not (name.startswith("fa_fwd_") or "tile_kernel" in name or "combine_kernel" in name
+                or "bwd_" in name):
+            continue
+        did = row.get("Dispatch_Id", "")
+        cname, val = row["Counter_Name"], float(row["Counter_Value"])
+        per.setdefault(did, {}).setdefault(cname, 0.0)
+        # rocprofv3 sums a counter's instances: for the per-SE / per-SIMD SQ
+        # counters that is the whole chip's count; GRBM_GUI_ACTIVE has one
+        # instance per XCD, each counting the same clocks (divided below)
+        per[did][cname] += val
+        names[did] = name
+        if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+            durations[did] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    kernels = sorted(set(names.values()))
+    # the device's XCD and SIMD counts and peak clock, from the run's agent info
+    xcc, simds, max_mhz = 8, 1024, None
+    info = csv_path.replace("_counter_collection.csv", "_agent_info.csv")
+    if os.path.exists(info):
+        for row in csv.DictReader(open(info, newline="")):
+            if int(row.get("Simd_Count", "0") or 0) > 0:
+                xcc, simds = int(row["Num_Xcc"]), int(row["Simd_Count"])
+                max_mhz = float(row.get("Max_Engine_Clk_Fcompute", 0) or 0) or None
+    out = {"csv": os.path.basename(csv_path), "xcd": xcc, "simds": simds,
+           "max_engine_clock_mhz": max_mhz, "kernels": {}}
+    for kname in kernels:
+        ds = [d for d in per if names[d] == kname]
+        keys = sorted({c for d in ds for c in per[d]})
+        avg = {c: sum(per[d].get(c, 0.0) for d in ds) / len(ds) for c in keys}
+        if "GRBM_GUI_ACTIVE" in avg:
+            avg["GRBM_GUI_ACTIVE"] /= xcc  # GPU clocks of the dispatch
+        entry = {"dispatches": len(ds), "counters_avg_per_dispatch": avg}
+        durs = [durations[d] for d in ds if d in durations]
+        if durs and avg.get("GRBM_GUI_ACTIVE"):
+            entry["dispatch_avg_us"] = round(sum(durs) / len(durs) / 1e3, 2)
+            entry["gpu_clock_mhz"] = round(avg["GRBM_GUI_ACTIVE"] / (sum(durs) / len(durs)) * 1e3, 1)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+            entry["mfma_busy_pct"] = round(100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+                                           / (avg["GRBM_GUI_ACTIVE"] * simds), 2)
+        if avg.get("SQ_LDS_IDX_ACTIVE"):
+            entry["lds_bank_conflict_per_active_cycle"] = round(
+                avg.get("SQ_LDS_BANK_CONFLICT", 0.0) / avg["SQ_LDS_IDX_ACTIVE"], 5)
+        flops = workloads.attention_flops(w.B, w.Sq, w.Skv, w.Hq, w.D, w.causal)
+        if which == "bwd":
+            flops *= 2.5
+        mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        if mops:
+            entry["mfma_flops_executed"] = mops * 512
+            entry["mfma_flops_over_algorithmic"] = round(mops * 512 / flops, 4)
+        if "SQ_INSTS_VALU_TRANS_F32" in avg:
+            exps = flops / (4.0 * w.D) * (1.0 if which == "fwd" else 1.0 / 2.5)
+            entry["trans_f32_lanes"] = avg["SQ_INSTS_VALU_TRANS_F32"] * 64
+            entry["exp_needed"] = exps
+            entry["trans_lanes_over_exp"] = round(avg["SQ_INSTS_VALU_TRANS_F32"] * 64 / exps, 4)
+        out["kernels"][kname] = entry
+    return out
 
 
 def cpu_baseline(w: workloads.Workload, q, k, v, target_s: float = 12.0):
@@ -234,6 +329,44 @@ def cpu_baseline(w: workloads.Workload, q, k, v, target_s: float = 12.0):
     }
 
 
+def cpu_baseline_bwd(w: workloads.Workload, q, k, v, target_s: float = 12.0):
+    """Time the CPU oracle's backward on whole (batch, kv-head group) slices
+    of the workload -- every row and key of the q-heads of one kv-head --
+    adding slices until about target_s seconds, and scale to TFLOP/s with the
+    backward's FLOP count (2.5x the forward's) of those slices."""
+    import numpy as np
+    import torch
+    import oracle
+
+    gen = torch.Generator().manual_seed(w.seed + 1000)
+    do = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(q.dtype)
+    g = w.Hq // w.Hkv
+    slices, t_used, fl = 0, 0.0, 0.0
+    total = w.B * w.Hkv
+    while slices < total and t_used < target_s:
+        b, hk = divmod(slices, w.Hkv)
+        hs = slice(hk * g, (hk + 1) * g)
+        qs = oracle._f64(q[b:b + 1, :, hs])
+        ks = oracle._f64(k[b:b + 1, :, hk:hk + 1])
+        vs = oracle._f64(v[b:b + 1, :, hk:hk + 1])
+        ds = oracle._f64(do[b:b + 1, :, hs])
+        t0 = time.perf_counter()
+        oracle.attn_bwd(qs, ks, vs, ds, w.causal, w.scale)
+        t_used += time.perf_counter() - t0
+        fl += 2.5 * workloads.attention_flops(1, w.Sq, w.Skv, g, w.D, w.causal)
+        slices += 1
+    del np
+    return {
+        "value": fl / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{slices} of {total} (batch, kv-head) slices, each with its {g} q-heads, all "
+                  f"rows and keys; {fl / 1e9:.1f} GFLOP (2.5x forward count) in {t_used:.2f} s "
+                  "(fp64, OpenMP over rows and keys)",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,13 +375,23 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE.name,
                     choices=list(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (default) or the backward pass (fa_bwd)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="first copy BYTES bytes device-to-device (HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="summarise rocprofv3 counter CSVs of this workload's attention kernels")
     ap.add_argument("--compute-units", type=int, default=256,
                     help="with --traffic-summary: compute units of the profiled device")
     args = ap.parse_args()
+
+    if args.counter_summary:
+        w = workloads.BY_NAME[args.workload]
+        for path in args.counter_summary:
+            print(json.dumps(counter_summary(path, w, args.which), indent=1))
+        return
 
     if args.traffic_summary:
         entry = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
@@ -309,6 +452,22 @@ def main():
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_fwd_ws")
 
+    if args.which == "bwd":
+        # the forward's O and LSE, an upstream gradient, the gradients and
+        # the delta workspace, all before the timed region
+        step()
+        gen = torch.Generator().manual_seed(w.seed + 1000)
+        dod = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(q.dtype).to(dev)
+        dqd, dkd, dvd = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        bws = torch.empty(max(4 * w.B * w.Hq * w.Sq, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+        def step():  # noqa: F811 -- the timed step is the backward pass
+            st = fa.fa_bwd(dt, qd, kd, vd, od, lsed, dod, dqd, dkd, dvd, w.B, w.Sq, w.Skv, w.Hq,
+                           w.Hkv, w.D, int(w.causal), w.scale, bws, bws.numel(), sh)
+            if st != fa.FA_OK:
+                raise fa.FAError(st, "fa_bwd")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -337,24 +496,45 @@ def main():
     launch_avg_ms = sum(launch_ms) / len(launch_ms)
 
     flops = workloads.attention_flops(w.B, w.Sq, w.Skv, w.Hq, w.D, w.causal)
+    if args.which == "bwd":
+        flops *= 2.5
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    kernel = launched_kernel(w, cus)
+    kernel = launched_kernel(w, cus) if args.which == "fwd" else \
+        "bwd_delta_kernel + bwd_dkv_kernel + bwd_dq_kernel"
     dev_peak = device_peak(w.dtype)
-    traffic = measured_traffic(w.name, kernel)
-    log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
+    traffic = measured_traffic(w.name, kernel) if args.which == "fwd" else None
+    log(f"[bench] {w.name} ({args.which}): {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak:.0f}); launch avg {launch_avg_ms * 1e3:.1f} us, "
         f"min {launch_ms[0] * 1e3:.1f} us, median {launch_ms[len(launch_ms) // 2] * 1e3:.1f} us")
+    # the bound: matrix cores, unless the call's FLOPs per algorithmic byte
+    # sit below the ridge (peak FLOP/s over HBM bandwidth): then HBM
+    abytes = algorithmic_bytes(w) if args.which == "fwd" else None
+    if abytes and flops / abytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = abytes / (launch_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": abytes}
+        log(f"[bench] memory-bound: {gbs:.0f} GB/s of algorithmic bytes ({abytes / 1e6:.1f} MB)")
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic}
+    roof.update({
+        "kernel_launch_avg_us": round(launch_avg_ms * 1e3, 2),
+        "timing": f"HIP events around each of {args.steps} launches on the launch stream",
+        "kernel": kernel,
+        "device": dev_peak,
+    })
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample of rows ...")
-        cpu = cpu_baseline(w, q, k, v)
+        log("[bench] timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(w, q, k, v) if args.which == "fwd" else cpu_baseline_bwd(w, q, k, v)
         log(f"[bench] cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -372,20 +552,11 @@ def main():
             "flops_per_step": flops, "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / peak, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic,
-            "kernel_launch_avg_us": round(launch_avg_ms * 1e3, 2),
-            "timing": f"HIP events around each of {args.steps} launches on the launch stream",
-            "kernel": kernel,
-            "device": dev_peak,
-        },
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.which == "bwd":
+        out["config"]["pass"] = "bwd"
     print(json.dumps(out), flush=True)
 
 
