@@ -114,10 +114,10 @@ bool group_magic(int Hq, int Hkv, uint32_t* magic) {
 hipError_t launch_kernel(DeviceKernels* dk, const LaunchArgs& a, int variant, bool x8, int l2s);
 
 int64_t work_items(int B, int Sq, int Hq) {
-  return (int64_t)((Sq + kBM - 1) / kBM) * B * Hq;
+  return (((int64_t)Sq + kBM - 1) / kBM) * B * Hq;
 }
 
-int query_tiles(int Sq) { return (Sq + kBM - 1) / kBM; }
+int query_tiles(int Sq) { return (int)(((int64_t)Sq + kBM - 1) / kBM); }
 
 int64_t min_item_tiles(int Sq, int Skv, int causal) {
   // Key ranges grow with the query tile, so the first 512-row query tile
@@ -132,7 +132,7 @@ int64_t min_item_tiles(int Sq, int Skv, int causal) {
 }
 
 bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
-  if (D != 128 || (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
+  if (D != 128 || (((int64_t)Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
   // The eight-wave kernel streams K/V tiles across consecutive items and
   // needs every item with a visible key to span at least 3 key tiles.
   const int64_t n = min_item_tiles(Sq, Skv, causal);
@@ -141,7 +141,7 @@ bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus)
 
 int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
   if (D != 128) return 0;
-  const int64_t items = (int64_t)((Sq + kBM8 - 1) / kBM8) * B * Hq;
+  const int64_t items = (((int64_t)Sq + kBM8 - 1) / kBM8) * B * Hq;
   if (items >= cus) return 0;
   const int64_t n = min_item_tiles(Sq, Skv, causal);
   if (n == 0) return 0;
@@ -158,7 +158,7 @@ int split_log2(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
   while (l > 0 && n < (min_range << l)) --l;
   return l;
 }
-int key_tiles(int Skv) { return (Skv + kBN - 1) / kBN; }
+int key_tiles(int Skv) { return (int)(((int64_t)Skv + kBN - 1) / kBN); }
 
 size_t split_ws_bytes(int B, int Sq, int Hq, int D, int ranges) {
   if (ranges <= 1) return 0;
@@ -277,7 +277,7 @@ hipError_t launch_kernel(DeviceKernels* dk, const LaunchArgs& a, int variant, bo
   ka.Hkv = a.Hkv;
   ka.causal = a.causal;
   ka.c = a.c;
-  const int64_t nq = x8 ? (a.Sq + kBM8 - 1) / kBM8 : query_tiles(a.Sq);
+  const int64_t nq = x8 ? ((int64_t)a.Sq + kBM8 - 1) / kBM8 : query_tiles(a.Sq);
   const int64_t items = (nq * a.B * a.Hq) << l2s;
   ka.log2split = (uint32_t)l2s;
   const int64_t grid = items < dk->cus ? items : dk->cus;
