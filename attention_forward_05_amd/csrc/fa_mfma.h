@@ -107,6 +107,24 @@ __device__ __forceinline__ s16x8 read_rows(const char* tile, int row0, int t, in
   return *reinterpret_cast<const s16x8*>(tile + lds_off<D>(row0 + (lane & 31), 2 * t + (lane >> 5)));
 }
 
+// Scheduling hints for the compiler: within the enclosing basic block,
+// order a chain of N MFMAs whose operands come from N*R LDS reads so that
+// the reads of the first AHEAD MFMAs are issued before the first MFMA and
+// each MFMA is followed by the reads of a later one (the reads' latency then
+// hides behind the MFMAs instead of stalling each one).
+template <int N, int AHEAD, int GROUP, int R = 1>
+__device__ __forceinline__ void sched_reads_ahead() {
+  // masks of __builtin_amdgcn_sched_group_barrier: 0x008 MFMA, 0x100 DS read;
+  // R reads per MFMA, AHEAD MFMAs' worth of reads issued first
+#pragma unroll
+  for (int i = 0; i < AHEAD && i < N; ++i) __builtin_amdgcn_sched_group_barrier(0x100, R, GROUP);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, GROUP);
+    if (i + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, R, GROUP);
+  }
+}
+
 // Registers 8t..8t+7 of a C result, rounded to the input dtype: the B operand
 // of k-step t of the next product.
 template <typename T>

@@ -53,6 +53,10 @@ using namespace mfma;
 
 __device__ __forceinline__ float wave_max32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
+// How far (log2 units) a row's max may pass the reference max before the
+// reference moves: p stays below 2^8, far from fp32 and fp16 overflow.
+constexpr float kLazy = 8.0f;
+
 }  // namespace
 
 struct TileArgs {
@@ -94,7 +98,8 @@ struct Tile {
 };
 
 template <typename T, int D, int TK, bool KEYS>
-__global__ void __launch_bounds__(256) fwd_tile_kernel(TileArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+fwd_tile_kernel(TileArgs a) {
   using P = Tile<T, D, TK, KEYS>;
   __shared__ __attribute__((aligned(16))) char lds[P::kLds];
 
@@ -144,6 +149,10 @@ __global__ void __launch_bounds__(256) fwd_tile_kernel(TileArgs a) {
     for (int t = 0; t < P::kNQ; ++t) {
       s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
       qf[t] = row_ok ? *reinterpret_cast<const s16x8*>(qp + 16 * t) : z;
+      // Q^T is only read (as the B operand) inside the loop: keep it in the
+      // accumulator registers so the O accumulators, which the softmax
+      // rescales with vector instructions, fit the vector registers
+      asm volatile("" : "+a"(qf[t]));
     }
   }
 
@@ -165,14 +174,11 @@ __global__ void __launch_bounds__(256) fwd_tile_kernel(TileArgs a) {
     for (int u = 0; u < P::kNC; ++u) {
       const int c = tid + P::kThreads * u;
       const int r = c / P::kCPR, ch = c % P::kCPR;
-      const int key = t * TK + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[u] = z;
-      vreg[u] = z;
-      if (key < a.Skv) {
-        kreg[u] = *reinterpret_cast<const u32x4*>(kbase + key * kv_row + 8 * ch);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vbase + key * kv_row + 8 * ch);
-      }
+      // rows past the last key read the last key's row again: valid, finite
+      // data whose logits are masked to -inf, so their p (and P.V terms) are 0
+      const int64_t kc = min(t * TK + r, a.Skv - 1);
+      kreg[u] = *reinterpret_cast<const u32x4*>(kbase + kc * kv_row + 8 * ch);
+      vreg[u] = *reinterpret_cast<const u32x4*>(vbase + kc * kv_row + 8 * ch);
     }
   };
   auto store_tile = [&](int stage) {
@@ -199,56 +205,65 @@ __global__ void __launch_bounds__(256) fwd_tile_kernel(TileArgs a) {
     const char* kl = lds + stage * P::kStageBytes;
     const char* vl = kl + P::kTileBytes;
 
-    // S^T for this wave's key blocks
+    // S^T for this wave's key blocks: the K operands of a block are read
+    // from LDS before its MFMA chain, so the reads are in flight together
     f32x16 sacc[P::kKB];
 #pragma unroll
     for (int kb = 0; kb < P::kKB; ++kb) {
       const int kr = (KEYS ? 32 * wave : 32 * kb) + l32;
-      f32x16 acc;
+      s16x8 kf[P::kNQ];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+      for (int q = 0; q < P::kNQ; ++q)
+        kf[q] = *reinterpret_cast<const s16x8*>(kl + lds_off<D>(kr, 2 * q + h));
+      f32x16 acc = zero16();
 #pragma unroll
-      for (int q = 0; q < P::kNQ; ++q) {
-        const s16x8 kf = *reinterpret_cast<const s16x8*>(kl + lds_off<D>(kr, 2 * q + h));
-        acc = T::mma(kf, qf[q], acc);
-      }
+      for (int q = 0; q < P::kNQ; ++q) acc = T::mma(kf[q], qf[q], acc);
       sacc[kb] = acc;
     }
+    sched_reads_ahead<P::kKB * P::kNQ, 4, 0>();
 
-    // mask, scale, row max
+    // mask (branch-free select), scale, row max
     const int key0 = t * TK;
-    const bool full = (key0 + TK <= kend) && (!a.causal || key0 + TK - 1 <= klimit);
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < P::kKB; ++kb) {
       const int kbase_key = key0 + (KEYS ? 32 * wave : 32 * kb) + 4 * h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float x = sacc[kb][i] * a.c;
-        if (!full) {
-          const int key = kbase_key + 8 * (i >> 2) + (i & 3);
-          if (key >= kend || key > klimit) x = -INFINITY;
-        }
+        const int key = kbase_key + 8 * (i >> 2) + (i & 3);
+        const bool vis = key < kend && key <= klimit;
+        const float x = vis ? sacc[kb][i] * a.c : -INFINITY;
         sacc[kb][i] = x;
         mt = fmaxf(mt, x);
       }
     }
     mt = wave_max32(mt);
-    const float mnew = fmaxf(m, mt);
-    const float mref = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
-    m = mnew;
-    l *= alpha;
-    if (__any(alpha != 1.0f)) {
+    // lazy reference max: m moves (and O, l are rescaled) only when a row's
+    // max passes it by more than kLazy, so p = exp2(x - m) <= 2^kLazy; the
+    // final O / l and LSE use the one m both were accumulated against
+    if (__any(mt > m + kLazy)) {
+      const float mnew = mt > m + kLazy ? mt : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.0f : mnew));
+      m = mnew;
+      l *= alpha;
 #pragma unroll
       for (int d = 0; d < P::kND; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
     }
+    const float mref = (m == -INFINITY) ? 0.0f : m;
 
-    // P^T = exp2(c*s - m), packed to the input dtype as B operands
+    // P^T = exp2(c*s - m), packed to the input dtype as B operands, and
+    // O^T += V^T . P^T over the 32 keys of each block (two k-steps), the V^T
+    // operands of a block read before its MFMAs
 #pragma unroll
     for (int kb = 0; kb < P::kKB; ++kb) {
+      const int kb_row = KEYS ? 32 * wave : 32 * kb;
+      s16x8 vf[2][P::kND];
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+        for (int d = 0; d < P::kND; ++d) vf[ts][d] = read_a_rows<D>(vl, kb_row, ts, 32 * d, lane);
       s16x8 pf[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -256,22 +271,12 @@ __global__ void __launch_bounds__(256) fwd_tile_kernel(TileArgs a) {
         l += p;
         pf[i >> 3][i & 7] = T::cvt(p);
       }
-      // O^T += V^T . P^T over the 32 keys of this block (two k-steps)
-      const int kb_row = KEYS ? 32 * wave : 32 * kb;
 #pragma unroll
-      for (int ts = 0; ts < 2; ++ts) {
-        const int r0 = kb_row + 16 * ts + 4 * h + ((lane & 15) >> 2);
-        const int colc = (lane >> 4) & 1;  // which 16-dim half of the 32-dim block
+      for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
-        for (int d = 0; d < P::kND; ++d) {
-          const int col = 32 * d + 16 * colc + 4 * (lane & 3);
-          const s16x4 lo = read_tr(vl + lds_off<D>(r0, col >> 3) + (col & 7) * 2);
-          const s16x4 hi = read_tr(vl + lds_off<D>(r0 + 8, col >> 3) + (col & 7) * 2);
-          const s16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[d] = T::mma(vf, pf[ts], oacc[d]);
-        }
-      }
+        for (int d = 0; d < P::kND; ++d) oacc[d] = T::mma(vf[ts][d], pf[ts], oacc[d]);
     }
+    sched_reads_ahead<P::kKB * 2 * P::kND, 3, 1, 2>();
 
     if (t + 1 < t1) store_tile(stage ^ 1);
     __syncthreads();
