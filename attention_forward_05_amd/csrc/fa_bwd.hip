@@ -115,14 +115,21 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
   // K^T and V^T as B operands: lane holds K[key][16t + 8h .. +7]
   s16x8 kf[NQ], vf[NQ];
   {
-    const int64_t kvoff = (((int64_t)b * a.Skv + key) * a.Hkv + hk) * D + 8 * h;
+    // a key past the end reads the last key's row: finite data, and its
+    // gradients are not stored
+    const int64_t kc = min(key, a.Skv - 1);
+    const int64_t kvoff = (((int64_t)b * a.Skv + kc) * a.Hkv + hk) * D + 8 * h;
     const short* kp = static_cast<const short*>(a.k) + kvoff;
     const short* vp = static_cast<const short*>(a.v) + kvoff;
-    const s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-      kf[t] = key_ok ? *reinterpret_cast<const s16x8*>(kp + 16 * t) : z;
-      vf[t] = key_ok ? *reinterpret_cast<const s16x8*>(vp + 16 * t) : z;
+      kf[t] = *reinterpret_cast<const s16x8*>(kp + 16 * t);
+      vf[t] = *reinterpret_cast<const s16x8*>(vp + 16 * t);
+      // only read (as B operands) in the loop: kept in the accumulator
+      // registers, leaving the vector registers to the accumulators and the
+      // operands read ahead
+      asm volatile("" : "+a"(kf[t]));
+      asm volatile("" : "+a"(vf[t]));
     }
   }
   f32x16 dka[ND], dva[ND];
@@ -148,15 +155,12 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
     for (int u = 0; u < NC; ++u) {
       const int c = tid + 256 * u;
       const int r = c / CPR, ch = c % CPR;
-      const int i = i0 + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[u] = z;
-      dreg[u] = z;
-      if (i < a.Sq) {
-        const int64_t e = (((int64_t)b * a.Sq + i) * a.Hq + hq) * D + 8 * ch;
-        qreg[u] = *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.q) + e);
-        dreg[u] = *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.dout) + e);
-      }
+      // a row past the end reads the last row: finite data whose P is 0
+      // (its LSE is taken as +inf below), so it adds nothing
+      const int i = min(i0 + r, a.Sq - 1);
+      const int64_t e = (((int64_t)b * a.Sq + i) * a.Hq + hq) * D + 8 * ch;
+      qreg[u] = *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.q) + e);
+      dreg[u] = *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.dout) + e);
     }
     if (tid < BQ) {
       const int i = i0 + tid;
@@ -200,12 +204,20 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
     const float* ll = reinterpret_cast<const float*>(dl + TILE);
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
-      // S = Q.K^T and dP = dO.V^T, C[query][key]
+      // S = Q.K^T and dP = dO.V^T, C[query][key]; the A operands (rows of
+      // the Q and dO blocks) read ahead of their MFMA chains
+      s16x8 qa[NQ], da[NQ];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        qa[t] = read_rows<D>(ql, 32 * qh, t, lane);
+        da[t] = read_rows<D>(dl, 32 * qh, t, lane);
+      }
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int t = 0; t < NQ; ++t) s = T::mma(read_rows<D>(ql, 32 * qh, t, lane), kf[t], s);
+      for (int t = 0; t < NQ; ++t) s = T::mma(qa[t], kf[t], s);
 #pragma unroll
-      for (int t = 0; t < NQ; ++t) dp = T::mma(read_rows<D>(dl, 32 * qh, t, lane), vf[t], dp);
+      for (int t = 0; t < NQ; ++t) dp = T::mma(da[t], vf[t], dp);
+      sched_reads_ahead<2 * NQ, 4, 0>();
       f32x16 p, ds;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -216,21 +228,41 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int qi = i0 + row + e;
           const bool vis = key_ok && (!a.causal || key <= qi + off);
-          const float pv = vis ? __builtin_amdgcn_exp2f(s[4 * j + e] * a.c - l4[e]) : 0.0f;
+          const float x = vis ? s[4 * j + e] * a.c - l4[e] : -INFINITY;
+          const float pv = __builtin_amdgcn_exp2f(x);
           p[4 * j + e] = pv;
           ds[4 * j + e] = pv * (dp[4 * j + e] - d4[e]);
         }
       }
-      // dV^T += dO^T.P and dK^T += Q^T.dS over the 32 rows (two k-steps)
+      // dV^T += dO^T.P, then dK^T += Q^T.dS, over the 32 rows (two k-steps
+      // each); their A operands read transposed from the dO and Q blocks
+      {
+        s16x8 dta[2][ND];
 #pragma unroll
-      for (int ts = 0; ts < 2; ++ts) {
-        const s16x8 pb = pack_b<T>(p, ts);
-        const s16x8 sb = pack_b<T>(ds, ts);
+        for (int ts = 0; ts < 2; ++ts)
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          dva[db] = T::mma(read_a_rows<D>(dl, 32 * qh, ts, 32 * db, lane), pb, dva[db]);
-          dka[db] = T::mma(read_a_rows<D>(ql, 32 * qh, ts, 32 * db, lane), sb, dka[db]);
+          for (int db = 0; db < ND; ++db) dta[ts][db] = read_a_rows<D>(dl, 32 * qh, ts, 32 * db, lane);
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) {
+          const s16x8 pb = pack_b<T>(p, ts);
+#pragma unroll
+          for (int db = 0; db < ND; ++db) dva[db] = T::mma(dta[ts][db], pb, dva[db]);
         }
+        sched_reads_ahead<2 * ND, 3, 1, 2>();
+      }
+      {
+        s16x8 qta[2][ND];
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+          for (int db = 0; db < ND; ++db) qta[ts][db] = read_a_rows<D>(ql, 32 * qh, ts, 32 * db, lane);
+#pragma unroll
+        for (int ts = 0; ts < 2; ++ts) {
+          const s16x8 sb = pack_b<T>(ds, ts);
+#pragma unroll
+          for (int db = 0; db < ND; ++db) dka[db] = T::mma(qta[ts][db], sb, dka[db]);
+        }
+        sched_reads_ahead<2 * ND, 3, 2, 2>();
       }
     }
     if (st + 1 < nsteps) store_step(stage ^ 1);
@@ -284,12 +316,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
   s16x8 qf[NQ], df[NQ];
   float lse2 = INFINITY, dl = 0.0f;
   {
-    const int64_t e = (((int64_t)b * a.Sq + qi) * a.Hq + hq) * D + 8 * h;
-    const s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    // a row past the end reads the last row (finite; its dQ is not stored)
+    const int64_t e = (((int64_t)b * a.Sq + min(qi, a.Sq - 1)) * a.Hq + hq) * D + 8 * h;
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-      qf[t] = row_ok ? *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.q) + e + 16 * t) : z;
-      df[t] = row_ok ? *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + e + 16 * t) : z;
+      qf[t] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.q) + e + 16 * t);
+      df[t] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + e + 16 * t);
+      asm volatile("" : "+a"(qf[t]));  // read-only B operands: accumulator registers
+      asm volatile("" : "+a"(df[t]));
     }
     if (row_ok) {
       const int64_t row = ((int64_t)b * a.Hq + hq) * a.Sq + qi;
@@ -315,14 +349,10 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
     for (int u = 0; u < NC; ++u) {
       const int c = tid + 256 * u;
       const int r = c / CPR, ch = c % CPR;
-      const int kk = t * TK + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[u] = z;
-      vreg[u] = z;
-      if (kk < a.Skv) {
-        kreg[u] = *reinterpret_cast<const u32x4*>(kbase + kk * kv_row + 8 * ch);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vbase + kk * kv_row + 8 * ch);
-      }
+      // keys past the end read the last key's row: finite, masked to P = 0
+      const int64_t kk = min(t * TK + r, a.Skv - 1);
+      kreg[u] = *reinterpret_cast<const u32x4*>(kbase + kk * kv_row + 8 * ch);
+      vreg[u] = *reinterpret_cast<const u32x4*>(vbase + kk * kv_row + 8 * ch);
     }
   };
   auto store_tile = [&](int stage) {
@@ -349,19 +379,33 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
     const char* vl = kl + TILE;
 #pragma unroll
     for (int kb = 0; kb < TK / 32; ++kb) {
-      // S^T = K.Q^T and dP^T = V.dO^T, C[key][query]
+      // S^T = K.Q^T and dP^T = V.dO^T, C[key][query]; the A operands (rows
+      // of the K and V tiles) read ahead of their MFMA chains
+      s16x8 ka[NQ], va[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        ka[u] = read_rows<D>(kl, 32 * kb, u, lane);
+        va[u] = read_rows<D>(vl, 32 * kb, u, lane);
+      }
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int u = 0; u < NQ; ++u) s = T::mma(read_rows<D>(kl, 32 * kb, u, lane), qf[u], s);
+      for (int u = 0; u < NQ; ++u) s = T::mma(ka[u], qf[u], s);
 #pragma unroll
-      for (int u = 0; u < NQ; ++u) dp = T::mma(read_rows<D>(vl, 32 * kb, u, lane), df[u], dp);
+      for (int u = 0; u < NQ; ++u) dp = T::mma(va[u], df[u], dp);
+      sched_reads_ahead<2 * NQ, 4, 0>();
+      s16x8 kta[2][ND];
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) kta[ts][db] = read_a_rows<D>(kl, 32 * kb, ts, 32 * db, lane);
       f32x16 ds;
       const int kb0 = t * TK + 32 * kb + 4 * h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = kb0 + 8 * (i >> 2) + (i & 3);
         const bool vis = kk < kend && kk <= klimit;
-        const float pv = vis ? __builtin_amdgcn_exp2f(s[i] * a.c - lse2) : 0.0f;
+        const float x = vis ? s[i] * a.c - lse2 : -INFINITY;
+        const float pv = __builtin_amdgcn_exp2f(x);
         ds[i] = pv * (dp[i] - dl);
       }
       // dQ^T += K^T.dS^T over the 32 keys (two k-steps)
@@ -369,9 +413,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
       for (int ts = 0; ts < 2; ++ts) {
         const s16x8 sb = pack_b<T>(ds, ts);
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
-          dqa[db] = T::mma(read_a_rows<D>(kl, 32 * kb, ts, 32 * db, lane), sb, dqa[db]);
+        for (int db = 0; db < ND; ++db) dqa[db] = T::mma(kta[ts][db], sb, dqa[db]);
       }
+      sched_reads_ahead<2 * ND, 3, 1, 2>();
     }
     if (t + 1 < ntiles) store_tile(stage ^ 1);
     __syncthreads();
