@@ -53,9 +53,9 @@ using namespace mfma;
 
 __device__ __forceinline__ float wave_max32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 
-// How far (log2 units) a row's max may pass the reference max before the
-// reference moves: p stays below 2^8, far from fp32 and fp16 overflow.
-constexpr float kLazy = 8.0f;
+// The slow-path trigger: a lane's sum of p over one tile above 2^8.  Every p
+// then stays at most 2^8, far from fp32 and fp16 overflow.
+constexpr float kTrigger = 256.0f;
 
 }  // namespace
 
@@ -222,40 +222,65 @@ fwd_tile_kernel(TileArgs a) {
     }
     sched_reads_ahead<P::kKB * P::kNQ, 4, 0>();
 
-    // mask (branch-free select), scale, row max
+    // mask: only a tile that some row of the wave does not fully see
+    // (a wave-uniform test), by setting its hidden logits to -inf
     const int key0 = t * TK;
-    float mt = -INFINITY;
+    const int klast = key0 + (KEYS ? 32 * wave + 31 : TK - 1);
+    if (!__all(klast < kend && klast <= klimit)) {
 #pragma unroll
-    for (int kb = 0; kb < P::kKB; ++kb) {
-      const int kbase_key = key0 + (KEYS ? 32 * wave : 32 * kb) + 4 * h;
+      for (int kb = 0; kb < P::kKB; ++kb) {
+        const int kbase_key = key0 + (KEYS ? 32 * wave : 32 * kb) + 4 * h;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kbase_key + 8 * (i >> 2) + (i & 3);
-        const bool vis = key < kend && key <= klimit;
-        const float x = vis ? sacc[kb][i] * a.c : -INFINITY;
-        sacc[kb][i] = x;
-        mt = fmaxf(mt, x);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase_key + 8 * (i >> 2) + (i & 3);
+          sacc[kb][i] = (key < kend && key <= klimit) ? sacc[kb][i] : -INFINITY;
+        }
       }
     }
-    mt = wave_max32(mt);
-    // lazy reference max: m moves (and O, l are rescaled) only when a row's
-    // max passes it by more than kLazy, so p = exp2(x - m) <= 2^kLazy; the
-    // final O / l and LSE use the one m both were accumulated against
-    if (__any(mt > m + kLazy)) {
-      const float mnew = mt > m + kLazy ? mt : m;
+    // p = exp2(c*s - m) against the lazy reference m.  While every lane's
+    // sum of its p in this tile stays at most kTrigger, each p is too, and m
+    // stays; otherwise (and while a row has no reference yet) the slow path
+    // takes the tile's row max, moves m, rescales O and l, and redoes p.
+    f32x16 pv[P::kKB];
+    float lt = 0.0f;
+    float mref = (m == -INFINITY) ? 0.0f : m;
+#pragma unroll
+    for (int kb = 0; kb < P::kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], a.c, -mref));
+        lt += pv[kb][i];
+      }
+    if (__any(!(lt <= kTrigger) || m == -INFINITY)) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < P::kKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i] * a.c);
+      mt = wave_max32(mt);
+      const float mnew = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - (mnew == -INFINITY ? 0.0f : mnew));
       m = mnew;
+      mref = (m == -INFINITY) ? 0.0f : m;
       l *= alpha;
 #pragma unroll
       for (int d = 0; d < P::kND; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      lt = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < P::kKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          pv[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], a.c, -mref));
+          lt += pv[kb][i];
+        }
     }
-    const float mref = (m == -INFINITY) ? 0.0f : m;
+    l += lt;
 
-    // P^T = exp2(c*s - m), packed to the input dtype as B operands, and
-    // O^T += V^T . P^T over the 32 keys of each block (two k-steps), the V^T
-    // operands of a block read before its MFMAs
+    // P^T packed to the input dtype as B operands, and O^T += V^T . P^T over
+    // the 32 keys of each block (two k-steps), the V^T operands of a block
+    // read before its MFMAs
 #pragma unroll
     for (int kb = 0; kb < P::kKB; ++kb) {
       const int kb_row = KEYS ? 32 * wave : 32 * kb;
@@ -266,11 +291,7 @@ fwd_tile_kernel(TileArgs a) {
         for (int d = 0; d < P::kND; ++d) vf[ts][d] = read_a_rows<D>(vl, kb_row, ts, 32 * d, lane);
       s16x8 pf[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kb][i] - mref);
-        l += p;
-        pf[i >> 3][i & 7] = T::cvt(p);
-      }
+      for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = T::cvt(pv[kb][i]);
 #pragma unroll
       for (int ts = 0; ts < 2; ++ts)
 #pragma unroll

@@ -308,6 +308,16 @@ def test_decode_tile_kernels(fa, D, Sq, Hq, Hkv, causal):
         full_case(fa, 2, Sq, 5000, Hq, Hkv, D, causal, dtype, seed=Sq + Hq + D, split=split)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_slow_path(fa, D):
+    """Decode shapes with 1% of the key rows scaled by 8, fp16: rows' maxima
+    jump inside the key ranges, so the tile kernel's reference max moves
+    (its slow path) in both the key and the row split."""
+    for Sq, Hq, Hkv in ((1, 32, 8), (16, 16, 2)):
+        full_case(fa, 1, Sq, 9000, Hq, Hkv, D, True, "f16", seed=60 + Sq + D, boost=0.01,
+                  split=True)
+
+
 # head dimension 256: the tile kernel, four waves over 128-row blocks
 D256_CASES = [
     # B, Sq, Skv, Hq, Hkv, causal, dtype, split
