@@ -631,6 +631,9 @@ class Gen8:
         case; the other combinations run out of line."""
         em, k0, dl, x = self.em, self.s_k0, self.s_dl, self.s_x[0]
         l_v, l_join = self.lab("mvar"), self.lab("mjoin")
+        # the wave in its MFMA phase issues ahead of the SIMD's other wave (in
+        # its softmax phase), so the matrix core is fed first
+        em.salu("s_setprio 1")
         test = dl[0]
         if not qk:                                 # P.V only: the previous sub-tile
             em.salu(f"s_sub_u32 {x}, {k0}, 32")
@@ -641,6 +644,7 @@ class Gen8:
         snap = em.snapshot()
         self.m_phase(pv, qk, first_pv)
         em.label(l_join)
+        em.salu("s_setprio 0")
 
         def variants():
             # block 0 is not live for the S^T sub-tile (or, P.V only, for P.V)
