@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(256) bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int qi = i0 + row + e;
-          const bool vis = key_ok && (!a.causal || key <= qi + off);
+          const bool vis = key_ok & ((a.causal == 0) | (key <= qi + off));  // no short-circuit branches
           const float x = vis ? s[4 * j + e] * a.c - l4[e] : -INFINITY;
           const float pv = __builtin_amdgcn_exp2f(x);
           p[4 * j + e] = pv;
@@ -403,7 +403,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = kb0 + 8 * (i >> 2) + (i & 3);
-        const bool vis = kk < kend && kk <= klimit;
+        const bool vis = (kk < kend) & (kk <= klimit);
         const float x = vis ? s[i] * a.c - lse2 : -INFINITY;
         const float pv = __builtin_amdgcn_exp2f(x);
         ds[i] = pv * (dp[i] - dl);

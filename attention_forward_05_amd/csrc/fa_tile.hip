@@ -226,14 +226,14 @@ fwd_tile_kernel(TileArgs a) {
     // (a wave-uniform test), by setting its hidden logits to -inf
     const int key0 = t * TK;
     const int klast = key0 + (KEYS ? 32 * wave + 31 : TK - 1);
-    if (!__all(klast < kend && klast <= klimit)) {
+    if (!__all((klast < kend) & (klast <= klimit))) {
 #pragma unroll
       for (int kb = 0; kb < P::kKB; ++kb) {
         const int kbase_key = key0 + (KEYS ? 32 * wave : 32 * kb) + 4 * h;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kbase_key + 8 * (i >> 2) + (i & 3);
-          sacc[kb][i] = (key < kend && key <= klimit) ? sacc[kb][i] : -INFINITY;
+          sacc[kb][i] = ((key < kend) & (key <= klimit)) ? sacc[kb][i] : -INFINITY;
         }
       }
     }
