@@ -1089,7 +1089,8 @@ VARIANTS = [("bf16", 128), ("bf16", 64), ("f16", 128), ("f16", 64)]
 
 def generate_all() -> str:
     """Every kernel of the library: the four-wave variants, then the
-    eight-wave D = 128 variants (fa_fwd_x8), whole key ranges and split."""
+    eight-wave D = 128 variants (fa_fwd_x8), whole key ranges and split,
+    and the eight-wave D = 64 variants on whole key ranges."""
     from .fa_fwd_x8 import Gen8
     texts, metas = [], []
     for dt, D in VARIANTS:
@@ -1102,6 +1103,10 @@ def generate_all() -> str:
             txt, info = Gen8(dt, split).assemble_text()
             texts.append(txt)
             metas.append(info)
+    for dt in ("bf16", "f16"):
+        txt, info = Gen8(dt, False, 64).assemble_text()
+        texts.append(txt)
+        metas.append(info)
     return "".join(texts) + metadata(metas)
 
 

@@ -50,22 +50,22 @@ AHEAD = 3         # tiles whose loads are in flight ahead of the tile in use
 THRESH = 32768.0  # slow-path trigger: a lane's 16-key partial row sum above 2^15
 
 
-def kernel_name(dtype: str, split: bool = False) -> str:
-    return f"fa_fwd_{dtype}_d128_x8{'s' if split else ''}_gfx950"
+def kernel_name(dtype: str, split: bool = False, D: int = 128) -> str:
+    return f"fa_fwd_{dtype}_d{D}_x8{'s' if split else ''}_gfx950"
 
 
 class Gen8:
-    D = 128
 
-    def __init__(self, dtype: str, split: bool = False):
-        assert dtype in ("bf16", "f16")
+    def __init__(self, dtype: str, split: bool = False, D: int = 128):
+        assert dtype in ("bf16", "f16") and D in (64, 128)
         self.dtype = dtype
+        self.D = D
         # split: every (batch, q-head, query tile) item is cut into 2^log2split
         # key ranges (kernel argument); each writes its normalised O (fp32)
         # and LSE to the partial buffers passed as o / lse, which a combine
         # kernel merges
         self.split = split
-        self.name = kernel_name(dtype, split)
+        self.name = kernel_name(dtype, split, D)
         self.mfma_op = "v_mfma_f32_32x32x16_bf16" if dtype == "bf16" else "v_mfma_f32_32x32x16_f16"
         self.cvt_op = "v_cvt_pk_bf16_f32" if dtype == "bf16" else "v_cvt_pk_f16_f32"
         D = self.D
@@ -76,18 +76,20 @@ class Gen8:
         self.CH = D // 8              # 16-byte chunks per row
         self.RPD = 64 // self.CH      # rows per 64-lane DMA instruction
         self.DPW = (BN // WAVES) // self.RPD  # DMA instructions per wave per K (or V) tile
+        self.LPT = 2 * self.DPW       # loads per wave per stream tile (K and V)
         self.KREG = 0
         self.VREG = SLOTS * self.TILE
         self.DUMP = 2 * SLOTS * self.TILE    # spare K and V tile for all-zero tiles
         self.LDS = self.DUMP + 2 * self.TILE
-        assert self.VREG == 65536 and self.DPW == 2 and self.LDS <= 160 * 1024
+        assert self.DPW >= 1 and self.LDS <= 160 * 1024
         self.em = Emitter()
         self._lab = 0
         self.deferred = []
 
     def lab(self, tag):
         self._lab += 1
-        return f".L{self.dtype}x8{'s' if self.split else ''}_{tag}_{self._lab}"
+        d = "" if self.D == 128 else f"d{self.D}"
+        return f".L{self.dtype}{d}x8{'s' if self.split else ''}_{tag}_{self._lab}"
 
     # ------------------------------------------------------------------------
     def alloc(self):
@@ -113,11 +115,11 @@ class Gen8:
         # O^T accumulators in VGPRs (the epilogue and the slow path scale them
         # in place), Q in AGPRs (only ever an MFMA operand)
         r["v_O"] = [[V.take(f"O{q}{d}", 16, 4) for d in range(self.NDB)] for q in range(2)]
-        self.nvgpr = 192
-        assert V.next == 192
+        self.nvgpr = V.next
+        assert V.next == 64 + 32 * self.NDB
         r["a_Q"] = [[A.take(f"Q{q}{s}", 4, 4) for s in range(self.NS)] for q in range(2)]
-        self.nagpr = 64
-        assert A.next == 64
+        self.nagpr = A.next
+        assert A.next == 8 * self.NS
         t = S.take
         # the current item
         r["s_hq"], r["s_qt"], r["s_b"], r["s_hk"] = t("hq", 1), t("qt", 1), t("b", 1), t("hk", 1)
@@ -174,6 +176,26 @@ class Gen8:
         em.salu(f"s_mul_i32 {self.s_rowb}, s22, {D * 2}")          # K/V row stride
         em.salu(f"s_mul_i32 {self.s_wrow}, {self.s_w}, {(BN // WAVES) * self.ROW}")
 
+    # LDS swizzles (the LDS serves 256 bytes per pass: 16 lanes of a K row
+    # read, 32 lanes of a transposing V read).  D = 128 (256-byte rows):
+    # chunk c of K row r sits at c ^ (r & 15), of V row r at c ^ 4*(r & 3).
+    # D = 64 (128-byte rows, two rows per pass of the banks): K at
+    # c ^ ((r >> 1) & 7), V at c ^ 4*((r >> 1) & 1).  Row reads of 16
+    # consecutive rows and transposing reads of 4 rows x 4 chunks then hit
+    # 64 distinct banks.
+    def emit_ksw(self, dst, row):
+        if self.D == 128:
+            self.em.valu(f"v_and_b32 {dst}, 15, {row}", dst=[dst], src=[row])
+        else:
+            self.em.valu(f"v_bfe_u32 {dst}, {row}, 1, 3", dst=[dst], src=[row])
+
+    def emit_vsw(self, dst, row):
+        if self.D == 128:
+            self.em.valu(f"v_and_b32 {dst}, 3, {row}", dst=[dst], src=[row])
+        else:
+            self.em.valu(f"v_bfe_u32 {dst}, {row}, 1, 1", dst=[dst], src=[row])
+        self.em.valu(f"v_lshlrev_b32 {dst}, 2, {dst}", dst=[dst], src=[dst])
+
     def tmps(self):
         """Scratch VGPRs for set-up code (the S registers are free then)."""
         return [self.v_S[i // 16].r(i % 16) for i in range(32)]
@@ -220,25 +242,23 @@ class Gen8:
             r_, off, sw = t[4], t[5], t[6]
             em.valu(f"v_add_u32 {r_}, {self.RPD * i}, {t[2]}", dst=[r_], src=[t[2]])
             em.valu(f"v_mul_lo_u32 {off}, {r_}, {self.s_rowb}", dst=[off], src=[r_])
-            em.valu(f"v_and_b32 {sw}, 15, {r_}", dst=[sw], src=[r_])
+            self.emit_ksw(sw, r_)
             em.valu(f"v_xor_b32 {sw}, {sw}, {t[3]}", dst=[sw], src=[sw, t[3]])
             em.valu(f"v_lshl_add_u32 {self.v_kdma.r(i)}, {sw}, 4, {off}", dst=[self.v_kdma.r(i)], src=[sw, off])
-            em.valu(f"v_and_b32 {sw}, 3, {r_}", dst=[sw], src=[r_])
-            em.valu(f"v_lshlrev_b32 {sw}, 2, {sw}", dst=[sw], src=[sw])
+            self.emit_vsw(sw, r_)
             em.valu(f"v_xor_b32 {sw}, {sw}, {t[3]}", dst=[sw], src=[sw, t[3]])
             em.valu(f"v_lshl_add_u32 {self.v_vdma.r(i)}, {sw}, 4, {off}", dst=[self.v_vdma.r(i)], src=[sw, off])
-        # K operand of k-step s: l32*ROW + 16*((2s + h) ^ (l32 & 15)) = klane ^ (s << 5)
-        em.valu(f"v_and_b32 {t[2]}, 15, {l32}", dst=[t[2]], src=[l32])
+        # K operand of k-step s: l32*ROW + 16*((2s + h) ^ ksw(l32)) = klane ^ (s << 5)
+        self.emit_ksw(t[2], l32)
         em.valu(f"v_xor_b32 {t[2]}, {t[2]}, {h}", dst=[t[2]], src=[t[2], h])
         em.valu(f"v_mul_u32_u24 {t[3]}, {self.ROW}, {l32}", dst=[t[3]], src=[l32])
         em.valu(f"v_lshl_add_u32 {self.v_klane}, {t[2]}, 4, {t[3]}", dst=[str(self.v_klane)], src=[t[2], t[3]])
         # V operand of d-block db (transposing reads): tr_i = lane & 15,
         # tr_row = 4h + (tr_i >> 2), chunk (4db + 2*((lane >> 4) & 1) + ((lane >> 1) & 1))
-        # ^ 4*(tr_row & 3), byte 8*(lane & 1):  vlane ^ (db << 6)
+        # ^ vsw(tr_row), byte 8*(lane & 1):  vlane ^ (db << 6)
         em.valu(f"v_bfe_u32 {t[2]}, {lane}, 2, 2", dst=[t[2]], src=[lane])
         em.valu(f"v_lshl_add_u32 {t[2]}, {h}, 2, {t[2]}", dst=[t[2]], src=[h, t[2]])       # tr_row
-        em.valu(f"v_and_b32 {t[3]}, 3, {t[2]}", dst=[t[3]], src=[t[2]])
-        em.valu(f"v_lshlrev_b32 {t[3]}, 2, {t[3]}", dst=[t[3]], src=[t[3]])                # sw
+        self.emit_vsw(t[3], t[2])                                                          # sw
         em.valu(f"v_bfe_u32 {t[4]}, {lane}, 4, 1", dst=[t[4]], src=[lane])
         em.valu(f"v_bfe_u32 {t[5]}, {lane}, 1, 1", dst=[t[5]], src=[lane])
         em.valu(f"v_lshl_add_u32 {t[4]}, {t[4]}, 1, {t[5]}", dst=[t[4]], src=[t[4], t[5]])
@@ -1120,7 +1140,7 @@ class Gen8:
             self.emit_dma(self.s_y[5])
         self.item_start()
         em.drain()
-        em.salu(f"s_waitcnt vmcnt({4 * (AHEAD - 1)})")     # Q and tile 0
+        em.salu(f"s_waitcnt vmcnt({self.LPT * (AHEAD - 1)})")     # Q and tile 0
         em.salu("s_barrier")
         self.zero_dead_blocks()
         self.prefetch(self.qk_frags(0))
@@ -1136,7 +1156,7 @@ class Gen8:
         em.salu("s_barrier")
         self.v_phase(0, first=True, next_frags=self.pv_frags(0))
         self.m_phase_sel(self.pv_frags(0), self.qk_frags(1), first_pv=True)
-        em.salu("s_waitcnt vmcnt(4)")                       # stream tile 1
+        em.salu(f"s_waitcnt vmcnt({self.LPT})")               # stream tile 1
         em.salu("s_barrier")
         self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
         em.salu(f"s_add_u32 {self.s_u}, {self.s_u}, 1")
@@ -1150,7 +1170,7 @@ class Gen8:
         em.salu("s_barrier")
         self.v_phase(0, next_frags=self.pv_frags(0), vb_tile=self.s_u)
         self.m_phase_sel(self.pv_frags(0), self.qk_frags(1))
-        em.salu("s_waitcnt vmcnt(4)")                       # stream tile u+1
+        em.salu(f"s_waitcnt vmcnt({self.LPT})")               # stream tile u+1
         em.salu("s_barrier")
         self.v_phase(1, dma=True, next_frags=self.pv_frags(1))
         em.salu(f"s_add_u32 {self.s_u}, {self.s_u}, 1")
@@ -1177,7 +1197,7 @@ class Gen8:
         self.item_start()
         self.zero_dead_blocks()
         # Q of this item (its tile 2 and the previous epilogue's stores came later)
-        em.salu(f"s_waitcnt vmcnt({4 + self.epilogue_stores()})")
+        em.salu(f"s_waitcnt vmcnt({self.LPT + self.epilogue_stores()})")
         self.prefetch(self.qk_frags(0))
         em.salu("s_barrier")
         em.drain()

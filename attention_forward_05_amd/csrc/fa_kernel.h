@@ -44,7 +44,7 @@ struct LaunchArgs {
 int64_t work_items(int B, int Sq, int Hq);
 // Query tiles of 256 rows and key tiles of 64 keys.
 int query_tiles(int Sq);
-// Whether the eight-wave kernel (512-row query tiles, D = 128) runs: when its
+// Whether the eight-wave kernel (512-row query tiles, D = 64 or 128) runs: when its
 // items alone give each of the `cus` compute units one and every item with a
 // visible key spans more than 128 keys.
 bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus);

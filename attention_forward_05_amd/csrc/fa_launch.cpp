@@ -2,15 +2,16 @@
 // generators in attention_forward_05_amd/asm and embedded in this library as
 // a code object) and launches them.
 //
-// Two kernel shapes: four waves on 256-row query tiles (every D), and, for
-// D = 128 when the 512-row tiles alone give every compute unit an item (and
+// Two kernel shapes, for D = 64 and 128: four waves on 256-row query tiles,
+// and, when the 512-row tiles alone give every compute unit an item (and
 // each item with keys spans at least 3 key tiles), eight waves (two per
 // SIMD, alternating MFMA and softmax phases) on 512-row tiles, which halves
 // the K/V traffic into LDS per FLOP and streams K/V tiles across items.
-// When the 512-row items would leave compute units idle, the key ranges are
-// long and the caller passed a workspace, each item's keys are split into
-// 2..16 ranges whose partial results (in that workspace) a combine kernel
-// (fa_combine.hip) merges.  The library itself allocates no device memory.
+// For D = 128, when the 512-row items would leave compute units idle, the
+// key ranges are long and the caller passed a workspace, each item's keys
+// are split into 2..16 ranges whose partial results (in that workspace) a
+// combine kernel (fa_combine.hip) merges.  The library itself allocates no
+// device memory.
 //
 // The kernels are persistent: the grid has G = min(items, compute units)
 // workgroups, one per CU, and workgroup g takes item r*G + (g or G-1-g,
@@ -58,11 +59,12 @@ struct alignas(8) KernArgs {
 };
 static_assert(sizeof(KernArgs) == 96, "kernarg layout of the generated kernels");
 
-constexpr int kKernels = 8;
+constexpr int kKernels = 10;
 const char* kNames[kKernels] = {"fa_fwd_bf16_d128_gfx950",     "fa_fwd_bf16_d64_gfx950",
                                 "fa_fwd_f16_d128_gfx950",      "fa_fwd_f16_d64_gfx950",
                                 "fa_fwd_bf16_d128_x8_gfx950",  "fa_fwd_f16_d128_x8_gfx950",
-                                "fa_fwd_bf16_d128_x8s_gfx950", "fa_fwd_f16_d128_x8s_gfx950"};
+                                "fa_fwd_bf16_d128_x8s_gfx950", "fa_fwd_f16_d128_x8s_gfx950",
+                                "fa_fwd_bf16_d64_x8_gfx950",   "fa_fwd_f16_d64_x8_gfx950"};
 
 struct DeviceKernels {
   bool loaded = false;
@@ -132,7 +134,7 @@ int64_t min_item_tiles(int Sq, int Skv, int causal) {
 }
 
 bool use_eight_waves(int B, int Sq, int Skv, int Hq, int D, int causal, int cus) {
-  if (D != 128 || (((int64_t)Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
+  if ((D != 128 && D != 64) || (((int64_t)Sq + kBM8 - 1) / kBM8) * B * Hq < cus) return false;
   // The eight-wave kernel streams K/V tiles across consecutive items and
   // needs every item with a visible key to span at least 3 key tiles.
   const int64_t n = min_item_tiles(Sq, Skv, causal);
@@ -252,7 +254,7 @@ int launch(const LaunchArgs& a) {
     e = launch_kernel(dk, s, a.dtype == DType::kBF16 ? 6 : 7, true, l2s);
   } else {
     const bool x8 = p.kernel == kEightWave;
-    const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5)
+    const int variant = x8 ? (a.dtype == DType::kBF16 ? 4 : 5) + (a.D == 128 ? 0 : 4)
                            : (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
     e = launch_kernel(dk, a, variant, x8, 0);
   }

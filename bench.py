@@ -87,7 +87,7 @@ def kernel_code_hash(kernel: str):
     if shape == []:
         gen = Gen(dt, D)
     elif shape in (["x8"], ["x8s"]):
-        gen = Gen8(dt, shape == ["x8s"])
+        gen = Gen8(dt, shape == ["x8s"], D)
     else:
         return None
     text = gen.assemble_text()[0]
@@ -128,7 +128,7 @@ def launched_kernel(w: workloads.Workload, cus: int) -> str:
     if kern == fa.FA_KERNEL_FOUR_WAVE:
         return f"fa_fwd_{w.dtype}_d{w.D}_gfx950"
     if ranges == 1:
-        return f"fa_fwd_{w.dtype}_d128_x8_gfx950"
+        return f"fa_fwd_{w.dtype}_d{w.D}_x8_gfx950"
     return f"fa_fwd_{w.dtype}_d128_x8s_gfx950{merge}"
 
 

@@ -203,7 +203,7 @@ int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o
 /* Kernel shapes reported by fa_fwd_plan. */
 enum {
   FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD (D = 64, 128) */
-  FA_KERNEL_EIGHT_WAVE = 1, /* 512-row query tiles, two waves per SIMD (D = 128) */
+  FA_KERNEL_EIGHT_WAVE = 1, /* 512-row query tiles, two waves per SIMD (D = 64, 128) */
   FA_KERNEL_TILE_ROWS = 2,  /* 128-row blocks, four waves over the rows: D = 256,
                                and calls with Sq <= 64 whose q-heads of one
                                kv-head make more than 32 rows together */

@@ -109,7 +109,7 @@ def test_python_wrapper_raises_on_bad_tensors(lib):
 
 # fa_fwd_plan: the kernel-shape rule on the host, with the expected shapes
 # worked out by hand from the rule stated in include/fa.h and the launcher:
-# eight waves (512-row items) when B*Hq*ceil(Sq/512) >= compute units and the
+# eight waves (512-row items, D = 64 or 128) when B*Hq*ceil(Sq/512) >= compute units and the
 # shortest item with a visible key spans >= 3 key tiles of 64; else, with
 # D = 128, a workspace and fewer items than compute units, the fewest
 # power-of-two key ranges (<= 16) that cover the compute units, reduced until
@@ -129,7 +129,9 @@ PLAN_CASES = [
     (1, 2048, 8192, 16, 128, 1, 256, 1, 4),    # 64 items, 128 four-wave ones; 4 ranges of >= 26 tiles
     (2, 700, 5000, 16, 128, 1, 256, 1, 4),     # 64 items; shortest 76 tiles
     (1, 3000, 2600, 16, 128, 1, 256, 0, 1),    # first keyed tile has 2 key tiles
-    (1, 512, 8192, 4, 64, 0, 256, 0, 1),       # D = 64: four waves, never split
+    (1, 512, 8192, 4, 64, 0, 256, 0, 1),       # D = 64: 4 items, four waves, never split
+    (1, 4096, 4096, 32, 64, 1, 256, 1, 1),     # D = 64: 256 items, eight waves
+    (1, 4096, 4096, 16, 64, 1, 256, 0, 1),     # D = 64: 128 items, four waves
     (1, 512, 8192, 4, 128, 0, 4, 1, 1),        # 4 compute units: 4 items fill them
     (1, 200, 100, 256, 128, 1, 256, 0, 1),     # 256 items of 2 key tiles: four waves
 ]
