@@ -455,6 +455,19 @@ def test_named_workload(fa, w, parity_figures):
     check(o, lse, o_ref, lse_ref, w.name, figures=parity_figures)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("w", workloads.HEAD_DIM_WORKLOADS,
+                         ids=[w.name for w in workloads.HEAD_DIM_WORKLOADS])
+def test_head_dim_workload(fa, w, parity_figures):
+    """The head-dimension workloads (D = 64 on the four-wave and the
+    eight-wave kernel, D = 256 on the tile kernel) at full size, every
+    output element against the oracle."""
+    q, k, v = workloads.workload_inputs(w)
+    o, lse = run_gpu(fa, q, k, v, w.causal, w.scale)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale)
+    check(o, lse, o_ref, lse_ref, w.name, figures=parity_figures)
+
+
 @pytest.mark.parametrize("w", workloads.WORKLOADS[2:], ids=[w.name for w in workloads.WORKLOADS[2:]])
 def test_named_workload_v_ones_property(fa, w):
     """V = 1 makes every output row 1 (the weights of a row sum to one); this

@@ -83,6 +83,9 @@ DECODE_WORKLOADS = [
 HEAD_DIM_WORKLOADS = [
     Workload("causal_b1_h16_s4096_d64_bf16", 1, 16, 16, 4096, 4096, 64, True, "bf16", 51),
     Workload("causal_b1_h16_s4096_d256_bf16", 1, 16, 16, 4096, 4096, 256, True, "bf16", 52),
+    # the headline shape at head dimension 64 (enough 512-row items for the
+    # eight-wave kernel)
+    Workload("causal_b2_h32_s4096_d64_bf16", 2, 32, 32, 4096, 4096, 64, True, "bf16", 53),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + SPLIT_WORKLOADS + DECODE_WORKLOADS + HEAD_DIM_WORKLOADS}
 
