@@ -204,9 +204,12 @@ int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o
 enum {
   FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD (D = 64, 128) */
   FA_KERNEL_EIGHT_WAVE = 1, /* 512-row query tiles, two waves per SIMD (D = 64, 128) */
-  FA_KERNEL_TILE_ROWS = 2,  /* 128-row blocks, four waves over the rows: D = 256,
-                               and calls with Sq <= 64 whose q-heads of one
-                               kv-head make more than 32 rows together */
+  FA_KERNEL_TILE_ROWS = 2,  /* 128-row blocks, four waves over the rows: D = 256;
+                               calls with Sq <= 64 whose q-heads of one
+                               kv-head make more than 32 rows together; and
+                               causal D = 64 calls without enough 512-row
+                               tiles for the eight-wave kernel whose 256-row
+                               tiles fit in one round on the compute units */
   FA_KERNEL_TILE_KEYS = 3   /* one 32-row block, four waves over the keys: calls
                                with Sq <= 64 and Sq * Hq / Hkv <= 32 (decode) */
 };

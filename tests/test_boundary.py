@@ -131,7 +131,9 @@ PLAN_CASES = [
     (1, 3000, 2600, 16, 128, 1, 256, 0, 1),    # first keyed tile has 2 key tiles
     (1, 512, 8192, 4, 64, 0, 256, 0, 1),       # D = 64: 4 items, four waves, never split
     (1, 4096, 4096, 32, 64, 1, 256, 1, 1),     # D = 64: 256 items, eight waves
-    (1, 4096, 4096, 16, 64, 1, 256, 0, 1),     # D = 64: 128 items, four waves
+    (1, 4096, 4096, 16, 64, 1, 256, 2, 1),     # D = 64 causal: one round of 256-row items: tile kernel
+    (1, 4096, 4096, 16, 64, 0, 256, 0, 1),     # D = 64 non-causal: four waves
+    (1, 4096, 4096, 24, 64, 1, 256, 0, 1),     # D = 64 causal, 384 items of 256 rows: four waves
     (1, 512, 8192, 4, 128, 0, 4, 1, 1),        # 4 compute units: 4 items fill them
     (1, 200, 100, 256, 128, 1, 256, 0, 1),     # 256 items of 2 key tiles: four waves
 ]
