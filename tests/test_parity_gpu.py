@@ -207,6 +207,30 @@ def test_eight_wave_shapes(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, D):
     full_case(fa, B, Sq, Skv, Hq, Hkv, D, causal, dtype, seed=Sq + 3 * Skv + Hkv + D)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_eight_wave_special_arguments(fa, D):
+    """The eight-wave kernel with scale 0 (O = mean of the visible V rows,
+    LSE = ln(count)), without LSE (same O bits), and twice in a row (same
+    bits), on a bottom-right causal shape with 256 items."""
+    B, Sq, Skv, Hq, Hkv = 1, 512, 700, 256, 64
+    if compute_units() == 256:
+        assert plan(fa, B, Sq, Skv, Hq, Hkv, D, True, False)[0] == fa.FA_KERNEL_EIGHT_WAVE
+    q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, D, "bf16", 61 + D)
+    o, lse = run_gpu(fa, q, k, v, True, 0.0)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, True, 0.0)
+    check(o, lse, o_ref, lse_ref, f"scale 0, D {D}")
+    n = np.arange(Sq) + (Skv - Sq) + 1
+    np.testing.assert_allclose(lse[0, 5], np.log(n), atol=1e-4)
+    scale = 1.0 / math.sqrt(D)
+    o1, l1 = run_gpu(fa, q, k, v, True, scale)
+    o2, l2 = run_gpu(fa, q, k, v, True, scale, with_lse=False)
+    o3, l3 = run_gpu(fa, q, k, v, True, scale)
+    assert l2 is None
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(o1, o3)
+    np.testing.assert_array_equal(l1, l3)
+
+
 def rounding_bound(o, o_ref, v, dtype):
     """Elementwise bound of the two roundings the kernel does (P and O to the
     input dtype, unit roundoff u = 2^-8 for bf16, 2^-11 for fp16): P rounded
@@ -218,15 +242,16 @@ def rounding_bound(o, o_ref, v, dtype):
     return float((np.abs(o - o_ref) / bound).max())
 
 
-def test_eight_wave_slow_path_bf16(fa):
+@pytest.mark.parametrize("D", [128, 64])
+def test_eight_wave_slow_path_bf16(fa, D):
     """bf16 on the eight-wave kernel with 1% of the key rows scaled by 8: the
     reference max moves (the slow path) in bf16 as well.  The softmax is
     nearly one-hot here, so |O| reaches |V| (about 4.5) and bf16 rounding of
     O alone can exceed the 2e-2 bar of the N(0,1) workloads: the bar is the
     rounding bound instead, with the mean and LSE bars unchanged."""
     if compute_units() == 256:
-        assert plan(fa, 1, 256, 1024, 256, 8, 128, True, False)[0] == fa.FA_KERNEL_EIGHT_WAVE
-    B, Sq, Skv, Hq, Hkv, D = 1, 256, 1024, 256, 8, 128
+        assert plan(fa, 1, 256, 1024, 256, 8, D, True, False)[0] == fa.FA_KERNEL_EIGHT_WAVE
+    B, Sq, Skv, Hq, Hkv = 1, 256, 1024, 256, 8
     q, k, v = workloads.make_inputs(B, Sq, Skv, Hq, Hkv, D, "bf16", 24, k_row_boost_frac=0.01)
     scale = 1.0 / math.sqrt(D)
     o, lse = run_gpu(fa, q, k, v, True, scale)
