@@ -181,7 +181,7 @@ def attention_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, stream=None
     """Convenience wrapper: gradients (dq, dk, dv) of the forward on torch
     tensors (q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D], o and dout like q, lse
     [B,Hq,Sq] fp32 from the forward), allocated with torch together with the
-    4*B*Hq*Sq-byte workspace.  Raises FAError on a non-zero status."""
+    8*B*Hq*Sq-byte workspace.  Raises FAError on a non-zero status."""
     import torch
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
@@ -195,7 +195,7 @@ def attention_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, stream=None
         if not t.is_contiguous() or not t.is_cuda:
             raise FAError(FA_ERR_INVALID, f"attention_bwd: {name} must be a contiguous GPU tensor")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(4 * B * Hq * Sq, 16), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(max(8 * B * Hq * Sq, 16), dtype=torch.uint8, device=q.device)
     if isinstance(stream, torch.cuda.Stream):
         ws.record_stream(stream)
     st = fa_bwd(dt, q, k, v, o, lse, dout, dq, dk, dv, B, Sq, Skv, Hq, Hkv, D, int(bool(causal)),

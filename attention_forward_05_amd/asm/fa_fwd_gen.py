@@ -1056,17 +1056,19 @@ def metadata(kernels) -> str:
             f"  - .agpr_count: {k['na']}",
             "    .args:",
         ]
-        for off, kind, access in [(0, "global_buffer", "read_only"), (8, "global_buffer", "read_only"),
-                                  (16, "global_buffer", "read_only"), (24, "global_buffer", "write_only"),
-                                  (32, "global_buffer", "write_only")]:
+        # pointer arguments (offset, access), then 4-byte values up to the end
+        ptrs = k.get("ptrs", [(0, "read_only"), (8, "read_only"), (16, "read_only"),
+                              (24, "write_only"), (32, "write_only")])
+        size = k.get("kernarg", KERNARG_BYTES)
+        for off, access in ptrs:
             lines += [f"      - .actual_access: {access}", "        .address_space: global",
-                      f"        .offset: {off}", "        .size: 8", f"        .value_kind: {kind}"]
-        for off in range(40, KERNARG_BYTES, 4):
+                      f"        .offset: {off}", "        .size: 8", "        .value_kind: global_buffer"]
+        for off in range(ptrs[-1][0] + 8, size, 4):
             lines += [f"      - .offset: {off}", "        .size: 4", "        .value_kind: by_value"]
         lines += [
             f"    .group_segment_fixed_size: {k['lds']}",
             "    .kernarg_segment_align: 8",
-            f"    .kernarg_segment_size: {KERNARG_BYTES}",
+            f"    .kernarg_segment_size: {size}",
             f"    .max_flat_workgroup_size: {k.get('wg', 256)}",
             f"    .name: {k['name']}",
             "    .private_segment_fixed_size: 0",
@@ -1090,7 +1092,8 @@ VARIANTS = [("bf16", 128), ("bf16", 64), ("f16", 128), ("f16", 64)]
 def generate_all() -> str:
     """Every kernel of the library: the four-wave variants, then the
     eight-wave D = 128 variants (fa_fwd_x8), whole key ranges and split,
-    and the eight-wave D = 64 variants on whole key ranges."""
+    the eight-wave D = 64 variants on whole key ranges, and the backward's
+    dK/dV and dQ kernels (fa_bwd_gen)."""
     from .fa_fwd_x8 import Gen8
     texts, metas = [], []
     for dt, D in VARIANTS:
@@ -1105,6 +1108,11 @@ def generate_all() -> str:
             metas.append(info)
     for dt in ("bf16", "f16"):
         txt, info = Gen8(dt, False, 64).assemble_text()
+        texts.append(txt)
+        metas.append(info)
+    from .fa_bwd_gen import GenBwd, VARIANTS as BWD_VARIANTS
+    for kind, dt, D in BWD_VARIANTS:
+        txt, info = GenBwd(kind, dt, D).assemble_text()
         texts.append(txt)
         metas.append(info)
     return "".join(texts) + metadata(metas)

@@ -169,13 +169,17 @@ int bwd(fa::DType dtype, const void* q, const void* k, const void* v, const void
       if (overlap(outs[x], out_bytes[x], outs[y], out_bytes[y])) return FA_ERR_INVALID;
   }
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  // the workspace holds delta, one fp32 per query row: [B][Hq][Sq]
-  if (!ws || ws_bytes < lseb) return FA_ERR_WORKSPACE;
+  // the gradient kernels address one batch slice of k / v with 32 bits
+  if ((uint64_t)Skv * (uint64_t)Hkv * (uint64_t)D * 2u >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
+  // the workspace holds two fp32 per query row, [2][B][Hq][Sq]: LSE in log2
+  // units and delta
+  const uint64_t wsb = 2 * lseb;
+  if (!ws || ws_bytes < wsb) return FA_ERR_WORKSPACE;
   if (!aligned16(ws)) return FA_ERR_INVALID;
   for (int y = 0; y < 6; ++y)
-    if (overlap(ws, lseb, ins[y], in_bytes[y])) return FA_ERR_INVALID;
+    if (overlap(ws, wsb, ins[y], in_bytes[y])) return FA_ERR_INVALID;
   for (int x = 0; x < 3; ++x)
-    if (overlap(ws, lseb, outs[x], out_bytes[x])) return FA_ERR_INVALID;
+    if (overlap(ws, wsb, outs[x], out_bytes[x])) return FA_ERR_INVALID;
 
   fa::BwdLaunchArgs b;
   b.dtype = dtype;
@@ -188,7 +192,7 @@ int bwd(fa::DType dtype, const void* q, const void* k, const void* v, const void
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
-  b.delta = static_cast<float*>(ws);
+  b.ws = static_cast<float*>(ws);
   b.B = B;
   b.Sq = Sq;
   b.Skv = Skv;
@@ -199,7 +203,7 @@ int bwd(fa::DType dtype, const void* q, const void* k, const void* v, const void
   b.scale = scale;
   b.c = a.c;
   b.stream = stream;
-  return fa::launch_bwd(b) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa::launch_bwd(b);
 }
 
 }  // namespace

@@ -93,14 +93,17 @@ struct BwdLaunchArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: [B][Hq][Sq] fp32
+  float* ws;  // workspace: l2 = LSE * log2(e), then delta, each [B][Hq][Sq] fp32
   int B, Sq, Skv, Hq, Hkv, D, causal;
   float scale;
   float c;  // scale * log2(e), clamped to >= FLT_MIN
   hipStream_t stream;
 };
-// Enqueue the three backward kernels (delta, dK/dV, dQ) on a.stream.
-hipError_t launch_bwd(const BwdLaunchArgs& a);
+// Enqueue the backward: the delta kernel (fa_bwd.hip), then the dK/dV and
+// dQ kernels (generated, in the code object).  Returns an fa_status.
+int launch_bwd(const BwdLaunchArgs& a);
+// The delta kernel alone: l2 and delta of every query row into a.ws.
+hipError_t launch_bwd_delta(const BwdLaunchArgs& a);
 
 // Argument checks shared by every forward entry point (no HIP call); on
 // FA_OK fills `a` (everything but ws / ws_bytes).

@@ -59,12 +59,39 @@ struct alignas(8) KernArgs {
 };
 static_assert(sizeof(KernArgs) == 96, "kernarg layout of the generated kernels");
 
-constexpr int kKernels = 10;
+constexpr int kKernels = 18;
 const char* kNames[kKernels] = {"fa_fwd_bf16_d128_gfx950",     "fa_fwd_bf16_d64_gfx950",
                                 "fa_fwd_f16_d128_gfx950",      "fa_fwd_f16_d64_gfx950",
                                 "fa_fwd_bf16_d128_x8_gfx950",  "fa_fwd_f16_d128_x8_gfx950",
                                 "fa_fwd_bf16_d128_x8s_gfx950", "fa_fwd_f16_d128_x8s_gfx950",
-                                "fa_fwd_bf16_d64_x8_gfx950",   "fa_fwd_f16_d64_x8_gfx950"};
+                                "fa_fwd_bf16_d64_x8_gfx950",   "fa_fwd_f16_d64_x8_gfx950",
+                                // backward: dK/dV then dQ, each (bf16, f16) x (D 128, 64)
+                                "fa_bwd_dkv_bf16_d128_gfx950", "fa_bwd_dkv_bf16_d64_gfx950",
+                                "fa_bwd_dkv_f16_d128_gfx950",  "fa_bwd_dkv_f16_d64_gfx950",
+                                "fa_bwd_dq_bf16_d128_gfx950",  "fa_bwd_dq_bf16_d64_gfx950",
+                                "fa_bwd_dq_f16_d128_gfx950",   "fa_bwd_dq_f16_d64_gfx950"};
+constexpr int kBwdFirst = 10;
+
+// Arguments of the generated backward kernels (fa_bwd_gen.py).
+struct alignas(8) BwdKernArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* l2;     // LSE * log2(e) per query row
+  const float* delta;  // rowsum(O * dO) per query row
+  void* dq;
+  void* dk;
+  void* dv;
+  int32_t B, Sq, Skv, Hq, Hkv, causal;
+  float c;       // scale * log2(e)
+  float scale;
+  uint32_t nqb;     // dQ: 128-row query blocks
+  uint32_t gmagic;  // hk = (hq * gmagic) >> 20
+  uint32_t group;   // Hq / Hkv
+  uint32_t pad[3];
+};
+static_assert(sizeof(BwdKernArgs) == 128, "kernarg layout of the generated backward kernels");
 
 struct DeviceKernels {
   bool loaded = false;
@@ -100,6 +127,50 @@ hipError_t kernels_for_current_device(DeviceKernels** out) {
 }
 
 }  // namespace
+
+int launch_bwd(const BwdLaunchArgs& a) {
+  DeviceKernels* dk = nullptr;
+  if (kernels_for_current_device(&dk) != hipSuccess) return FA_ERR_HIP;
+  uint32_t magic = 0;
+  if (!group_magic(a.Hq, a.Hkv, &magic)) return FA_ERR_UNSUPPORTED;
+  if (launch_bwd_delta(a) != hipSuccess) return FA_ERR_HIP;
+  const size_t rows = (size_t)a.B * a.Hq * a.Sq;
+  BwdKernArgs k;
+  memset(&k, 0, sizeof(k));
+  k.q = a.q;
+  k.k = a.k;
+  k.v = a.v;
+  k.dout = a.dout;
+  k.l2 = a.ws;
+  k.delta = a.ws + rows;
+  k.dq = a.dq;
+  k.dk = a.dk;
+  k.dv = a.dv;
+  k.B = a.B;
+  k.Sq = a.Sq;
+  k.Skv = a.Skv;
+  k.Hq = a.Hq;
+  k.Hkv = a.Hkv;
+  k.causal = a.causal;
+  k.c = a.c;
+  k.scale = a.scale;
+  k.nqb = (uint32_t)((a.Sq + 127) / 128);
+  k.gmagic = magic;
+  k.group = (uint32_t)(a.Hq / a.Hkv);
+  const int var = (a.dtype == DType::kBF16 ? 0 : 2) + (a.D == 128 ? 0 : 1);
+  size_t size = sizeof(k);
+  void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &k, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
+                 HIP_LAUNCH_PARAM_END};
+  // dK/dV: a workgroup per (128-key block, kv-head, batch); dQ: per (128-row
+  // query block, last first; q-head; batch)
+  hipError_t e = hipModuleLaunchKernel(dk->fn[kBwdFirst + var], (unsigned)((a.Skv + 127) / 128),
+                                       (unsigned)a.Hkv, (unsigned)a.B, 256, 1, 1, 0, a.stream,
+                                       nullptr, cfg);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  e = hipModuleLaunchKernel(dk->fn[kBwdFirst + 4 + var], k.nqb, (unsigned)a.Hq, (unsigned)a.B,
+                            256, 1, 1, 0, a.stream, nullptr, cfg);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 
 bool group_magic(int Hq, int Hkv, uint32_t* magic) {
   const uint32_t g = (uint32_t)(Hq / Hkv);

@@ -231,8 +231,8 @@ def counter_summary(csv_path: str, w: workloads.Workload, which: str = "fwd"):
     durations = {}
     for row in csv.DictReader(open(csv_path, newline="")):
         name = row["Kernel_Name"]
-        if not (name.startswith("fa_fwd_") or "tile_kernel" in name or "combine_kernel" in name
-                or "bwd_" in name):
+        if not (name.startswith(("fa_fwd_", "fa_bwd_")) or "tile_kernel" in name
+                or "combine_kernel" in name or "bwd_" in name):
             continue
         did = row.get("Dispatch_Id", "")
         cname, val = row["Counter_Name"], float(row["Counter_Value"])
@@ -454,12 +454,12 @@ def main():
 
     if args.which == "bwd":
         # the forward's O and LSE, an upstream gradient, the gradients and
-        # the delta workspace, all before the timed region
+        # the workspace (l2 and delta per query row), all before the timed region
         step()
         gen = torch.Generator().manual_seed(w.seed + 1000)
         dod = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(q.dtype).to(dev)
         dqd, dkd, dvd = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        bws = torch.empty(max(4 * w.B * w.Hq * w.Sq, 16), dtype=torch.uint8, device=dev)
+        bws = torch.empty(max(8 * w.B * w.Hq * w.Sq, 16), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
         def step():  # noqa: F811 -- the timed step is the backward pass
@@ -502,7 +502,7 @@ def main():
     achieved = flops / (launch_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kernel = launched_kernel(w, cus) if args.which == "fwd" else \
-        "bwd_delta_kernel + bwd_dkv_kernel + bwd_dq_kernel"
+        f"bwd_delta_kernel + fa_bwd_dkv_{w.dtype}_d{w.D}_gfx950 + fa_bwd_dq_{w.dtype}_d{w.D}_gfx950"
     dev_peak = device_peak(w.dtype)
     traffic = measured_traffic(w.name, kernel) if args.which == "fwd" else None
     log(f"[bench] {w.name} ({args.which}): {ms_per_step * 1e3:.1f} us/step, {value:.1f} TFLOP/s "

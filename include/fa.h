@@ -184,16 +184,17 @@ int fa_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, void*
  *   dq          : written, [B,Sq,Hq,D]
  *   dk, dv      : written, [B,Skv,Hkv,D]
  *   B .. scale  : as in fa_fwd; D = 64 or 128
- *   workspace   : device memory of at least 4*B*Hq*Sq bytes, 16-byte aligned
- *                 (one fp32 delta per query row); contents undefined after
+ *   workspace   : device memory of at least 8*B*Hq*Sq bytes, 16-byte aligned
+ *                 (two fp32 per query row: LSE in log2 units and delta);
+ *                 contents undefined after
  *   stream      : HIP stream to enqueue on
  *
  * dq, dk, dv and the workspace must overlap neither each other nor any
  * input.  Asynchronous like fa_fwd; the library allocates nothing.  Returns
  * FA_OK, FA_ERR_INVALID (as fa_fwd, plus NULL o/lse/dout/dk/dv and the
- * overlaps above), FA_ERR_UNSUPPORTED (D not 64 or 128, and fa_fwd's
- * limits), FA_ERR_WORKSPACE (workspace NULL or smaller than 4*B*Hq*Sq
- * bytes) or FA_ERR_HIP.
+ * overlaps above), FA_ERR_UNSUPPORTED (D not 64 or 128, one batch slice of
+ * k or v of 2 GiB or more, and fa_fwd's limits), FA_ERR_WORKSPACE
+ * (workspace NULL or smaller than 8*B*Hq*Sq bytes) or FA_ERR_HIP.
  */
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,

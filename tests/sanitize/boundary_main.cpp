@@ -22,7 +22,7 @@ hipError_t launch_combine(DType, const float*, const float*, void*, float*, int,
   return hipErrorInvalidValue;
 }
 hipError_t launch_tile(const LaunchArgs&, bool, bool, int, float*, float*) { return hipErrorInvalidValue; }
-hipError_t launch_bwd(const BwdLaunchArgs&) { return hipErrorInvalidValue; }
+hipError_t launch_bwd_delta(const BwdLaunchArgs&) { return hipErrorInvalidValue; }
 }  // namespace fa
 
 static int failures = 0;
@@ -74,7 +74,7 @@ int main() {
   // backward
   EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 128, 1, 0.1f, nullptr, 0, 0),
          FA_ERR_WORKSPACE);
-  EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 128, 1, 0.1f, W, 4 * 4 * 128 - 1, 0),
+  EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 128, 1, 0.1f, W, 8 * 4 * 128 - 1, 0),
          FA_ERR_WORKSPACE);
   EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DK, 1, 128, 128, 4, 2, 128, 1, 0.1f, W, 1 << 20, 0),
          FA_ERR_INVALID);
@@ -84,6 +84,9 @@ int main() {
          FA_ERR_UNSUPPORTED);
   EXPECT(fa_bwd(3, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 128, 1, 0.1f, W, 1 << 20, 0),
          FA_ERR_INVALID);
+  // one batch slice of k (2^20 keys x 8 heads x 128 dims x 2 bytes) at 2 GiB
+  EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 1 << 20, 8, 8, 128, 0, 0.1f, W, 1 << 20, 0),
+         FA_ERR_UNSUPPORTED);
 
   // the plan over a sweep of sizes (host only)
   int kern, ranges;
