@@ -41,8 +41,6 @@ from .regs import Alloc, Emitter, Op
 from .fa_fwd_gen import f32_hex
 
 NST = 4             # LDS stages (tiles) in flight
-RING = 8            # operand buffers
-LOOK = 4            # MFMAs whose operand reads are issued ahead
 KERNARG_BYTES = 128
 LOG2E = 1.4426950408889634
 
@@ -56,6 +54,16 @@ class Item:
 
     def __init__(self, reads, mfma):
         self.reads, self.mfma = reads, mfma
+
+
+class Block4:
+    """Four consecutive registers of a larger block."""
+
+    def __init__(self, blk, off):
+        self.blk, self.off = blk, off
+
+    def r(self, i=0, n=1):
+        return self.blk.r(self.off + i, n)
 
 
 class GenBwd:
@@ -74,11 +82,21 @@ class GenBwd:
         self.REG_B = NST * self.TILE            # LDS: second tensor's stages
         self.REG_L = 2 * NST * self.TILE        # LDS: l2 stages, then delta stages (dK/dV)
         self.LDS = self.REG_L + (2 * NST * 256 if self.dkv else 0)
+        # operand buffers (accumulator registers) and the MFMAs whose reads are
+        # issued ahead; at most 15 LDS reads are in flight (two per Z MFMA)
+        self.RING = 16 if D == 128 else 8
+        self.LOOK = 7 if D == 128 else 5
+        # MFMAs of a step's first block whose reads the previous step issues
+        self.PRE = min(self.LOOK, 2 * self.ND * (2 if self.dkv else 1))
         self.mfma_op = f"v_mfma_f32_32x32x16_{dtype}"
         self.cvt_op = "v_cvt_pk_bf16_f32" if dtype == "bf16" else "v_cvt_pk_f16_f32"
         self.name = kernel_name(kind, dtype, D)
         self.em = Emitter()
         self._lab = 0
+        # workgroup ids: the grid is (heads, batch, blocks), so that the
+        # blocks with the most work (dK/dV: the first keys; dQ: the last
+        # rows) are dispatched first over every head
+        self.g_head, self.g_b, self.g_blk = "s2", "s3", "s4"
 
     def lab(self, tag):
         self._lab += 1
@@ -98,7 +116,6 @@ class GenBwd:
         if self.dkv:
             r["v_L"] = [V.take(f"L{p}", 16, 4) for p in range(2)]     # l2 of the half's rows
             r["v_Dl"] = [V.take(f"Dl{p}", 16, 4) for p in range(2)]   # delta of the half's rows
-        r["v_R"] = [V.take(f"R{i}", 4, 4) for i in range(RING)]
         r["v_xa"] = V.take("xa", self.NQ)        # row reads of the first tensor (k-step t)
         r["v_xb"] = V.take("xb", self.NQ)        # row reads of the second tensor
         r["v_za"] = V.take("za", 2 * self.ND)    # transposing reads, first tensor (db, lo/hi)
@@ -122,6 +139,7 @@ class GenBwd:
             r["a_acc2"] = [A.take(f"g2{d}", 16, 4) for d in range(self.ND)]   # dV
         r["a_f1"] = [A.take(f"f1{t}", 4, 4) for t in range(self.NQ)]   # K or Q rows
         r["a_f2"] = [A.take(f"f2{t}", 4, 4) for t in range(self.NQ)]   # V or dO rows
+        r["a_R"] = [A.take(f"R{i}", 4, 4) for i in range(self.RING)]     # operand ring
         self.nagpr = (A.next + 3) // 4 * 4
         t = S.take
         r["s_w"] = t("w", 1)
@@ -196,13 +214,13 @@ class GenBwd:
             self.setup_dq()
 
     def setup_dkv(self):
-        """Workgroup (key block s2, kv-head s3, batch s4): the keys 128*s2 ..;
+        """Workgroup (key block kb, kv-head hk, batch b): the keys 128*kb ..;
         steps over (q-head of the group, 64-row query block), query blocks
         innermost, from the first block with a row that sees a key."""
         em, x, t = self.em, self.s_x, self.v_t
         D2 = 2 * self.D
         em.salu(f"s_mul_i32 {self.s_rowb}, s29, {D2}")                # Q / dO row stride
-        em.salu(f"s_lshl_b32 {x[0]}, s2, 7")                          # k0
+        em.salu(f"s_lshl_b32 {x[0]}, {self.g_blk}, 7")                          # k0
         em.salu(f"s_sub_i32 {x[1]}, {x[0]}, {self.s_off}")
         em.salu(f"s_max_i32 {x[1]}, {x[1]}, 0")
         em.salu(f"s_lshr_b32 {x[1]}, {x[1]}, 6")
@@ -215,9 +233,9 @@ class GenBwd:
         em.salu(f"s_mul_i32 {self.s_n}, {x[2]}, s36")
         em.salu(f"s_lshl_b32 {x[3]}, {self.s_w}, 5")
         em.salu(f"s_add_u32 {self.s_lim}, {x[0]}, {x[3]}")           # the wave's first key
-        em.salu(f"s_mul_i32 {x[5]}, s3, s36")                         # hq0 = hk * g
+        em.salu(f"s_mul_i32 {x[5]}, {self.g_head}, s36")                         # hq0 = hk * g
         # l2 (wave 0) or delta (wave 1) rows of (b, hq0): ((b*Hq + hq0) * Sq) * 4
-        em.salu(f"s_mul_i32 {x[4]}, s4, s29")
+        em.salu(f"s_mul_i32 {x[4]}, {self.g_b}, s29")
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {x[5]}")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s27")
         self.mul64(x[6], x[7], x[4], 4)
@@ -227,7 +245,7 @@ class GenBwd:
         em.salu(f"s_add_u32 {self.s_bl.r(0)}, {x[0]}, {x[6]}")
         em.salu(f"s_addc_u32 {self.s_bl.r(1)}, {x[1]}, {x[7]}")
         # Q / dO of (b, hq0): ((b*Sq)*Hq + hq0) * 2D
-        em.salu(f"s_mul_i32 {x[4]}, s4, s27")
+        em.salu(f"s_mul_i32 {x[4]}, {self.g_b}, s27")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s29")
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {x[5]}")
         self.mul64(x[6], x[7], x[4], D2)
@@ -236,12 +254,12 @@ class GenBwd:
             em.salu(f"s_addc_u32 {base.r(1)}, s{ptr + 1}, {x[7]}")
         # K / V / dK / dV of (b, hk): ((b*Skv)*Hkv + hk) * 2D, ranges up to
         # the tensor's end (a key past Skv is out of range)
-        em.salu(f"s_mul_i32 {x[4]}, s4, s28")
+        em.salu(f"s_mul_i32 {x[4]}, {self.g_b}, s28")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s30")
-        em.salu(f"s_add_u32 {x[4]}, {x[4]}, s3")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.g_head}")
         self.mul64(x[6], x[7], x[4], D2)
         em.salu(f"s_mul_i32 {x[5]}, s28, s30")
-        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, s3")
+        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, {self.g_head}")
         em.salu(f"s_mul_i32 {x[5]}, {x[5]}, {D2}")
         for rs, ptr in ((self.s_ra, 10), (self.s_rb, 12), (self.s_ro1, 22), (self.s_ro2, 24)):
             em.salu(f"s_add_u32 {x[0]}, s{ptr}, {x[6]}")
@@ -269,15 +287,15 @@ class GenBwd:
                                 f"offset:{32 * tt}", str(frags[tt]), src=[t.r(2)])
 
     def setup_dq(self):
-        """Workgroup (s2: query block counted from the last, q-head s3, batch
-        s4): the rows 128*qb ..; steps over the 64-key tiles they see."""
+        """Workgroup (query block counted from the last, q-head hq, batch b):
+        the rows 128*qb ..; steps over the 64-key tiles they see."""
         em, x, t = self.em, self.s_x, self.v_t
         D2 = 2 * self.D
         em.salu(f"s_mul_i32 {self.s_rowb}, s30, {D2}")                # K / V row stride
-        em.salu(f"s_mul_i32 {self.s_hk}, s3, s35")
+        em.salu(f"s_mul_i32 {self.s_hk}, {self.g_head}, s35")
         em.salu(f"s_lshr_b32 {self.s_hk}, {self.s_hk}, 20")           # hk = (hq * magic) >> 20
         em.salu(f"s_sub_u32 {x[0]}, s34, 1")
-        em.salu(f"s_sub_u32 {x[0]}, {x[0]}, s2")
+        em.salu(f"s_sub_u32 {x[0]}, {x[0]}, {self.g_blk}")
         em.salu(f"s_lshl_b32 {x[0]}, {x[0]}, 7")                      # the block's first row
         # causal: a row i sees the keys k <= i + off; offe = off, else Skv
         # (every key)
@@ -307,8 +325,8 @@ class GenBwd:
         em.valu(f"v_sub_u32 {self.v_col}, {t.r(2)}, {t.r(3)}", dst=[str(self.v_col)], src=[t.r(2), t.r(3)])
         # l2 and delta of (b, hq, qi); a row past Sq reads 0 (its Q and dO
         # are 0 too, so its products are 0)
-        em.salu(f"s_mul_i32 {x[4]}, s4, s29")
-        em.salu(f"s_add_u32 {x[4]}, {x[4]}, s3")
+        em.salu(f"s_mul_i32 {x[4]}, {self.g_b}, s29")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.g_head}")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s27")
         self.mul64(x[6], x[7], x[4], 4)
         em.salu(f"s_lshl_b32 {x[5]}, s27, 2")
@@ -319,13 +337,13 @@ class GenBwd:
             self.set_desc(rs, x[0], x[1], x[5])
             em.vmem_load_to(f"buffer_load_dword {dst}, {t.r(4)}, {rs}, 0 offen", str(dst), src=[t.r(4)])
         # Q / dO rows of (b, qi, hq): base ((b*Sq)*Hq + hq) * 2D, lane qi*rowq + 16h
-        em.salu(f"s_mul_i32 {x[4]}, s4, s27")
+        em.salu(f"s_mul_i32 {x[4]}, {self.g_b}, s27")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s29")
-        em.salu(f"s_add_u32 {x[4]}, {x[4]}, s3")
+        em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.g_head}")
         self.mul64(x[6], x[7], x[4], D2)
         em.salu(f"s_mul_i32 {x[2]}, s29, {D2}")                       # Q row stride
         em.salu(f"s_mul_i32 {x[5]}, s27, s29")
-        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, s3")
+        em.salu(f"s_sub_u32 {x[5]}, {x[5]}, {self.g_head}")
         em.salu(f"s_mul_i32 {x[5]}, {x[5]}, {D2}")                    # up to the end of q
         em.valu(f"v_mul_lo_u32 {t.r(5)}, {t.r(0)}, {x[2]}", dst=[t.r(5)], src=[t.r(0)])
         em.valu(f"v_lshl_add_u32 {t.r(6)}, {t.r(1)}, 4, {t.r(5)}", dst=[t.r(6)], src=[t.r(1), t.r(5)])
@@ -341,7 +359,7 @@ class GenBwd:
         em.salu(f"s_addc_u32 {x[1]}, s21, {x[7]}")
         self.set_desc(self.s_ro1, x[0], x[1], x[5])                   # dQ stores
         # K / V of (b, hk)
-        em.salu(f"s_mul_i32 {x[4]}, s4, s28")
+        em.salu(f"s_mul_i32 {x[4]}, {self.g_b}, s28")
         em.salu(f"s_mul_i32 {x[4]}, {x[4]}, s30")
         em.salu(f"s_add_u32 {x[4]}, {x[4]}, {self.s_hk}")
         self.mul64(x[6], x[7], x[4], D2)
@@ -516,11 +534,11 @@ class GenBwd:
                 dst = str((self.v_S if which == 0 else self.v_P)[hb])
 
                 def reads(buf, addr=addr):
-                    R = self.v_R[buf]
+                    R = self.a_R[buf]
                     em.ds_read(f"ds_read_b128 {R}, {addr} offset:{32 * hb * self.ROW}", str(R), addr)
 
                 def mfma(buf, dst=dst, frag=frag, first=(tt == 0)):
-                    em.mfma(self.mfma_op, dst, str(self.v_R[buf]), str(frag), "0" if first else dst)
+                    em.mfma(self.mfma_op, dst, str(self.a_R[buf]), str(frag), "0" if first else dst)
                 items.append(Item(reads, mfma))
         if self.dkv:
             extra = []
@@ -555,13 +573,13 @@ class GenBwd:
                     off = (32 * hb + 16 * ts) * self.ROW
 
                     def reads(buf, zr=zr, db=db, off=off):
-                        R = self.v_R[buf]
+                        R = self.a_R[buf]
                         for e in range(2):
                             em.ds_read(f"ds_read_b64_tr_b16 {R.r(2 * e, 2)}, {zr.r(2 * db + e)} offset:{off}",
                                        R.r(2 * e, 2), zr.r(2 * db + e))
 
                     def mfma(buf, acc=acc, bop=bop):
-                        em.mfma(self.mfma_op, str(acc), str(self.v_R[buf]), str(bop), str(acc))
+                        em.mfma(self.mfma_op, str(acc), str(self.a_R[buf]), str(bop), str(acc))
                     items.append(Item(reads, mfma))
         return items
 
@@ -632,23 +650,25 @@ class GenBwd:
                 k = st["n"]
                 if any(fenced[b] for b in range(cur + 1, bidx[k] + 1)):
                     return
-                seq[k].reads(k % RING)
+                seq[k].reads(k % self.RING)
+                issued.add(k)
                 st["n"] += 1
 
+        issued = set(range(pre))
         k = 0
         for bi, (items, ops, fence) in enumerate(blocks):
             if fence is not None:
                 assert st["n"] == k, "reads issued across a fence"
                 fence()
-            issue(k + LOOK, bi)
+            issue(k + self.LOOK, bi)
             total = sum(o.cost for o in ops)
             done, oi = 0.0, 0
             M = len(items)
             for m in range(M):
-                assert st["n"] > k
-                seq[k].mfma(k % RING)
+                assert k in issued, "an MFMA's operand reads were never issued"
+                seq[k].mfma(k % self.RING)
                 k += 1
-                issue(k + LOOK, bi)
+                issue(k + self.LOOK, bi)
                 target = total * (m + 1) / M
                 while oi < len(ops) and done + ops[oi].cost * 0.5 <= target:
                     ops[oi]()
@@ -657,7 +677,7 @@ class GenBwd:
             while oi < len(ops):
                 ops[oi]()
                 oi += 1
-        assert len(seq) - k < LOOK or st["n"] == k + LOOK
+        assert st["n"] == min(len(seq), k + self.LOOK)
         return seq
 
     def loop_edge(self):
@@ -709,7 +729,7 @@ class GenBwd:
             (self.z_items(0), self.y_ops(1, 0, m1, self.s_q1), None),
             (self.x_items(0), self.y_ops(1, 1, m1, self.s_q1), barrier),
         ]
-        self.run_blocks(blocks, self.z_items(1)[:LOOK], LOOK)
+        self.run_blocks(blocks, self.z_items(1)[:self.PRE], self.PRE)
 
     def epilogue(self):
         """The gradients, scaled (dK, dQ) and rounded, to their rows: lane
@@ -718,11 +738,14 @@ class GenBwd:
         outs = [(self.a_acc1, self.s_ro1, True)]
         if self.dkv:
             outs.append((self.a_acc2, self.s_ro2, False))
+        # temporaries: the S / dP registers, four at a time
+        tmps = [(blk, 4 * q) for blk in self.v_S + self.v_P for q in range(4)]
         n = 0
         for db in range(self.ND):
             for j in range(4):
                 for acc, rs, scaled in outs:
-                    R = self.v_R[n % RING]
+                    blk, o = tmps[n % len(tmps)]
+                    R = Block4(blk, o)
                     n += 1
                     for e in range(4):
                         em.valu(f"v_accvgpr_read_b32 {R.r(e)}, {acc[db].r(4 * j + e)}", dst=[R.r(e)],
@@ -756,7 +779,7 @@ class GenBwd:
         em.salu(f"s_waitcnt vmcnt({2 * self.DPW})")          # resident operands, tile 0
         em.salu("s_barrier")
         self.emit_dma()
-        self.run_blocks([(self.x_items(0), [], None)], self.z_items(1)[:LOOK], 0)
+        self.run_blocks([(self.x_items(0), [], None)], self.z_items(1)[:self.PRE], 0)
         self.loop_edge()
         snap = em.snapshot()
         pend = [set(p) for p in em.lds_pending]
@@ -810,7 +833,7 @@ class GenBwd:
             em.salu(f"s_branch {l_exit}")
         em.restore(snap)
         em.label(l_exit)
-        self.run_blocks([(self.z_items(1), [], None)], [], LOOK)
+        self.run_blocks([(self.z_items(1), [], None)], [], self.PRE)
         em.drain()
         em.label(l_store)
         self.epilogue()

@@ -161,13 +161,15 @@ int launch_bwd(const BwdLaunchArgs& a) {
   size_t size = sizeof(k);
   void* cfg[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, &k, HIP_LAUNCH_PARAM_BUFFER_SIZE, &size,
                  HIP_LAUNCH_PARAM_END};
-  // dK/dV: a workgroup per (128-key block, kv-head, batch); dQ: per (128-row
-  // query block, last first; q-head; batch)
-  hipError_t e = hipModuleLaunchKernel(dk->fn[kBwdFirst + var], (unsigned)((a.Skv + 127) / 128),
-                                       (unsigned)a.Hkv, (unsigned)a.B, 256, 1, 1, 0, a.stream,
+  // dK/dV: a workgroup per (kv-head, batch, 128-key block); dQ: per (q-head,
+  // batch, 128-row query block from the last).  The block index varies
+  // slowest, so the workgroups with the most work start first (a causal
+  // call's first keys and last rows see the most of the other side).
+  hipError_t e = hipModuleLaunchKernel(dk->fn[kBwdFirst + var], (unsigned)a.Hkv, (unsigned)a.B,
+                                       (unsigned)((a.Skv + 127) / 128), 256, 1, 1, 0, a.stream,
                                        nullptr, cfg);
   if (e != hipSuccess) return FA_ERR_HIP;
-  e = hipModuleLaunchKernel(dk->fn[kBwdFirst + 4 + var], k.nqb, (unsigned)a.Hq, (unsigned)a.B,
+  e = hipModuleLaunchKernel(dk->fn[kBwdFirst + 4 + var], (unsigned)a.Hq, (unsigned)a.B, k.nqb,
                             256, 1, 1, 0, a.stream, nullptr, cfg);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
