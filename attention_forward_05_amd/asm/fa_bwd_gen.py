@@ -38,11 +38,9 @@ registers, also across the step loop's back-edge.
 from __future__ import annotations
 
 from .regs import Alloc, Emitter, Op
-from .fa_fwd_gen import f32_hex
 
 NST = 4             # LDS stages (tiles) in flight
 KERNARG_BYTES = 128
-LOG2E = 1.4426950408889634
 
 
 def kernel_name(kind: str, dtype: str, D: int) -> str:
@@ -108,7 +106,7 @@ class GenBwd:
         A = Alloc("a", 0, 256)
         S = Alloc("s", 40, 102)
         r = self.__dict__
-        r["v_lane"] = V.take("lane", 1)
+        V.take("lane", 1)                          # v0: the lane id
         r["v_S"] = [V.take(f"S{p}", 16, 4) for p in range(2)]     # S, then P in place
         r["v_P"] = [V.take(f"dP{p}", 16, 4) for p in range(2)]    # dP, then dS in place
         r["v_pk"] = [[V.take(f"pk{p}{t}", 4, 4) for t in range(2)] for p in range(2)]  # P rounded

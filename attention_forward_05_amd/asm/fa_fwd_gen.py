@@ -542,6 +542,7 @@ class Gen:
         for i in range(self.DPW):
             def f(i=i):
                 em.salu(f"s_add_u32 m0, {slot}, {self.RPD * i * self.ROW}")
+                em.salu("s_nop 0")                 # SALU write of M0 -> LDS DMA: one wait state
                 em.vmem(f"buffer_load_dwordx4 {voff.r(i)}, {desc}, 0 offen lds", src=[voff.r(i)])
             ops.append(Op(f, 0.75))
         return ops

@@ -566,6 +566,7 @@ class Gen8:
         for desc, slot, voff in ((self.s_rk, y[5], self.v_kdma), (self.s_rv, y[1], self.v_vdma)):
             for i in range(self.DPW):
                 em.salu(f"s_add_u32 m0, {slot}, {self.RPD * i * self.ROW}")
+                em.salu("s_nop 0")                 # SALU write of M0 -> LDS DMA: one wait state
                 em.vmem(f"buffer_load_dwordx4 {voff.r(i)}, {desc}, 0 offen lds", src=[voff.r(i)])
 
     # ------------------------------------------------------------------------
