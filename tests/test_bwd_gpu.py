@@ -129,3 +129,34 @@ def test_backward_full_size_sampled(fa, w):
            dk[krows[:, 0], krows[:, 2], krows[:, 1]],
            dv[krows[:, 0], krows[:, 2], krows[:, 1]])
     check_grads(got, (rq, rk, rv), w.dtype, w.name)
+
+
+def test_backward_scale_zero(fa):
+    """scale = 0: every visible key gets the same weight, so dQ = dK = 0 exactly
+    (each is scale times a finite sum) and dV is dO averaged over the rows that
+    see each key; against the oracle at the same tolerance."""
+    q, k, v, do = _inputs(1, 200, 333, 4, 2, 128, "bf16", seed=11)
+    dq, dk, dv = run_bwd(fa, q, k, v, do, True, 0.0)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    ref = oracle.attn_bwd(q, k, v, do, True, 0.0)
+    check_grads((dq, dk, dv), ref, "bf16", "scale 0")
+
+
+def test_backward_one_kv_head(fa):
+    """Sixteen q-heads on one kv-head: the dK / dV sum runs over 16 heads' query
+    blocks in one workgroup's step sequence."""
+    q, k, v, do = _inputs(1, 300, 700, 16, 1, 128, "bf16", seed=12)
+    scale = 1.0 / math.sqrt(128)
+    got = run_bwd(fa, q, k, v, do, True, scale)
+    ref = oracle.attn_bwd(q, k, v, do, True, scale)
+    check_grads(got, ref, "bf16", "Hq16 Hkv1")
+
+
+def test_backward_is_deterministic(fa):
+    """Two calls on the same inputs give the same bits (every gradient element
+    has one writer and a fixed summation order)."""
+    q, k, v, do = _inputs(2, 517, 517, 8, 2, 64, "f16", seed=13)
+    a = run_bwd(fa, q, k, v, do, True, 0.125)
+    b = run_bwd(fa, q, k, v, do, True, 0.125)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
