@@ -81,7 +81,7 @@ hipError_t launch_combine(DType dtype, const float* part_o, const float* part_ls
 hipError_t launch_tile(const LaunchArgs& a, bool keys, bool packed, int nsplit, float* part_o,
                        float* part_lse);
 
-// The backward pass (fa_bwd.hip).
+// The backward pass (fa_bwd.hip and the generated gradient kernels).
 struct BwdLaunchArgs {
   DType dtype;
   const void* q;
