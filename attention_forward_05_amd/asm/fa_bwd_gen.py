@@ -155,7 +155,11 @@ class GenBwd:
         r["s_b1"] = t("base1", 2, 2)
         r["s_bl"] = t("basel", 2, 2)
         r["s_ds"] = t("dstep", 1)                # DMA stream: step
-        r["s_dj"], r["s_dq"] = t("dj", 1), t("dqb", 1)   # its head in the group and block (dK/dV)
+        r["s_dq"] = t("dqb", 1)                  # its query block (dK/dV)
+        r["s_full"] = t("full", 1)               # bytes of 64 rows of the streamed tensors
+        r["s_wd"], r["s_wdh"] = t("wrapd", 1), t("wrapdh", 1)  # base step to the next q-head (64-bit)
+        r["s_wdl"] = t("wrapdl", 1)              # the same for l2 / delta
+        r["s_wb"], r["s_wl"] = t("wbase", 1), t("wlbase", 1)   # the wave's LDS DMA offsets
         r["s_cq"] = t("cqb", 1)                  # the current step's query block (dK/dV)
         r["s_qb0"], r["s_nqb"] = t("qb0", 1), t("nqb", 1)
         r["s_lim"] = t("lim", 1)                 # dK/dV: the wave's first key; dQ: last key seen by all its rows
@@ -453,70 +457,93 @@ class GenBwd:
         em.salu("s_waitcnt lgkmcnt(0)")
 
     # ------------------------------------------------------------------------
+    def dma_init(self):
+        """The stream's running state for step 0: descriptors at its first
+        block (dK/dV: q-head hk*g, query block qb0; dQ: key tile 0), the
+        per-step and next-q-head base steps, and the wave's LDS offsets."""
+        em, x = self.em, self.s_x
+        em.salu(f"s_lshl_b32 {self.s_full}, {self.s_rowb}, 6")
+        em.salu(f"s_mov_b32 {self.s_ds}, 0")
+        if self.dkv:
+            em.salu(f"s_mov_b32 {self.s_dq}, {self.s_qb0}")
+            em.salu(f"s_mul_i32 {x[0]}, {self.s_qb0}, {self.s_full}")       # rows 64*qb0 on
+            em.salu(f"s_lshl_b32 {x[1]}, {self.s_qb0}, 8")
+            # next q-head: + 2D, back by the blocks after qb0 (signed)
+            em.salu(f"s_sub_u32 {x[2]}, {self.s_nqb}, {self.s_qb0}")
+            em.salu(f"s_sub_u32 {x[2]}, {x[2]}, 1")
+            em.salu(f"s_mul_i32 {x[3]}, {x[2]}, {self.s_full}")
+            em.salu(f"s_sub_u32 {self.s_wd}, {2 * self.D}, {x[3]}")
+            em.salu(f"s_ashr_i32 {self.s_wdh}, {self.s_wd}, 31")
+            em.salu(f"s_lshl_b32 {x[3]}, {x[2]}, 8")
+            em.salu(f"s_lshl_b32 {self.s_wdl}, s27, 2")
+            em.salu(f"s_sub_u32 {self.s_wdl}, {self.s_wdl}, {x[3]}")
+        else:
+            em.salu(f"s_mov_b32 {x[0]}, 0")
+            em.salu(f"s_mov_b32 {x[1]}, 0")
+        for rs, base in ((self.s_ra, self.s_b0), (self.s_rb, self.s_b1)):
+            em.salu(f"s_add_u32 {x[4]}, {base.r(0)}, {x[0]}")
+            em.salu(f"s_addc_u32 {x[5]}, {base.r(1)}, 0")
+            self.set_desc(rs, x[4], x[5], 0)
+        if self.dkv:
+            em.salu(f"s_add_u32 {x[4]}, {self.s_bl.r(0)}, {x[1]}")
+            em.salu(f"s_addc_u32 {x[5]}, {self.s_bl.r(1)}, 0")
+            self.set_desc(self.s_rl, x[4], x[5], 0)
+            em.salu(f"s_mul_i32 {self.s_wl}, {self.s_w}, {NST * 256}")
+            em.salu(f"s_add_u32 {self.s_wl}, {self.s_wl}, {self.REG_L}")
+        em.salu(f"s_mul_i32 {self.s_wb}, {self.s_w}, {self.DPW * 1024}")
+
     def emit_dma(self):
         """The wave's loads of stream step s_ds into LDS stage s_ds % NST,
-        then the stream counters advance.  Past the last step the ranges are
-        0 bytes: the loads write zeros into a stage no one reads, and every
-        step issues the same number of loads."""
+        then the stream advances.  Past the last step the ranges are 0
+        bytes: the loads write zeros into a stage no one reads, and every
+        step issues the same number of loads.  The last block of a q-head
+        (of the keys) has a range of its rows only."""
         em, x = self.em, self.s_x
-        D2 = 2 * self.D
-        if self.dkv:
-            em.salu(f"s_lshl_b32 {x[0]}, {self.s_dq}, 6")             # first row
-            em.salu(f"s_sub_u32 {x[1]}, s27, {x[0]}")
-            em.salu(f"s_min_u32 {x[1]}, {x[1]}, 64")
-            em.salu(f"s_cmp_lt_u32 {self.s_ds}, {self.s_n}")
-            em.salu(f"s_cselect_b32 {x[1]}, {x[1]}, 0")               # rows
-            em.salu(f"s_mul_i32 {x[2]}, {x[1]}, {self.s_rowb}")
-            em.salu(f"s_mul_i32 {x[3]}, {x[0]}, s29")
-            em.salu(f"s_add_u32 {x[3]}, {x[3]}, {self.s_dj}")
-            em.salu(f"s_mul_i32 {x[3]}, {x[3]}, {D2}")                # (i0*Hq + j) * 2D
-        else:
-            em.salu(f"s_lshl_b32 {x[0]}, {self.s_ds}, 6")             # first key
-            em.salu(f"s_sub_u32 {x[1]}, s28, {x[0]}")
-            em.salu(f"s_min_u32 {x[1]}, {x[1]}, 64")
-            em.salu(f"s_cmp_lt_u32 {self.s_ds}, {self.s_n}")
-            em.salu(f"s_cselect_b32 {x[1]}, {x[1]}, 0")
-            em.salu(f"s_mul_i32 {x[2]}, {x[1]}, {self.s_rowb}")
-            em.salu(f"s_mul_i32 {x[3]}, {x[0]}, {self.s_rowb}")
-        for rs, base in ((self.s_ra, self.s_b0), (self.s_rb, self.s_b1)):
-            em.salu(f"s_add_u32 {x[4]}, {base.r(0)}, {x[3]}")
-            em.salu(f"s_addc_u32 {x[5]}, {base.r(1)}, 0")
-            self.set_desc(rs, x[4], x[5], x[2])
+        TB = self.TILE.bit_length() - 1
+        em.salu(f"s_lshl_b32 {x[0]}, {self.s_dq if self.dkv else self.s_ds}, 6")   # first row (key)
+        em.salu(f"s_sub_u32 {x[1]}, {'s27' if self.dkv else 's28'}, {x[0]}")
+        em.salu(f"s_min_u32 {x[1]}, {x[1]}, 64")
+        em.salu(f"s_cmp_lt_u32 {self.s_ds}, {self.s_n}")
+        em.salu(f"s_cselect_b32 {x[1]}, {x[1]}, 0")                   # rows
+        em.salu(f"s_mul_i32 {self.s_ra.r(2)}, {x[1]}, {self.s_rowb}")
+        em.salu(f"s_mov_b32 {self.s_rb.r(2)}, {self.s_ra.r(2)}")
         em.salu(f"s_and_b32 {x[6]}, {self.s_ds}, {NST - 1}")
-        em.salu(f"s_mul_i32 {x[6]}, {x[6]}, {self.TILE}")
-        em.salu(f"s_mul_i32 {x[7]}, {self.s_w}, {self.DPW * 1024}")
-        em.salu(f"s_add_u32 {x[6]}, {x[6]}, {x[7]}")
+        em.salu(f"s_lshl_b32 {x[7]}, {x[6]}, {TB}")
+        em.salu(f"s_add_u32 {x[7]}, {x[7]}, {self.s_wb}")
         for region, rs in ((0, self.s_ra), (self.REG_B, self.s_rb)):
             for i in range(self.DPW):
-                em.salu(f"s_add_u32 m0, {x[6]}, {region + 1024 * i}")
+                em.salu(f"s_add_u32 m0, {x[7]}, {region + 1024 * i}")
                 em.salu("s_nop 0")
                 em.vmem(f"buffer_load_dwordx4 {self.v_dma.r(i)}, {rs}, 0 offen lds", src=[self.v_dma.r(i)])
         if self.dkv:
-            # 64 rows of l2 (wave 0) or delta (wave 1): (j*Sq + i0) * 4 past s_bl
+            # 64 rows of l2 (wave 0) or delta (wave 1)
             l_skip = self.lab("nol")
             em.salu(f"s_cmp_ge_u32 {self.s_w}, 2")
             em.salu(f"s_cbranch_scc1 {l_skip}")
-            em.salu(f"s_mul_i32 {x[3]}, {self.s_dj}, s27")
-            em.salu(f"s_add_u32 {x[3]}, {x[3]}, {x[0]}")
-            self.mul64(x[4], x[5], x[3], 4)
-            em.salu(f"s_add_u32 {x[4]}, {self.s_bl.r(0)}, {x[4]}")
-            em.salu(f"s_addc_u32 {x[5]}, {self.s_bl.r(1)}, {x[5]}")
-            em.salu(f"s_lshl_b32 {x[1]}, {x[1]}, 2")
-            self.set_desc(self.s_rl, x[4], x[5], x[1])
-            em.salu(f"s_and_b32 {x[6]}, {self.s_ds}, {NST - 1}")
+            em.salu(f"s_lshl_b32 {self.s_rl.r(2)}, {x[1]}, 2")
             em.salu(f"s_lshl_b32 {x[6]}, {x[6]}, 8")
-            em.salu(f"s_mul_i32 {x[7]}, {self.s_w}, {NST * 256}")
-            em.salu(f"s_add_u32 {x[6]}, {x[6]}, {x[7]}")
-            em.salu(f"s_add_u32 m0, {x[6]}, {self.REG_L}")
+            em.salu(f"s_add_u32 m0, {x[6]}, {self.s_wl}")
             em.salu("s_nop 0")
             em.vmem(f"buffer_load_dword {self.v_dml}, {self.s_rl}, 0 offen lds", src=[str(self.v_dml)])
             em.label(l_skip)
         em.salu(f"s_add_u32 {self.s_ds}, {self.s_ds}, 1")
         if self.dkv:
+            # the next block, or the next q-head's first block
             em.salu(f"s_add_u32 {self.s_dq}, {self.s_dq}, 1")
             em.salu(f"s_cmp_eq_u32 {self.s_dq}, {self.s_nqb}")
             em.salu(f"s_cselect_b32 {self.s_dq}, {self.s_qb0}, {self.s_dq}")
-            em.salu(f"s_addc_u32 {self.s_dj}, {self.s_dj}, 0")
+            em.salu(f"s_cselect_b32 {x[2]}, {self.s_wd}, {self.s_full}")
+            em.salu(f"s_cselect_b32 {x[3]}, {self.s_wdh}, 0")
+            em.salu(f"s_cselect_b32 {x[4]}, {self.s_wdl}, 256")
+            for rs in (self.s_ra, self.s_rb):
+                em.salu(f"s_add_u32 {rs.r(0)}, {rs.r(0)}, {x[2]}")
+                em.salu(f"s_addc_u32 {rs.r(1)}, {rs.r(1)}, {x[3]}")
+            em.salu(f"s_add_u32 {self.s_rl.r(0)}, {self.s_rl.r(0)}, {x[4]}")
+            em.salu(f"s_addc_u32 {self.s_rl.r(1)}, {self.s_rl.r(1)}, 0")
+        else:
+            for rs in (self.s_ra, self.s_rb):
+                em.salu(f"s_add_u32 {rs.r(0)}, {rs.r(0)}, {self.s_full}")
+                em.salu(f"s_addc_u32 {rs.r(1)}, {rs.r(1)}, 0")
 
     # ------------------------------------------------------------------------
     def x_items(self, hb):
@@ -766,12 +793,10 @@ class GenBwd:
         l_store, l_head, l_exit = self.lab("store"), self.lab("head"), self.lab("exit")
         em.salu(f"s_cmp_eq_u32 {self.s_n}, 0")
         em.salu(f"s_cbranch_scc1 {l_store}")
-        em.salu(f"s_mov_b32 {self.s_ds}, 0")
         em.salu(f"s_mov_b32 {self.s_t}, 0")
         if self.dkv:
-            em.salu(f"s_mov_b32 {self.s_dj}, 0")
-            em.salu(f"s_mov_b32 {self.s_dq}, {self.s_qb0}")
             em.salu(f"s_mov_b32 {self.s_cq}, {self.s_qb0}")
+        self.dma_init()
         self.emit_dma()
         self.emit_dma()
         em.salu(f"s_waitcnt vmcnt({2 * self.DPW})")          # resident operands, tile 0
@@ -834,8 +859,10 @@ class GenBwd:
         self.run_blocks([(self.z_items(1), [], None)], [], self.PRE)
         em.drain()
         em.label(l_store)
-        self.epilogue()
+        # every load (LDS DMA included) is done before the wave's last
+        # instructions; the stores need not be waited for
         em.salu("s_waitcnt vmcnt(0)")
+        self.epilogue()
         em.salu("s_endpgm")
 
     def assemble_text(self):
