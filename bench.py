@@ -202,7 +202,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload_na
                     "copy_kib": copy_kib, "copy_kernel": copy_name,
                     "factor_counter_bytes_per_byte": factor,
                     "bytes": sum(fa_vals) / len(fa_vals) * 1024.0 / factor}
-    w = workloads.BY_NAME[workload_name]
+    w = workloads.get(workload_name)
     return {
         "bytes_per_launch": round(res["fetch"]["bytes"] + res["write"]["bytes"]),
         "fetch_bytes": round(res["fetch"]["bytes"]),
@@ -373,7 +373,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=workloads.HEADLINE.name,
-                    choices=list(workloads.BY_NAME))
+                    help="a named workload (" + ", ".join(workloads.BY_NAME) + ") or an ad-hoc "
+                    "shape B,Hq,Hkv,Sq,Skv,D,causal,dtype")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the backward pass (fa_bwd)")
@@ -388,7 +389,7 @@ def main():
     args = ap.parse_args()
 
     if args.counter_summary:
-        w = workloads.BY_NAME[args.workload]
+        w = workloads.get(args.workload)
         for path in args.counter_summary:
             print(json.dumps(counter_summary(path, w, args.which), indent=1))
         return
@@ -396,7 +397,7 @@ def main():
     if args.traffic_summary:
         entry = traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
                                 args.copy_bytes, args.workload)
-        kernel = launched_kernel(workloads.BY_NAME[args.workload], args.compute_units)
+        kernel = launched_kernel(workloads.get(args.workload), args.compute_units)
         entry["kernel"] = kernel
         entry["kernel_code_sha256_16"] = kernel_code_hash(kernel)
         try:
@@ -424,7 +425,7 @@ def main():
         sys.exit(1)
     fa.load()
 
-    w = workloads.BY_NAME[args.workload]
+    w = workloads.get(args.workload)
     dev = torch.device("cuda:0")
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)

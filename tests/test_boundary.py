@@ -160,13 +160,19 @@ def test_plan_without_workspace_never_splits(lib, B, Sq, Skv, Hq, D, causal, cus
 # The tile kernels (include/fa.h): head dimension 256, and calls with Sq <= 64
 # whose q-heads of one kv-head are packed into rows (keys split over the four
 # waves when those rows number at most 32).  With a workspace, key ranges
-# double while items * ranges stays below the compute units (twice over for
-# the key split) and the shortest item keeps >= 4 (keys) / 8 (rows) tiles of
-# 128 / 64 keys (32 keys at D = 256) per range, at most 64 ranges.
+# double while items * ranges stays below the compute units and the shortest
+# item keeps >= 4 (keys) / 8 (rows) tiles of 128 / 64 keys (32 keys at
+# D = 256) per range, at most 64 ranges; the key split doubles once more
+# while items * ranges stays below twice the compute units and the ranges
+# keep >= 32 tiles.
 TILE_PLAN_CASES = [
     # B, Sq, Skv, Hq, Hkv, D, causal, kernel, ranges
-    # decode, g = 4: 4 rows, 8 items, 128 tiles of 128 keys -> 32 ranges (256 < 512)
+    # decode, g = 4: 4 rows, 8 items, 128 tiles of 128 keys -> 32 ranges (8 * 32 = 256)
     (1, 1, 16384, 32, 8, 128, 0, 3, 32),
+    # decode, g = 8: 8 items, 256 tiles -> 32 ranges of 8 tiles (too short to double again)
+    (1, 1, 32768, 64, 8, 128, 1, 3, 32),
+    # decode, 128 items, 256 tiles -> 2 ranges cover the units; 128 tiles each -> 4
+    (16, 1, 32768, 32, 8, 128, 1, 3, 4),
     # Sq 64, g = 4: 256 packed rows, 2 row blocks x 8 kv-heads = 16 items; the
     # first block's last query 31 sees 16352 keys = 256 tiles of 64 -> 16 ranges
     (1, 64, 16384, 32, 8, 128, 1, 2, 16),
@@ -271,3 +277,15 @@ def test_noalloc_unsupported_arguments(lib, over):
 ])
 def test_ws_rejects_bad_workspace(lib, args):
     assert _call_ws(**args) == fa.FA_ERR_INVALID
+
+
+def test_workload_shapes():
+    """bench.py's workloads: a name, or an ad-hoc shape string."""
+    import workloads
+    assert workloads.get(workloads.HEADLINE.name) is workloads.HEADLINE
+    w = workloads.get("2,32,8,4096,8192,128,1,f16")
+    assert (w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.causal, w.dtype) == (2, 32, 8, 4096, 8192, 128, True, "f16")
+    assert w.name == "causal_b2_hq32_hkv8_sq4096_skv8192_d128_f16"
+    for bad in ("nope", "2,32,8,4096,8192,128,2,bf16", "2,32,8,4096,8192,128,1,fp8", "1,2,3"):
+        with pytest.raises(ValueError):
+            workloads.get(bad)

@@ -93,6 +93,21 @@ BY_NAME = {w.name: w for w in WORKLOADS + SPLIT_WORKLOADS + DECODE_WORKLOADS + H
 HEADLINE = WORKLOADS[2]
 
 
+def get(spec: str) -> Workload:
+    """A named workload, or an ad-hoc shape "B,Hq,Hkv,Sq,Skv,D,causal,dtype"
+    (causal 0 or 1, dtype bf16 or f16) with seeded N(0, 1) inputs."""
+    if spec in BY_NAME:
+        return BY_NAME[spec]
+    f = spec.split(",")
+    if len(f) != 8 or f[7] not in ("bf16", "f16") or f[6] not in ("0", "1"):
+        raise ValueError(f"not a workload name or B,Hq,Hkv,Sq,Skv,D,causal,dtype: {spec!r}")
+    B, Hq, Hkv, Sq, Skv, D = (int(x) for x in f[:6])
+    causal = f[6] == "1"
+    name = (f"{'causal' if causal else 'noncausal'}_b{B}_hq{Hq}_hkv{Hkv}_sq{Sq}_skv{Skv}"
+            f"_d{D}_{f[7]}")
+    return Workload(name, B, Hq, Hkv, Sq, Skv, D, causal, f[7], 100)
+
+
 def make_inputs(B, Sq, Skv, Hq, Hkv, D, dtype="bf16", seed=0,
                 k_row_boost_frac=0.0, dist="normal"):
     """Draw q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] on the CPU.
