@@ -433,7 +433,7 @@ hipError_t launch_t(const TileArgs& a, int D, bool keys, int items, hipStream_t 
   }
   if (D == 64) return launch_one<T, 64, 64, false>(a, items, stream);
   if (D == 128) return launch_one<T, 128, 64, false>(a, items, stream);
-  if (D == 256) return launch_one<T, 256, 32, false>(a, items, stream);
+  if (D == 256) return launch_one<T, 256, 64, false>(a, items, stream);
   return hipErrorInvalidValue;
 }
 

@@ -161,10 +161,9 @@ def test_plan_without_workspace_never_splits(lib, B, Sq, Skv, Hq, D, causal, cus
 # whose q-heads of one kv-head are packed into rows (keys split over the four
 # waves when those rows number at most 32).  With a workspace, key ranges
 # double while items * ranges stays below the compute units and the shortest
-# item keeps >= 4 (keys) / 8 (rows) tiles of 128 / 64 keys (32 keys at
-# D = 256) per range, at most 64 ranges; the key split doubles once more
-# while items * ranges stays below twice the compute units and the ranges
-# keep >= 32 tiles.
+# item keeps >= 4 (keys) / 8 (rows) tiles of 128 / 64 keys per range, at
+# most 64 ranges; the key split doubles once more while items * ranges stays
+# below twice the compute units and the ranges keep >= 32 tiles.
 TILE_PLAN_CASES = [
     # B, Sq, Skv, Hq, Hkv, D, causal, kernel, ranges
     # decode, g = 4: 4 rows, 8 items, 128 tiles of 128 keys -> 32 ranges (8 * 32 = 256)
@@ -176,10 +175,10 @@ TILE_PLAN_CASES = [
     # Sq 64, g = 4: 256 packed rows, 2 row blocks x 8 kv-heads = 16 items; the
     # first block's last query 31 sees 16352 keys = 256 tiles of 64 -> 16 ranges
     (1, 64, 16384, 32, 8, 128, 1, 2, 16),
-    # D = 256, 8 blocks of 128 rows x 8 heads = 64 items, first block 4 tiles: no split
+    # D = 256, 8 blocks of 128 rows x 8 heads = 64 items, first block 2 tiles: no split
     (1, 1000, 1000, 8, 8, 256, 1, 2, 1),
-    # D = 256, 8 items, 256 tiles of 32 keys -> 32 ranges (8 * 32 = 256)
-    (1, 256, 8192, 4, 4, 256, 0, 2, 32),
+    # D = 256, 8 items, 128 tiles of 64 keys -> 16 ranges of 8 tiles
+    (1, 256, 8192, 4, 4, 256, 0, 2, 16),
     # D = 64 decode, g = 8: 4 items, 32 tiles -> 8 ranges (32 < 4 * 2 * 8)
     (2, 1, 4096, 16, 2, 64, 1, 3, 8),
 ]

@@ -352,7 +352,7 @@ D256_CASES = [
     (1, 100, 1000, 8, 2, True, "f16", False),     # bottom-right, GQA 4
     (1, 1000, 100, 2, 1, True, "bf16", False),    # rows with no visible key
     (2, 513, 777, 3, 3, False, "f16", False),     # ragged, Hq % 8 != 0
-    (1, 256, 8192, 4, 4, False, "bf16", True),    # 32 key ranges merged
+    (1, 256, 8192, 4, 4, False, "bf16", True),    # 16 key ranges merged
     (1, 200, 6000, 6, 2, True, "f16", True),      # split, bottom-right, GQA 3
     (1, 40, 3000, 8, 1, True, "bf16", True),      # few rows (not packed at D = 256)
 ]
