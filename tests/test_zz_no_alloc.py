@@ -58,7 +58,7 @@ def test_noalloc_matches_workspace_entry_two_calls():
     shapes = [
         # B, Sq, Skv, Hq, Hkv, D, causal, dtype
         (1, 1, 32768, 64, 8, 128, True, "bf16"),    # decode, many key ranges
-        (1, 4, 8192, 32, 8, 128, False, "f16"),     # smaller: fewer rows and ranges
+        (1, 4, 4096, 32, 8, 128, False, "f16"),     # smaller: fewer rows and ranges
     ]
     sizes = []
     for n, (B, Sq, Skv, Hq, Hkv, D, causal, dtype) in enumerate(shapes):
