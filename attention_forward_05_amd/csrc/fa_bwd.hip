@@ -38,30 +38,49 @@ namespace {
 using namespace mfma;
 
 // delta[(b*Hq + hq)*Sq + i] = sum_d O[b,i,hq,d] * dO[b,i,hq,d] in fp32 and
-// l2[...] = LSE[...] * log2(e); D/8 lanes per row, 8 elements each.
+// l2[...] = LSE[...] * log2(e).  Rows are taken in memory order (b, i, hq),
+// so a wave reads contiguous bytes; D/8 lanes per row, 8 elements each, and
+// each lane group takes kRowsPerGroup rows a block's width apart, their
+// loads issued together.
+constexpr int kRowsPerGroup = 4;
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
   constexpr int L = D / 8;
+  constexpr int G = 256 / L;  // lane groups (rows) per pass of the block
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  const int64_t r = (int64_t)blockIdx.x * (256 / L) + threadIdx.x / L;
   const int lane = threadIdx.x % L;
-  float acc = 0.0f;
-  if (r < rows) {
-    const int i = (int)(r % a.Sq);
-    const int64_t bh = r / a.Sq;
-    const int hq = (int)(bh % a.Hq);
-    const int b = (int)(bh / a.Hq);
-    const int64_t off = (((int64_t)b * a.Sq + i) * a.Hq + hq) * D + 8 * lane;
-    const s16x8 o8 = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.o) + off);
-    const s16x8 d8 = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + off);
+  const int64_t r0 = (int64_t)blockIdx.x * G * kRowsPerGroup + threadIdx.x / L;
+  s16x8 o8[kRowsPerGroup], d8[kRowsPerGroup];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += T::widen(o8[e]) * T::widen(d8[e]);
+  for (int u = 0; u < kRowsPerGroup; ++u) {
+    const int64_t r = r0 + (int64_t)u * G;  // memory row (b, i, hq)
+    if (r < rows) {
+      const int64_t off = r * D + 8 * lane;
+      o8[u] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.o) + off);
+      d8[u] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + off);
+    } else {
+      o8[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      d8[u] = o8[u];
+    }
   }
 #pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (r < rows && lane == 0) {
-    a.delta[r] = acc;
-    a.l2[r] = a.lse[r] * kLog2e;
+  for (int u = 0; u < kRowsPerGroup; ++u) {
+    const int64_t r = r0 + (int64_t)u * G;
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += T::widen(o8[u][e]) * T::widen(d8[u][e]);
+#pragma unroll
+    for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (r < rows && lane == 0) {
+      const int hq = (int)(r % a.Hq);
+      const int64_t bi = r / a.Hq;
+      const int i = (int)(bi % a.Sq);
+      const int64_t b = bi / a.Sq;
+      const int64_t s = (b * a.Hq + hq) * a.Sq + i;  // statistics row (b, hq, i)
+      a.delta[s] = acc;
+      a.l2[s] = a.lse[s] * kLog2e;
+    }
   }
 }
 
@@ -70,7 +89,7 @@ hipError_t launch_delta_d(const BwdArgs& in, hipStream_t stream) {
   BwdArgs a = in;
   void* args[] = {&a};
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  const int rows_per_block = 256 / (D / 8);
+  const int rows_per_block = 256 / (D / 8) * kRowsPerGroup;
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<T, D>),
                          dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
                          args, 0, stream);
