@@ -273,6 +273,10 @@ def _dma_stream(kind, D, shape, wave, steps):
     (1, 300, 700, 16, 1, 1, 0, 0, 0),    # sixteen q-heads per kv-head, bottom-right offset
     (3, 130, 77, 2, 2, 0, 0, 1, 2),      # non-causal, Skv < 128
     (1, 4096, 4096, 32, 32, 1, 5, 31, 0),
+    # a batch slice of q just under 2 GiB at D = 128: the step from a q-head's
+    # last query block back to the next q-head's first is -2.14e9 bytes, near
+    # the signed 32-bit limit, and batch 1 starts 2.1e9 bytes in
+    (2, 65472, 65472, 128, 64, 0, 500, 63, 1),
 ])
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("wave", [0, 1, 3])
@@ -324,6 +328,8 @@ def test_dkv_dma_stream(shape, D, wave):
     (1, 300, 700, 16, 1, 1, 1, 15, 0),
     (3, 130, 77, 2, 2, 0, 0, 1, 2),
     (1, 4096, 4096, 32, 8, 1, 3, 17, 0),
+    # a batch slice of k just under 2 GiB at D = 128 (the longest block: 1023 tiles)
+    (2, 65472, 65472, 128, 128, 1, 0, 127, 1),
 ])
 @pytest.mark.parametrize("D", [128, 64])
 def test_dq_dma_stream(shape, D):
