@@ -62,8 +62,7 @@ def load():
     path = library_path()
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m attention_forward_05_amd.build` "
-            "(or __graft_entry__.build())")
+            f"{path} is missing: build it with `python -m attention_forward_05_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i = ctypes.c_void_p, ctypes.c_int
     for name in ("fa_fwd", "fa_fwd_f16"):
