@@ -4,7 +4,7 @@
 // in `_attention_forward`: malformed arguments (shapes that do not agree, a
 // q-head count that is not a multiple of the kv-head count) are errors,
 // well-formed requests outside what the kernels implement (head dimensions
-// other than 64, 128 and 256 here) are "not implemented".  Unlike that page, any
+// other than 64, 128, 192 and 256 here) are "not implemented".  Unlike that page, any
 // sequence lengths >= 1 are accepted; the kernel masks ragged tails.
 //
 // Every check runs before the first HIP call, so invalid calls never touch
@@ -65,7 +65,7 @@ int check_fwd_args(DType dtype, const void* q, const void* k, const void* v, voi
     return FA_ERR_INVALID;
   if (lse && overlap(o, qb, lse, nlse * 4)) return FA_ERR_INVALID;
 
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   if (scale < 0.0f) return FA_ERR_UNSUPPORTED;
   // Size limits of the kernel's 32-bit address arithmetic and item decoding:
   // query tiles at most 65535; fewer than 2^24 (batch, q-head, query tile)
@@ -250,7 +250,7 @@ int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal, int 
   if (Hq % Hkv != 0) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (with_workspace != 0 && with_workspace != 1) return FA_ERR_INVALID;
-  if (D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
   const fa::Plan p =
       fa::make_plan(B, Sq, Skv, Hq, Hkv, D, causal, compute_units, with_workspace != 0);
   *kernel = p.kernel;
@@ -266,7 +266,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_INVALID:
       return "invalid argument";
     case FA_ERR_UNSUPPORTED:
-      return "unsupported argument (D must be 64, 128 or 256, scale >= 0, sizes within the kernel's limits)";
+      return "unsupported argument (D must be 64, 128, 192 or 256, scale >= 0, sizes within the kernel's limits)";
     case FA_ERR_HIP:
       return "HIP runtime error at kernel launch";
     case FA_ERR_WORKSPACE:

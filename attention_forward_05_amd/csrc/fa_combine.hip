@@ -55,6 +55,7 @@ combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_
   constexpr int kLanesPerRow = D / 4;
   constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
   const int64_t rows = (int64_t)B * Hq * Sq;
+  if ((int)threadIdx.x >= kRowsPerBlock * kLanesPerRow) return;  // D = 192: 5 rows of 48 lanes
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   if (r >= rows) return;
   const int lane = threadIdx.x % kLanesPerRow;
@@ -126,6 +127,7 @@ hipError_t launch_t(const float* part_o, const float* part_lse, T* o, float* lse
   switch (D) {
     case 64: return launch_d<T, 64>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
     case 128: return launch_d<T, 128>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
+    case 192: return launch_d<T, 192>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
     case 256: return launch_d<T, 256>(part_o, part_lse, o, lse, nsplit, B, Hq, Sq, stream);
     default: return hipErrorInvalidValue;
   }

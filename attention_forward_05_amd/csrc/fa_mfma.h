@@ -63,6 +63,15 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// LDS row pitch, in 16-bit elements, of a tile with rows of D elements:
+// D itself, except D = 192, whose rows are padded to 256 so that the XOR
+// swizzle below (of the low four chunk-index bits) keeps every chunk inside
+// its row (chunks 0..23 map to 0..31).
+template <int D>
+constexpr int lds_pitch() {
+  return D == 192 ? 256 : D;
+}
+
 // 16-byte chunk swizzle of an LDS tile with rows of D 16-bit elements.
 // Row reads (16 consecutive rows at one chunk) and transposing reads (4
 // consecutive rows x 4 consecutive chunks per 16 lanes) both hit distinct
@@ -74,7 +83,7 @@ __device__ __forceinline__ int swz(int r) {
 }
 template <int D>
 __device__ __forceinline__ int lds_off(int r, int chunk) {
-  return r * (2 * D) + ((chunk ^ swz<D>(r)) << 4);
+  return r * (2 * lds_pitch<D>()) + ((chunk ^ swz<D>(r)) << 4);
 }
 
 // ds_read_b64_tr_b16 on a generic pointer into LDS: within each group of 16

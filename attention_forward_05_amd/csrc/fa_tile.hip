@@ -1,7 +1,8 @@
 // fa_tile.hip -- the tile kernels: the fused attention forward pass written
 // in HIP C++ on gfx950 MFMA, for the shapes the generated assembly kernels do
-// not take: head dimension 256 (the JAX Pallas FlashAttention3 page's `main`
-// sweeps head_dim 64, 128 and 256), and decode-shaped calls (a few query
+// not take: head dimensions 192 and 256 (the JAX Pallas FlashAttention3
+// page's `main` sweeps head_dim 64, 128 and 256, and its forward takes any
+// multiple of 64), and decode-shaped calls (a few query
 // rows over a long key range, where the q-heads of one kv-head are packed
 // into one block of rows so that K and V are read once per kv-head).
 //
@@ -85,7 +86,7 @@ struct Tile {
   static constexpr int kCPR = D / 8;                 // 16-byte chunks per row
   static constexpr int kChunks = TK * kCPR;          // chunks per K (or V) tile
   static constexpr int kNC = kChunks / kThreads;     // chunks per thread per tile
-  static constexpr int kTileBytes = TK * D * 2;
+  static constexpr int kTileBytes = TK * lds_pitch<D>() * 2;
   static constexpr int kKB = KEYS ? 1 : TK / 32;     // 32-key blocks per wave per tile
   static constexpr int kND = D / 32;                 // 32-dim blocks of O^T
   static constexpr int kNQ = D / 16;                 // k-steps of S^T
@@ -433,6 +434,7 @@ hipError_t launch_t(const TileArgs& a, int D, bool keys, int items, hipStream_t 
   }
   if (D == 64) return launch_one<T, 64, 64, false>(a, items, stream);
   if (D == 128) return launch_one<T, 128, 64, false>(a, items, stream);
+  if (D == 192) return launch_one<T, 192, 64, false>(a, items, stream);
   if (D == 256) return launch_one<T, 256, 64, false>(a, items, stream);
   return hipErrorInvalidValue;
 }

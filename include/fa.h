@@ -50,7 +50,7 @@ typedef enum {
                               causal not 0/1, scale not finite, pointer not
                               16-byte aligned, o overlapping q/k/v, a workspace
                               overlapping a tensor, size overflow, unknown dtype */
-  FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64, 128 or 256,
+  FA_ERR_UNSUPPORTED = -2, /* valid but not implemented: D not 64, 128, 192 or 256,
                               scale < 0, sizes beyond the kernel's limits
                               (ceil(Sq/256) at most 65535, B*Hq*ceil(Sq/256)
                               below 2^24, ceil(Skv/64) below 65536,
@@ -73,7 +73,7 @@ enum { FA_DTYPE_BF16 = 0, FA_DTYPE_F16 = 1 };
  *   o    : device pointer, [B, Sq, Hq, D] bf16, written; must not overlap q, k or v
  *   lse  : device pointer, [B, Hq, Sq] fp32, written; may be NULL (not written)
  *   B, Sq, Skv, Hq, Hkv : sizes >= 1, Hq a multiple of Hkv
- *   D    : head dimension, 64, 128 or 256
+ *   D    : head dimension, 64, 128, 192 or 256
  *   causal : 0 (no mask) or 1 (bottom-right aligned causal mask)
  *   scale  : multiplies the logits before the softmax; finite and >= 0
  *            (usually 1/sqrt(D))
@@ -205,7 +205,7 @@ int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o
 enum {
   FA_KERNEL_FOUR_WAVE = 0,  /* 256-row query tiles, one wave per SIMD (D = 64, 128) */
   FA_KERNEL_EIGHT_WAVE = 1, /* 512-row query tiles, two waves per SIMD (D = 64, 128) */
-  FA_KERNEL_TILE_ROWS = 2,  /* 128-row blocks, four waves over the rows: D = 256;
+  FA_KERNEL_TILE_ROWS = 2,  /* 128-row blocks, four waves over the rows: D = 192, 256;
                                calls with Sq <= 64 whose q-heads of one
                                kv-head make more than 32 rows together; and
                                causal D = 64 calls without enough 512-row
@@ -231,7 +231,7 @@ enum {
  *
  * Returns FA_OK, FA_ERR_INVALID (NULL output pointer, size or compute_units
  * < 1, Hq % Hkv != 0, causal or with_workspace not 0/1) or
- * FA_ERR_UNSUPPORTED (D not 64, 128 or 256); the outputs are written only on
+ * FA_ERR_UNSUPPORTED (D not 64, 128, 192 or 256); the outputs are written only on
  * FA_OK.  Size limits of fa_fwd are not checked here.
  */
 int fa_fwd_plan(int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,

@@ -95,7 +95,7 @@ int main() {
   for (int sq : sizes)
     for (int skv : sizes)
       for (int hq : {1, 8, 64, 256})
-        for (int d : {64, 128, 256})
+        for (int d : {64, 128, 192, 256})
           for (int c = 0; c < 2; ++c)
             for (int w = 0; w < 2; ++w) {
               EXPECT(fa_fwd_plan(2, sq, skv, hq, hq > 4 ? hq / 4 : 1, d, c, 256, w, &kern, &ranges, &ws),

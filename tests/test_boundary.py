@@ -179,6 +179,9 @@ TILE_PLAN_CASES = [
     (1, 1000, 1000, 8, 8, 256, 1, 2, 1),
     # D = 256, 8 items, 128 tiles of 64 keys -> 16 ranges of 8 tiles
     (1, 256, 8192, 4, 4, 256, 0, 2, 16),
+    # D = 192 (rows padded to 256 in LDS): the same plan as D = 256; few rows are not packed
+    (1, 256, 8192, 4, 4, 192, 0, 2, 16),
+    (1, 1, 8192, 32, 8, 192, 1, 2, 8),
     # D = 64 decode, g = 8: 4 items, 32 tiles -> 8 ranges (32 < 4 * 2 * 8)
     (2, 1, 4096, 16, 2, 64, 1, 3, 8),
 ]

@@ -344,8 +344,9 @@ def test_decode_slow_path(fa, D):
                   split=True)
 
 
-# head dimension 256: the tile kernel, four waves over 128-row blocks
-D256_CASES = [
+# head dimensions 192 and 256: the tile kernel, four waves over 128-row blocks
+# (D = 192 with its LDS rows padded to 256 dimensions)
+LARGE_D_CASES = [
     # B, Sq, Skv, Hq, Hkv, causal, dtype, split
     (1, 128, 128, 1, 1, True, "bf16", False),
     (2, 300, 300, 4, 2, True, "bf16", False),     # ragged rows and keys, GQA 2
@@ -358,16 +359,18 @@ D256_CASES = [
 ]
 
 
-@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype,split", D256_CASES)
-def test_head_dim_256(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, split):
-    assert plan(fa, B, Sq, Skv, Hq, Hkv, 256, causal, split)[0] == fa.FA_KERNEL_TILE_ROWS
-    full_case(fa, B, Sq, Skv, Hq, Hkv, 256, causal, dtype, seed=Sq + Skv + 256, split=split)
+@pytest.mark.parametrize("D", [192, 256])
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,causal,dtype,split", LARGE_D_CASES)
+def test_head_dim_large(fa, B, Sq, Skv, Hq, Hkv, causal, dtype, split, D):
+    assert plan(fa, B, Sq, Skv, Hq, Hkv, D, causal, split)[0] == fa.FA_KERNEL_TILE_ROWS
+    full_case(fa, B, Sq, Skv, Hq, Hkv, D, causal, dtype, seed=Sq + Skv + D, split=split)
 
 
-def test_head_dim_256_large_logits(fa):
-    """D = 256 with scale 1 on N(0, 1) inputs (nearly one-hot softmax, the
-    running max moves often), fp16: within the rounding bound."""
-    q, k, v = workloads.make_inputs(1, 200, 700, 2, 1, 256, "f16", 77)
+@pytest.mark.parametrize("D", [192, 256])
+def test_head_dim_large_logits(fa, D):
+    """D = 192, 256 with scale 1 on N(0, 1) inputs (nearly one-hot softmax,
+    the running max moves often), fp16: within the rounding bound."""
+    q, k, v = workloads.make_inputs(1, 200, 700, 2, 1, D, "f16", 77)
     o, lse = run_gpu(fa, q, k, v, True, 1.0)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, True, 1.0)
     assert rounding_bound(o, o_ref, v, "f16") <= 1.0
@@ -485,8 +488,8 @@ def test_named_workload(fa, w, parity_figures):
                          ids=[w.name for w in workloads.HEAD_DIM_WORKLOADS])
 def test_head_dim_workload(fa, w, parity_figures):
     """The head-dimension workloads (D = 64 on the four-wave and the
-    eight-wave kernel, D = 256 on the tile kernel) at full size, every
-    output element against the oracle."""
+    eight-wave kernel, D = 192 and 256 on the tile kernel) at full size,
+    every output element against the oracle."""
     q, k, v = workloads.workload_inputs(w)
     o, lse = run_gpu(fa, q, k, v, w.causal, w.scale)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, w.scale)

@@ -83,6 +83,8 @@ DECODE_WORKLOADS = [
 HEAD_DIM_WORKLOADS = [
     Workload("causal_b1_h16_s4096_d64_bf16", 1, 16, 16, 4096, 4096, 64, True, "bf16", 51),
     Workload("causal_b1_h16_s4096_d256_bf16", 1, 16, 16, 4096, 4096, 256, True, "bf16", 52),
+    # the multiple of 64 between them (the page's forward takes any)
+    Workload("causal_b1_h16_s4096_d192_bf16", 1, 16, 16, 4096, 4096, 192, True, "bf16", 54),
     # the headline shape at head dimension 64 (enough 512-row items for the
     # eight-wave kernel)
     Workload("causal_b2_h32_s4096_d64_bf16", 2, 32, 32, 4096, 4096, 64, True, "bf16", 53),
