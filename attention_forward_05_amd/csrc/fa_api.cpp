@@ -168,8 +168,9 @@ int bwd(fa::DType dtype, const void* q, const void* k, const void* v, const void
     for (int y = x + 1; y < 3; ++y)
       if (overlap(outs[x], out_bytes[x], outs[y], out_bytes[y])) return FA_ERR_INVALID;
   }
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  // the gradient kernels address one batch slice of k / v with 32 bits
+  // (D = 64, 128: the generated gradient kernels; 192, 256: the HIP C++ ones)
+  if (D != 64 && D != 128 && D != 192 && D != 256) return FA_ERR_UNSUPPORTED;
+  // the generated gradient kernels address one batch slice of k / v with 32 bits
   if ((uint64_t)Skv * (uint64_t)Hkv * (uint64_t)D * 2u >= (1ull << 31)) return FA_ERR_UNSUPPORTED;
   // the workspace holds two fp32 per query row, [2][B][Hq][Sq]: LSE in log2
   // units and delta

@@ -11,7 +11,8 @@
 //   dK, dV  = scale * dS^T.Q,  P^T.dO, summed over the q-heads of a kv-head
 //                                                     (`kernel_dkv`)
 // The dK/dV and dQ kernels are generated gfx950 assembly
-// (attention_forward_05_amd/asm/fa_bwd_gen.py), launched from fa_launch.cpp
+// (attention_forward_05_amd/asm/fa_bwd_gen.py) for D = 64 and 128, and HIP
+// C++ (fa_bwd_wide.hip) for D = 192 and 256, launched from fa_launch.cpp
 // after this one.  A row without a visible key (LSE = -inf) gets l2 = -inf;
 // the causal mask hides every key from it, so its P is 0.
 
@@ -39,29 +40,41 @@ using namespace mfma;
 
 // delta[(b*Hq + hq)*Sq + i] = sum_d O[b,i,hq,d] * dO[b,i,hq,d] in fp32 and
 // l2[...] = LSE[...] * log2(e).  Rows are taken in memory order (b, i, hq),
-// so a wave reads contiguous bytes; D/8 lanes per row, 8 elements each, and
-// each lane group takes kRowsPerGroup rows a block's width apart, their
-// loads issued together.
+// so a wave reads contiguous bytes; L lanes per row (a power of two) with E
+// 16-byte chunks each, and each lane group takes kRowsPerGroup rows a
+// block's width apart, their loads issued together.
 constexpr int kRowsPerGroup = 4;
+
+template <int D>
+struct DeltaShape {
+  static constexpr int kChunks = D / 8;                      // 16-byte chunks per row
+  static constexpr int L = D == 192 ? 8 : kChunks;           // lanes per row
+  static constexpr int E = kChunks / L;                      // chunks per lane
+  static constexpr int G = 256 / L;                          // rows per pass of the block
+  static_assert(L * E == kChunks && (L & (L - 1)) == 0, "lanes per row");
+};
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
-  constexpr int L = D / 8;
-  constexpr int G = 256 / L;  // lane groups (rows) per pass of the block
+  using S = DeltaShape<D>;
+  constexpr int L = S::L, E = S::E, G = S::G;
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   const int lane = threadIdx.x % L;
   const int64_t r0 = (int64_t)blockIdx.x * G * kRowsPerGroup + threadIdx.x / L;
-  s16x8 o8[kRowsPerGroup], d8[kRowsPerGroup];
+  s16x8 o8[kRowsPerGroup][E], d8[kRowsPerGroup][E];
 #pragma unroll
   for (int u = 0; u < kRowsPerGroup; ++u) {
     const int64_t r = r0 + (int64_t)u * G;  // memory row (b, i, hq)
-    if (r < rows) {
-      const int64_t off = r * D + 8 * lane;
-      o8[u] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.o) + off);
-      d8[u] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + off);
-    } else {
-      o8[u] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      d8[u] = o8[u];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (r < rows) {
+        const int64_t off = r * D + 8 * (lane * E + e);
+        o8[u][e] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.o) + off);
+        d8[u][e] = *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + off);
+      } else {
+        o8[u][e] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        d8[u][e] = o8[u][e];
+      }
     }
   }
 #pragma unroll
@@ -69,7 +82,9 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
     const int64_t r = r0 + (int64_t)u * G;
     float acc = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += T::widen(o8[u][e]) * T::widen(d8[u][e]);
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc += T::widen(o8[u][e][x]) * T::widen(d8[u][e][x]);
 #pragma unroll
     for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (r < rows && lane == 0) {
@@ -89,7 +104,7 @@ hipError_t launch_delta_d(const BwdArgs& in, hipStream_t stream) {
   BwdArgs a = in;
   void* args[] = {&a};
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  const int rows_per_block = 256 / (D / 8) * kRowsPerGroup;
+  const int rows_per_block = DeltaShape<D>::G * kRowsPerGroup;
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_delta_kernel<T, D>),
                          dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(256),
                          args, 0, stream);
@@ -110,6 +125,8 @@ hipError_t launch_bwd_delta(const BwdLaunchArgs& in) {
   const bool bf = in.dtype == DType::kBF16;
   if (in.D == 64) return bf ? launch_delta_d<BF16, 64>(a, in.stream) : launch_delta_d<F16, 64>(a, in.stream);
   if (in.D == 128) return bf ? launch_delta_d<BF16, 128>(a, in.stream) : launch_delta_d<F16, 128>(a, in.stream);
+  if (in.D == 192) return bf ? launch_delta_d<BF16, 192>(a, in.stream) : launch_delta_d<F16, 192>(a, in.stream);
+  if (in.D == 256) return bf ? launch_delta_d<BF16, 256>(a, in.stream) : launch_delta_d<F16, 256>(a, in.stream);
   return hipErrorInvalidValue;
 }
 

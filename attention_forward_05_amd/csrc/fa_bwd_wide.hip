@@ -1,0 +1,424 @@
+// fa_bwd_wide.hip -- the backward's dK/dV and dQ kernels for head
+// dimensions 192 and 256, in HIP C++ on gfx950 MFMA.
+//
+// The arithmetic is that of the JAX Pallas FlashAttention3 page's backward
+// (`kernel_dkv`, `kernel_dq`), with the scale on the logits and this
+// library's natural-log LSE (l2 = LSE * log2(e), written with delta by the
+// delta kernel of fa_bwd.hip):
+//   P  = exp2(c*S - l2),  dP = dO.V^T,  dS = P * (dP - delta)
+//   dV = P^T.dO,  dK = scale * dS^T.Q  (summed over the q-heads of a kv-head),
+//   dQ = scale * dS.K
+// with P and dS rounded to the input dtype before the products that read
+// them.
+//
+// At these head dimensions one wave cannot hold the gradients of 32 keys
+// (2 * D * 32 fp32) next to the resident K and V, as the generated kernels
+// for D <= 128 do.  Here a workgroup of D/64 waves splits the head dimension
+// instead: wave w owns dimensions 64w .. 64w+63 of the resident operands and
+// of the gradients.  Each wave computes S and dP of a 32 x 32 block over its
+// 64 dimensions; the partial sums meet in LDS, every wave adds them in the
+// same order (so all hold the same S and dP), and then multiplies its own
+// slice of the gradient products.
+//
+// Products on v_mfma_f32_32x32x16 (64 lanes; the layouts are listed in
+// fa_mfma.h):
+//   dK/dV kernel, per 32-row block of Q / dO:
+//     S = Q.K^T and dP = dO.V^T as C[rows][keys]: A = Q (dO) rows read from
+//     LDS, B = the wave's K^T (V^T) slice, resident;
+//     dV^T += dO^T.P, dK^T += Q^T.dS as C[dims][keys]: A = the tile read
+//     transposed, B = P (dS) straight from the C registers of S.
+//   dQ kernel, per 32-key block of K / V:
+//     S^T = K.Q^T and dP^T = V.dO^T as C[keys][rows]: A = K (V) rows read from
+//     LDS, B = the wave's Q^T (dO^T) slice, resident;
+//     dQ^T += K^T.dS^T as C[dims][rows].
+// Q / dO (K / V) tiles go global -> registers -> LDS (XOR-swizzled rows,
+// D = 192 padded to 256 dimensions), two stages, with a barrier per block
+// plus one between the partial sums' stores and loads.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_kernel.h"
+#include "fa_mfma.h"
+
+namespace fa {
+namespace {
+
+using namespace mfma;
+
+struct WideArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* l2;     // [B][Hq][Sq]: LSE * log2(e)
+  const float* delta;  // [B][Hq][Sq]: rowsum(O * dO)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Sq, Skv, Hq, Hkv, causal, g;
+  float c;      // scale * log2(e)
+  float scale;
+};
+
+template <int D>
+struct Wide {
+  static constexpr int kWaves = D / 64;               // wave w owns dims 64w .. 64w+63
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kCPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int kNC = 32 * kCPR / kThreads;    // chunks per thread per 32-row tile
+  static constexpr int kTileBytes = 32 * lds_pitch<D>() * 2;
+  static constexpr int kStats = 2 * 32 * 4;           // l2 and delta of 32 rows (dK/dV kernel)
+  static constexpr int kStage = 2 * kTileBytes + kStats;
+  static constexpr int kPart = 2 * 64 * 16 * 4;       // one wave's partial S and dP
+  static constexpr int kLds = 2 * kStage + kWaves * kPart;
+  static_assert(D % 64 == 0 && 32 * kCPR % kThreads == 0, "tile chunks per thread");
+};
+
+template <typename T>
+__device__ __forceinline__ void store4(void* base, int64_t elem, const f32x16& acc, int i0,
+                                       float mul) {
+  s16x4 v = {T::cvt(acc[i0] * mul), T::cvt(acc[i0 + 1] * mul), T::cvt(acc[i0 + 2] * mul),
+             T::cvt(acc[i0 + 3] * mul)};
+  *reinterpret_cast<s16x4*>(static_cast<short*>(base) + elem) = v;
+}
+
+// Partial S and dP of this wave into the exchange area, then the sums of all
+// waves' partials (in wave order) back into s and dp.
+template <int D>
+__device__ __forceinline__ void exchange(char* xbase, int w, int lane, f32x16& s, f32x16& dp) {
+  using W = Wide<D>;
+  float* mine = reinterpret_cast<float*>(xbase + w * W::kPart) + lane * 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<f32x4*>(mine + 4 * j) = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+    *reinterpret_cast<f32x4*>(mine + 64 * 16 + 4 * j) =
+        f32x4{dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]};
+  }
+  __syncthreads();
+  s = zero16();
+  dp = zero16();
+#pragma unroll
+  for (int ww = 0; ww < W::kWaves; ++ww) {
+    const float* p = reinterpret_cast<const float*>(xbase + ww * W::kPart) + lane * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * j);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(p + 64 * 16 + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[4 * j + e] += a[e];
+        dp[4 * j + e] += b[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: a workgroup per (32-key block, batch, kv-head), the key blocks in
+// order (under a causal mask the first see the most rows); it streams every
+// 32-row block of every q-head of its group that sees one of its keys.
+template <typename T, int D>
+__global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
+  using W = Wide<D>;
+  __shared__ __attribute__((aligned(16))) char lds[W::kLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+
+  int idx = blockIdx.x;
+  const int hk = idx % a.Hkv;
+  idx /= a.Hkv;
+  const int b = idx % a.B;
+  const int j0 = 32 * (idx / a.B);
+  const int off = a.Skv - a.Sq;
+  const int64_t kvrow = (int64_t)a.Hkv * D, qrow = (int64_t)a.Hq * D;
+
+  // K^T and V^T of the wave's dimensions as B operands: lane holds
+  // K[j0 + l32][64w + 16t + 8h .. +7]
+  const int j = j0 + l32;
+  const bool key_ok = j < a.Skv;
+  s16x8 kB[4], vB[4];
+  {
+    const int64_t e = ((int64_t)b * a.Skv + (key_ok ? j : 0)) * kvrow + (int64_t)hk * D + 64 * w + 8 * h;
+    const s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      kB[t] = key_ok ? *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.k) + e + 16 * t) : z;
+      vB[t] = key_ok ? *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.v) + e + 16 * t) : z;
+    }
+  }
+  f32x16 dv[2] = {zero16(), zero16()}, dk[2] = {zero16(), zero16()};
+
+  // the 32-row blocks that see a key of the block: from the first row that
+  // sees key j0 to the last row, for each q-head of the group
+  const int i_first = a.causal ? (j0 - off > 0 ? j0 - off : 0) : 0;
+  const int nib = (a.Sq + 31) / 32;
+  const int ib0 = i_first / 32;
+  const int per_head = (j0 < a.Skv && i_first < a.Sq) ? nib - ib0 : 0;
+  const int nsteps = per_head * a.g;
+
+  u32x4 qr[W::kNC], dr[W::kNC];
+  float stat = 0.0f;
+  auto load = [&](int s) {
+    const int hq = hk * a.g + s / per_head;
+    const int ib = ib0 + s % per_head;
+    const int64_t base = ((int64_t)b * a.Sq) * qrow + (int64_t)hq * D;
+#pragma unroll
+    for (int u = 0; u < W::kNC; ++u) {
+      const int c = tid + W::kThreads * u;
+      const int r = c / W::kCPR, ch = c % W::kCPR;
+      const int i = 32 * ib + r;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const int64_t e = base + (int64_t)(i < a.Sq ? i : 0) * qrow + 8 * ch;
+      qr[u] = i < a.Sq ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.q) + e) : z;
+      dr[u] = i < a.Sq ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.dout) + e) : z;
+    }
+    if (tid < 64) {  // l2 (lanes 0-31) and delta (32-63) of the 32 rows
+      const int i = 32 * ib + l32;
+      const int64_t row = ((int64_t)b * a.Hq + hq) * a.Sq + (i < a.Sq ? i : 0);
+      stat = i < a.Sq ? (h == 0 ? a.l2[row] : a.delta[row]) : 0.0f;
+    }
+  };
+  auto store = [&](int stage) {
+    char* qt = lds + stage * W::kStage;
+#pragma unroll
+    for (int u = 0; u < W::kNC; ++u) {
+      const int c = tid + W::kThreads * u;
+      const int r = c / W::kCPR, ch = c % W::kCPR;
+      *reinterpret_cast<u32x4*>(qt + lds_off<D>(r, ch)) = qr[u];
+      *reinterpret_cast<u32x4*>(qt + W::kTileBytes + lds_off<D>(r, ch)) = dr[u];
+    }
+    if (tid < 64) reinterpret_cast<float*>(qt + 2 * W::kTileBytes)[tid] = stat;
+  };
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  char* xbase = lds + 2 * W::kStage;
+  for (int s = 0; s < nsteps; ++s) {
+    const int stage = s & 1;
+    if (s + 1 < nsteps) load(s + 1);
+    const char* qt = lds + stage * W::kStage;
+    const char* dt = qt + W::kTileBytes;
+    const float* st = reinterpret_cast<const float*>(qt + 2 * W::kTileBytes);
+    const int ib = ib0 + s % per_head;
+
+    // partial S and dP over the wave's dimensions, C[rows][keys]
+    f32x16 sv = zero16(), dpv = zero16();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sv = T::mma(read_rows<D>(qt, 0, 4 * w + t, lane), kB[t], sv);
+      dpv = T::mma(read_rows<D>(dt, 0, 4 * w + t, lane), vB[t], dpv);
+    }
+    exchange<D>(xbase, w, lane, sv, dpv);
+
+    // P and dS: lane = key j, register i = row 8(i/4) + 4h + i%4 of the block
+    f32x16 pv, dsv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
+      const int row = 32 * ib + rl;
+      const bool vis = key_ok & (row < a.Sq) & (!a.causal | (j <= row + off));
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.c, -st[rl]));
+      pv[i] = vis ? p : 0.0f;
+      dsv[i] = pv[i] * (dpv[i] - st[32 + rl]);
+    }
+    const s16x8 pb[2] = {pack_b<T>(pv, 0), pack_b<T>(pv, 1)};
+    const s16x8 sb[2] = {pack_b<T>(dsv, 0), pack_b<T>(dsv, 1)};
+    // dV^T += dO^T.P and dK^T += Q^T.dS over the wave's dimensions
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts) {
+        dv[d] = T::mma(read_a_rows<D>(dt, 0, ts, 64 * w + 32 * d, lane), pb[ts], dv[d]);
+        dk[d] = T::mma(read_a_rows<D>(qt, 0, ts, 64 * w + 32 * d, lane), sb[ts], dk[d]);
+      }
+
+    if (s + 1 < nsteps) store(stage ^ 1);
+    __syncthreads();
+  }
+
+  // dK = scale * (dK^T)^T, dV: lane = key, register i = dim 8(i/4) + 4h + i%4 of a 32-dim block
+  if (key_ok) {
+    const int64_t e = ((int64_t)b * a.Skv + j) * kvrow + (int64_t)hk * D + 64 * w + 4 * h;
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        store4<T>(a.dk, e + 32 * d + 8 * q, dk[d], 4 * q, a.scale);
+        store4<T>(a.dv, e + 32 * d + 8 * q, dv[d], 4 * q, 1.0f);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a workgroup per (32-row block, batch, q-head), the row blocks from the
+// last (under a causal mask the last rows see the most keys); it streams the
+// 32-key blocks of K and V its rows see.
+template <typename T, int D>
+__global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
+  using W = Wide<D>;
+  __shared__ __attribute__((aligned(16))) char lds[W::kLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+
+  int idx = blockIdx.x;
+  const int hq = idx % a.Hq;
+  idx /= a.Hq;
+  const int b = idx % a.B;
+  const int nib = (a.Sq + 31) / 32;
+  const int i0 = 32 * (nib - 1 - idx / a.B);
+  const int hk = hq / a.g;
+  const int off = a.Skv - a.Sq;
+  const int64_t kvrow = (int64_t)a.Hkv * D, qrow = (int64_t)a.Hq * D;
+
+  // Q^T and dO^T of the wave's dimensions as B operands: lane holds
+  // Q[i0 + l32][64w + 16t + 8h .. +7]
+  const int i = i0 + l32;
+  const bool row_ok = i < a.Sq;
+  s16x8 qB[4], oB[4];
+  {
+    const int64_t e = ((int64_t)b * a.Sq + (row_ok ? i : 0)) * qrow + (int64_t)hq * D + 64 * w + 8 * h;
+    const s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      qB[t] = row_ok ? *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.q) + e + 16 * t) : z;
+      oB[t] = row_ok ? *reinterpret_cast<const s16x8*>(static_cast<const short*>(a.dout) + e + 16 * t) : z;
+    }
+  }
+  const int64_t srow = ((int64_t)b * a.Hq + hq) * a.Sq + (row_ok ? i : 0);
+  const float l2v = row_ok ? a.l2[srow] : 0.0f;
+  const float dlv = row_ok ? a.delta[srow] : 0.0f;
+  f32x16 dq[2] = {zero16(), zero16()};
+
+  // the key blocks up to the last key a row of the block sees
+  const int last_row = (i0 + 31 < a.Sq ? i0 + 31 : a.Sq - 1);
+  int kend = a.Skv;
+  if (a.causal && last_row + off + 1 < kend) kend = last_row + off + 1;
+  const int nsteps = kend > 0 ? (kend + 31) / 32 : 0;
+
+  u32x4 kr[W::kNC], vr[W::kNC];
+  auto load = [&](int s) {
+    const int64_t base = ((int64_t)b * a.Skv) * kvrow + (int64_t)hk * D;
+#pragma unroll
+    for (int u = 0; u < W::kNC; ++u) {
+      const int c = tid + W::kThreads * u;
+      const int r = c / W::kCPR, ch = c % W::kCPR;
+      const int jj = 32 * s + r;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const int64_t e = base + (int64_t)(jj < a.Skv ? jj : 0) * kvrow + 8 * ch;
+      kr[u] = jj < a.Skv ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.k) + e) : z;
+      vr[u] = jj < a.Skv ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.v) + e) : z;
+    }
+  };
+  auto store = [&](int stage) {
+    char* kt = lds + stage * W::kStage;
+#pragma unroll
+    for (int u = 0; u < W::kNC; ++u) {
+      const int c = tid + W::kThreads * u;
+      const int r = c / W::kCPR, ch = c % W::kCPR;
+      *reinterpret_cast<u32x4*>(kt + lds_off<D>(r, ch)) = kr[u];
+      *reinterpret_cast<u32x4*>(kt + W::kTileBytes + lds_off<D>(r, ch)) = vr[u];
+    }
+  };
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  char* xbase = lds + 2 * W::kStage;
+  for (int s = 0; s < nsteps; ++s) {
+    const int stage = s & 1;
+    if (s + 1 < nsteps) load(s + 1);
+    const char* kt = lds + stage * W::kStage;
+    const char* vt = kt + W::kTileBytes;
+
+    // partial S^T and dP^T over the wave's dimensions, C[keys][rows]
+    f32x16 sv = zero16(), dpv = zero16();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sv = T::mma(read_rows<D>(kt, 0, 4 * w + t, lane), qB[t], sv);
+      dpv = T::mma(read_rows<D>(vt, 0, 4 * w + t, lane), oB[t], dpv);
+    }
+    exchange<D>(xbase, w, lane, sv, dpv);
+
+    // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
+    f32x16 dsv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
+      const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], a.c, -l2v));
+      dsv[r] = (vis ? p : 0.0f) * (dpv[r] - dlv);
+    }
+    const s16x8 sb[2] = {pack_b<T>(dsv, 0), pack_b<T>(dsv, 1)};
+    // dQ^T += K^T.dS^T over the wave's dimensions
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int ts = 0; ts < 2; ++ts)
+        dq[d] = T::mma(read_a_rows<D>(kt, 0, ts, 64 * w + 32 * d, lane), sb[ts], dq[d]);
+
+    if (s + 1 < nsteps) store(stage ^ 1);
+    __syncthreads();
+  }
+
+  // dQ = scale * (dQ^T)^T: lane = row, register r = dim 8(r/4) + 4h + r%4 of a 32-dim block
+  if (row_ok) {
+    const int64_t e = ((int64_t)b * a.Sq + i) * qrow + (int64_t)hq * D + 64 * w + 4 * h;
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store4<T>(a.dq, e + 32 * d + 8 * q, dq[d], 4 * q, a.scale);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_wide_d(const WideArgs& in, hipStream_t stream) {
+  using W = Wide<D>;
+  WideArgs a = in;
+  void* args[] = {&a};
+  const unsigned nkb = (unsigned)((a.Skv + 31) / 32), nib = (unsigned)((a.Sq + 31) / 32);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkv_wide<T, D>),
+                                 dim3(nkb * (unsigned)a.B * (unsigned)a.Hkv), dim3(W::kThreads), args,
+                                 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_wide<T, D>),
+                         dim3(nib * (unsigned)a.B * (unsigned)a.Hq), dim3(W::kThreads), args, 0,
+                         stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_wide(const BwdLaunchArgs& in) {
+  WideArgs a;
+  const size_t rows = (size_t)in.B * in.Hq * in.Sq;
+  a.q = in.q;
+  a.k = in.k;
+  a.v = in.v;
+  a.dout = in.dout;
+  a.l2 = in.ws;
+  a.delta = in.ws + rows;
+  a.dq = in.dq;
+  a.dk = in.dk;
+  a.dv = in.dv;
+  a.B = in.B;
+  a.Sq = in.Sq;
+  a.Skv = in.Skv;
+  a.Hq = in.Hq;
+  a.Hkv = in.Hkv;
+  a.causal = in.causal;
+  a.g = in.Hq / in.Hkv;
+  a.c = in.c;
+  a.scale = in.scale;
+  const bool bf = in.dtype == DType::kBF16;
+  if (in.D == 192) return bf ? launch_wide_d<BF16, 192>(a, in.stream) : launch_wide_d<F16, 192>(a, in.stream);
+  if (in.D == 256) return bf ? launch_wide_d<BF16, 256>(a, in.stream) : launch_wide_d<F16, 256>(a, in.stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

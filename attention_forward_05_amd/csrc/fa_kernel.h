@@ -104,6 +104,9 @@ struct BwdLaunchArgs {
 int launch_bwd(const BwdLaunchArgs& a);
 // The delta kernel alone: l2 and delta of every query row into a.ws.
 hipError_t launch_bwd_delta(const BwdLaunchArgs& a);
+// The dK/dV and dQ kernels for D = 192 and 256 (fa_bwd_wide.hip), after the
+// delta kernel.
+hipError_t launch_bwd_wide(const BwdLaunchArgs& a);
 
 // Argument checks shared by every forward entry point (no HIP call); on
 // FA_OK fills `a` (everything but ws / ws_bytes).

@@ -23,6 +23,7 @@ hipError_t launch_combine(DType, const float*, const float*, void*, float*, int,
 }
 hipError_t launch_tile(const LaunchArgs&, bool, bool, int, float*, float*) { return hipErrorInvalidValue; }
 hipError_t launch_bwd_delta(const BwdLaunchArgs&) { return hipErrorInvalidValue; }
+hipError_t launch_bwd_wide(const BwdLaunchArgs&) { return hipErrorInvalidValue; }
 }  // namespace fa
 
 static int failures = 0;
@@ -80,7 +81,7 @@ int main() {
          FA_ERR_INVALID);
   EXPECT(fa_bwd(0, Q, K, V, O, nullptr, G, DQ, DK, DV, 1, 128, 128, 4, 2, 128, 1, 0.1f, W, 1 << 20, 0),
          FA_ERR_INVALID);
-  EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 256, 1, 0.1f, W, 1 << 20, 0),
+  EXPECT(fa_bwd(0, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 96, 1, 0.1f, W, 1 << 20, 0),
          FA_ERR_UNSUPPORTED);
   EXPECT(fa_bwd(3, Q, K, V, O, L, G, DQ, DK, DV, 1, 128, 128, 4, 2, 128, 1, 0.1f, W, 1 << 20, 0),
          FA_ERR_INVALID);

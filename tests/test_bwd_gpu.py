@@ -77,6 +77,14 @@ BWD_CASES = [
     (2, 1, 4000, 16, 2, 128, True, "bf16"),    # one query row per sequence, GQA 8
     (1, 1024, 1024, 4, 4, 128, True, "f16"),   # several blocks each way
     (3, 77, 130, 2, 2, 64, False, "bf16"),
+    # head dimensions 192 and 256 (the HIP C++ gradient kernels, the head
+    # dimension split over the waves)
+    (1, 300, 300, 4, 4, 256, True, "bf16"),
+    (2, 200, 517, 8, 2, 192, True, "f16"),     # bottom-right, GQA 4, ragged
+    (1, 517, 200, 4, 1, 256, True, "f16"),     # rows without a visible key, GQA 4
+    (1, 333, 1000, 6, 3, 192, False, "bf16"),  # non-causal, GQA 2
+    (2, 1, 4000, 16, 2, 256, True, "bf16"),    # one query row per sequence, GQA 8
+    (3, 77, 130, 2, 2, 192, False, "f16"),
 ]
 
 
@@ -105,11 +113,15 @@ def test_backward_dead_rows_are_zero(fa):
     assert np.all(dq[:, :200] == 0.0)
 
 
+FULL_BWD = [workloads.WORKLOADS[2], workloads.WORKLOADS[3],
+            workloads.BY_NAME["causal_b1_h16_s4096_d256_bf16"]]
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("w", [workloads.WORKLOADS[2], workloads.WORKLOADS[3]],
-                         ids=[workloads.WORKLOADS[2].name, workloads.WORKLOADS[3].name])
+@pytest.mark.parametrize("w", FULL_BWD, ids=[w.name for w in FULL_BWD])
 def test_backward_full_size_sampled(fa, w):
-    """The backward of the S = 4096 and S = 8192 causal workloads at full size:
+    """The backward of the S = 4096 and S = 8192 causal workloads (and the
+    D = 256 one) at full size:
     dQ of sampled query rows and dK, dV of sampled key rows against the
     oracle (which computes LSE and delta of every row first)."""
     q, k, v = workloads.workload_inputs(w)
