@@ -183,7 +183,7 @@ int fa_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, void*
  *   dout        : dL/dO, [B,Sq,Hq,D]
  *   dq          : written, [B,Sq,Hq,D]
  *   dk, dv      : written, [B,Skv,Hkv,D]
- *   B .. scale  : as in fa_fwd; D = 64 or 128
+ *   B .. scale  : as in fa_fwd; D = 64, 128, 192 or 256
  *   workspace   : device memory of at least 8*B*Hq*Sq bytes, 16-byte aligned
  *                 (two fp32 per query row: LSE in log2 units and delta);
  *                 contents undefined after
@@ -192,7 +192,7 @@ int fa_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, void*
  * dq, dk, dv and the workspace must overlap neither each other nor any
  * input.  Asynchronous like fa_fwd; the library allocates nothing.  Returns
  * FA_OK, FA_ERR_INVALID (as fa_fwd, plus NULL o/lse/dout/dk/dv and the
- * overlaps above), FA_ERR_UNSUPPORTED (D not 64 or 128, one batch slice of
+ * overlaps above), FA_ERR_UNSUPPORTED (D not 64, 128, 192 or 256, one batch slice of
  * k or v of 2 GiB or more, and fa_fwd's limits), FA_ERR_WORKSPACE
  * (workspace NULL or smaller than 8*B*Hq*Sq bytes) or FA_ERR_HIP.
  */
