@@ -72,7 +72,7 @@ struct Wide {
   static constexpr int kStats = 2 * 32 * 4;           // l2 and delta of 32 rows (dK/dV kernel)
   static constexpr int kStage = 2 * kTileBytes + kStats;
   static constexpr int kPart = 2 * 64 * 16 * 4;       // one wave's partial S and dP
-  static constexpr int kLds = 2 * kStage + kWaves * kPart;
+  static constexpr int kLds = kStage + kWaves * kPart;  // small enough for two workgroups per CU
   static_assert(D % 64 == 0 && 32 * kCPR % kThreads == 0, "tile chunks per thread");
 };
 
@@ -197,11 +197,10 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
     store(0);
   }
   __syncthreads();
-  char* xbase = lds + 2 * W::kStage;
+  char* xbase = lds + W::kStage;
   for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
     if (s + 1 < nsteps) load(s + 1);
-    const char* qt = lds + stage * W::kStage;
+    const char* qt = lds;
     const char* dt = qt + W::kTileBytes;
     const float* st = reinterpret_cast<const float*>(qt + 2 * W::kTileBytes);
     const int ib = ib0 + s % per_head;
@@ -237,7 +236,10 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
         dk[d] = T::mma(read_a_rows<D>(qt, 0, ts, 64 * w + 32 * d, lane), sb[ts], dk[d]);
       }
 
-    if (s + 1 < nsteps) store(stage ^ 1);
+    if (s + 1 < nsteps) {
+      __syncthreads();  // every wave is done with this block's tiles
+      store(0);
+    }
     __syncthreads();
   }
 
@@ -330,11 +332,10 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
     store(0);
   }
   __syncthreads();
-  char* xbase = lds + 2 * W::kStage;
+  char* xbase = lds + W::kStage;
   for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
     if (s + 1 < nsteps) load(s + 1);
-    const char* kt = lds + stage * W::kStage;
+    const char* kt = lds;
     const char* vt = kt + W::kTileBytes;
 
     // partial S^T and dP^T over the wave's dimensions, C[keys][rows]
@@ -363,7 +364,10 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
       for (int ts = 0; ts < 2; ++ts)
         dq[d] = T::mma(read_a_rows<D>(kt, 0, ts, 64 * w + 32 * d, lane), sb[ts], dq[d]);
 
-    if (s + 1 < nsteps) store(stage ^ 1);
+    if (s + 1 < nsteps) {
+      __syncthreads();  // every wave is done with this block's tiles
+      store(0);
+    }
     __syncthreads();
   }
 
