@@ -32,8 +32,9 @@
 //     LDS, B = the wave's Q^T (dO^T) slice, resident;
 //     dQ^T += K^T.dS^T as C[dims][rows].
 // Q / dO (K / V) tiles go global -> registers -> LDS (XOR-swizzled rows,
-// D = 192 padded to 256 dimensions), two stages, with a barrier per block
-// plus one between the partial sums' stores and loads.
+// D = 192 padded to 256 dimensions), one stage, so that two workgroups
+// share a compute unit; barriers around the partial sums' reduction and
+// the next block's store.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -72,7 +73,8 @@ struct Wide {
   static constexpr int kStats = 2 * 32 * 4;           // l2 and delta of 32 rows (dK/dV kernel)
   static constexpr int kStage = 2 * kTileBytes + kStats;
   static constexpr int kPart = 2 * 64 * 16 * 4;       // one wave's partial S and dP
-  static constexpr int kLds = kStage + kWaves * kPart;  // small enough for two workgroups per CU
+  static constexpr int kPds = 2 * 16 * 64 * 4;        // P and dS after the reduction
+  static constexpr int kLds = kStage + kWaves * kPart + kPds;  // two workgroups fit a CU
   static_assert(D % 64 == 0 && 32 * kCPR % kThreads == 0, "tile chunks per thread");
 };
 
@@ -84,34 +86,43 @@ __device__ __forceinline__ void store4(void* base, int64_t elem, const f32x16& a
   *reinterpret_cast<s16x4*>(static_cast<short*>(base) + elem) = v;
 }
 
-// Partial S and dP of this wave into the exchange area, then the sums of all
-// waves' partials (in wave order) back into s and dp.
-template <int D>
-__device__ __forceinline__ void exchange(char* xbase, int w, int lane, f32x16& s, f32x16& dp) {
+// The waves' partial S and dP meet in LDS.  Wave w adds up, in wave order,
+// the registers i with i % kWaves == w, turns them into P and dS with
+// f(i, s, dp, p, ds), and stores those; after a barrier every wave reads
+// back all 16 registers of P and dS.  (Each wave reads a quarter of the
+// partials rather than all of them.)
+template <int D, typename F>
+__device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f32x16& s,
+                                           const f32x16& dp, f32x16& p, f32x16& ds, F&& f) {
   using W = Wide<D>;
-  float* mine = reinterpret_cast<float*>(xbase + w * W::kPart) + lane * 16;
+  float* x = reinterpret_cast<float*>(xbase);          // [wave][S, dP][register][lane]
+  float* y = x + W::kWaves * 2 * 16 * 64;               // [P, dS][register][lane]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<f32x4*>(mine + 4 * j) = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
-    *reinterpret_cast<f32x4*>(mine + 64 * 16 + 4 * j) =
-        f32x4{dp[4 * j], dp[4 * j + 1], dp[4 * j + 2], dp[4 * j + 3]};
+  for (int i = 0; i < 16; ++i) {
+    x[((2 * w) * 16 + i) * 64 + lane] = s[i];
+    x[((2 * w + 1) * 16 + i) * 64 + lane] = dp[i];
   }
   __syncthreads();
-  s = zero16();
-  dp = zero16();
 #pragma unroll
-  for (int ww = 0; ww < W::kWaves; ++ww) {
-    const float* p = reinterpret_cast<const float*>(xbase + ww * W::kPart) + lane * 16;
+  for (int i = 0; i < 16; ++i) {
+    if (i % W::kWaves == w) {
+      float ss = 0.0f, dd = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * j);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(p + 64 * 16 + 4 * j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[4 * j + e] += a[e];
-        dp[4 * j + e] += b[e];
+      for (int ww = 0; ww < W::kWaves; ++ww) {
+        ss += x[((2 * ww) * 16 + i) * 64 + lane];
+        dd += x[((2 * ww + 1) * 16 + i) * 64 + lane];
       }
+      float pp, dss;
+      f(i, ss, dd, pp, dss);
+      y[i * 64 + lane] = pp;
+      y[(16 + i) * 64 + lane] = dss;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = y[i * 64 + lane];
+    ds[i] = y[(16 + i) * 64 + lane];
   }
 }
 
@@ -212,19 +223,17 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
       sv = T::mma(read_rows<D>(qt, 0, 4 * w + t, lane), kB[t], sv);
       dpv = T::mma(read_rows<D>(dt, 0, 4 * w + t, lane), vB[t], dpv);
     }
-    exchange<D>(xbase, w, lane, sv, dpv);
-
     // P and dS: lane = key j, register i = row 8(i/4) + 4h + i%4 of the block
     f32x16 pv, dsv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
-      const int row = 32 * ib + rl;
-      const bool vis = key_ok & (row < a.Sq) & (!a.causal | (j <= row + off));
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.c, -st[rl]));
-      pv[i] = vis ? p : 0.0f;
-      dsv[i] = pv[i] * (dpv[i] - st[32 + rl]);
-    }
+    reduce_pds<D>(xbase, w, lane, sv, dpv, pv, dsv,
+                  [&](int i, float s_, float dp_, float& p_, float& ds_) {
+                    const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
+                    const int row = 32 * ib + rl;
+                    const bool vis = key_ok & (row < a.Sq) & (!a.causal | (j <= row + off));
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -st[rl]));
+                    p_ = vis ? e : 0.0f;
+                    ds_ = p_ * (dp_ - st[32 + rl]);
+                  });
     const s16x8 pb[2] = {pack_b<T>(pv, 0), pack_b<T>(pv, 1)};
     const s16x8 sb[2] = {pack_b<T>(dsv, 0), pack_b<T>(dsv, 1)};
     // dV^T += dO^T.P and dK^T += Q^T.dS over the wave's dimensions
@@ -345,17 +354,16 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
       sv = T::mma(read_rows<D>(kt, 0, 4 * w + t, lane), qB[t], sv);
       dpv = T::mma(read_rows<D>(vt, 0, 4 * w + t, lane), oB[t], dpv);
     }
-    exchange<D>(xbase, w, lane, sv, dpv);
-
     // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
-    f32x16 dsv;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
-      const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], a.c, -l2v));
-      dsv[r] = (vis ? p : 0.0f) * (dpv[r] - dlv);
-    }
+    f32x16 pv, dsv;
+    reduce_pds<D>(xbase, w, lane, sv, dpv, pv, dsv,
+                  [&](int r, float s_, float dp_, float& p_, float& ds_) {
+                    const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -l2v));
+                    p_ = vis ? e : 0.0f;
+                    ds_ = p_ * (dp_ - dlv);
+                  });
     const s16x8 sb[2] = {pack_b<T>(dsv, 0), pack_b<T>(dsv, 1)};
     // dQ^T += K^T.dS^T over the wave's dimensions
 #pragma unroll
