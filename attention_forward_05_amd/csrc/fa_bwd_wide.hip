@@ -73,7 +73,7 @@ struct Wide {
   static constexpr int kStats = 2 * 32 * 4;           // l2 and delta of 32 rows (dK/dV kernel)
   static constexpr int kStage = 2 * kTileBytes + kStats;
   static constexpr int kPart = 2 * 64 * 16 * 4;       // one wave's partial S and dP
-  static constexpr int kPds = 2 * 16 * 64 * 4;        // P and dS after the reduction
+  static constexpr int kPds = 2 * 2 * 64 * 16;        // P and dS operands after the reduction
   static constexpr int kLds = kStage + kWaves * kPart + kPds;  // two workgroups fit a CU
   static_assert(D % 64 == 0 && 32 * kCPR % kThreads == 0, "tile chunks per thread");
 };
@@ -88,15 +88,17 @@ __device__ __forceinline__ void store4(void* base, int64_t elem, const f32x16& a
 
 // The waves' partial S and dP meet in LDS.  Wave w adds up, in wave order,
 // the registers i with i % kWaves == w, turns them into P and dS with
-// f(i, s, dp, p, ds), and stores those; after a barrier every wave reads
-// back all 16 registers of P and dS.  (Each wave reads a quarter of the
-// partials rather than all of them.)
-template <int D, typename F>
+// f(i, s, dp, p, ds), and stores them rounded to the input dtype in the
+// layout of B operands; after a barrier every wave reads back the operands
+// of both k-steps: pb[t] (P, when kP) and sb[t] (dS).  Each wave reads a
+// quarter of the partials rather than all of them.
+template <typename T, int D, bool kP, typename F>
 __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f32x16& s,
-                                           const f32x16& dp, f32x16& p, f32x16& ds, F&& f) {
+                                           const f32x16& dp, s16x8 (&pb)[2], s16x8 (&sb)[2],
+                                           F&& f) {
   using W = Wide<D>;
-  float* x = reinterpret_cast<float*>(xbase);          // [wave][S, dP][register][lane]
-  float* y = x + W::kWaves * 2 * 16 * 64;               // [P, dS][register][lane]
+  float* x = reinterpret_cast<float*>(xbase);                 // [wave][S, dP][register][lane]
+  short* y = reinterpret_cast<short*>(x + W::kWaves * 2 * 16 * 64);  // [dS, P][k-step][lane][8]
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     x[((2 * w) * 16 + i) * 64 + lane] = s[i];
@@ -114,15 +116,16 @@ __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f
       }
       float pp, dss;
       f(i, ss, dd, pp, dss);
-      y[i * 64 + lane] = pp;
-      y[(16 + i) * 64 + lane] = dss;
+      // register i is element i % 8 of the B operand of k-step i / 8
+      y[(((i >> 3) * 64) + lane) * 8 + (i & 7)] = T::cvt(dss);
+      if constexpr (kP) y[(((2 + (i >> 3)) * 64) + lane) * 8 + (i & 7)] = T::cvt(pp);
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[i] = y[i * 64 + lane];
-    ds[i] = y[(16 + i) * 64 + lane];
+  for (int ts = 0; ts < 2; ++ts) {
+    sb[ts] = *reinterpret_cast<const s16x8*>(y + ((ts * 64) + lane) * 8);
+    if constexpr (kP) pb[ts] = *reinterpret_cast<const s16x8*>(y + (((2 + ts) * 64) + lane) * 8);
   }
 }
 
@@ -224,8 +227,8 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
       dpv = T::mma(read_rows<D>(dt, 0, 4 * w + t, lane), vB[t], dpv);
     }
     // P and dS: lane = key j, register i = row 8(i/4) + 4h + i%4 of the block
-    f32x16 pv, dsv;
-    reduce_pds<D>(xbase, w, lane, sv, dpv, pv, dsv,
+    s16x8 pb[2], sb[2];
+    reduce_pds<T, D, true>(xbase, w, lane, sv, dpv, pb, sb,
                   [&](int i, float s_, float dp_, float& p_, float& ds_) {
                     const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
                     const int row = 32 * ib + rl;
@@ -234,8 +237,6 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
                     p_ = vis ? e : 0.0f;
                     ds_ = p_ * (dp_ - st[32 + rl]);
                   });
-    const s16x8 pb[2] = {pack_b<T>(pv, 0), pack_b<T>(pv, 1)};
-    const s16x8 sb[2] = {pack_b<T>(dsv, 0), pack_b<T>(dsv, 1)};
     // dV^T += dO^T.P and dK^T += Q^T.dS over the wave's dimensions
 #pragma unroll
     for (int d = 0; d < 2; ++d)
@@ -355,8 +356,8 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
       dpv = T::mma(read_rows<D>(vt, 0, 4 * w + t, lane), oB[t], dpv);
     }
     // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
-    f32x16 pv, dsv;
-    reduce_pds<D>(xbase, w, lane, sv, dpv, pv, dsv,
+    s16x8 pb[2], sb[2];
+    reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, pb, sb,
                   [&](int r, float s_, float dp_, float& p_, float& ds_) {
                     const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
                     const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
@@ -364,7 +365,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
                     p_ = vis ? e : 0.0f;
                     ds_ = p_ * (dp_ - dlv);
                   });
-    const s16x8 sb[2] = {pack_b<T>(dsv, 0), pack_b<T>(dsv, 1)};
+    (void)pb;
     // dQ^T += K^T.dS^T over the wave's dimensions
 #pragma unroll
     for (int d = 0; d < 2; ++d)
