@@ -90,12 +90,11 @@ __device__ __forceinline__ void store4(void* base, int64_t elem, const f32x16& a
 // the registers i with i % kWaves == w, turns them into P and dS with
 // f(i, s, dp, p, ds), and stores them rounded to the input dtype in the
 // layout of B operands; after a barrier every wave reads back the operands
-// of both k-steps: pb[t] (P, when kP) and sb[t] (dS).  Each wave reads a
-// quarter of the partials rather than all of them.
+// of both k-steps: pb[t] (P, when kP; pb may be null otherwise) and sb[t]
+// (dS).  Each wave reads a quarter of the partials rather than all of them.
 template <typename T, int D, bool kP, typename F>
 __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f32x16& s,
-                                           const f32x16& dp, s16x8 (&pb)[2], s16x8 (&sb)[2],
-                                           F&& f) {
+                                           const f32x16& dp, s16x8* pb, s16x8 (&sb)[2], F&& f) {
   using W = Wide<D>;
   float* x = reinterpret_cast<float*>(xbase);                 // [wave][S, dP][register][lane]
   short* y = reinterpret_cast<short*>(x + W::kWaves * 2 * 16 * 64);  // [dS, P][k-step][lane][8]
@@ -356,8 +355,8 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
       dpv = T::mma(read_rows<D>(vt, 0, 4 * w + t, lane), oB[t], dpv);
     }
     // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
-    s16x8 pb[2], sb[2];
-    reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, pb, sb,
+    s16x8 sb[2];
+    reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, nullptr, sb,
                   [&](int r, float s_, float dp_, float& p_, float& ds_) {
                     const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
                     const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
@@ -365,7 +364,6 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
                     p_ = vis ? e : 0.0f;
                     ds_ = p_ * (dp_ - dlv);
                   });
-    (void)pb;
     // dQ^T += K^T.dS^T over the wave's dimensions
 #pragma unroll
     for (int d = 0; d < 2; ++d)
