@@ -214,7 +214,7 @@ enum {
   FA_KERNEL_TILE_KEYS = 3   /* one 32-row block, four waves over the keys: calls
                                with Sq <= 64 and Sq * Hq / Hkv <= 32 (decode) */
 };
-/* With Sq <= 64 (and D = 64 or 128) the rows of an item are (query, q-head)
+/* With Sq <= 64 the rows of an item are (query, q-head)
  * pairs of the q-heads of one kv-head, so K and V are read once per kv-head. */
 
 /*

@@ -179,9 +179,12 @@ TILE_PLAN_CASES = [
     (1, 1000, 1000, 8, 8, 256, 1, 2, 1),
     # D = 256, 8 items, 128 tiles of 64 keys -> 16 ranges of 8 tiles
     (1, 256, 8192, 4, 4, 256, 0, 2, 16),
-    # D = 192 (rows padded to 256 in LDS): the same plan as D = 256; few rows are not packed
+    # D = 192 (rows padded to 256 in LDS): the same plan as D = 256
     (1, 256, 8192, 4, 4, 192, 0, 2, 16),
-    (1, 1, 8192, 32, 8, 192, 1, 2, 8),
+    # decode at D = 192: the 4 q-heads of a kv-head packed into one row block
+    # (the row split: 128-key tiles of the key split do not fit the LDS),
+    # 8 items of 128 tiles -> 16 ranges
+    (1, 1, 8192, 32, 8, 192, 1, 2, 16),
     # D = 64 decode, g = 8: 4 items, 32 tiles -> 8 ranges (32 < 4 * 2 * 8)
     (2, 1, 4096, 16, 2, 64, 1, 3, 8),
 ]

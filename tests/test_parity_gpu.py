@@ -355,7 +355,8 @@ LARGE_D_CASES = [
     (2, 513, 777, 3, 3, False, "f16", False),     # ragged, Hq % 8 != 0
     (1, 256, 8192, 4, 4, False, "bf16", True),    # 16 key ranges merged
     (1, 200, 6000, 6, 2, True, "f16", True),      # split, bottom-right, GQA 3
-    (1, 40, 3000, 8, 1, True, "bf16", True),      # few rows (not packed at D = 256)
+    (1, 40, 3000, 8, 1, True, "bf16", True),      # few rows: 8 q-heads packed, 320 rows
+    (2, 1, 5000, 32, 4, True, "f16", True),       # decode, 8 q-heads packed into rows
 ]
 
 
