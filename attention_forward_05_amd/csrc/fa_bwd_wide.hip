@@ -86,38 +86,46 @@ __device__ __forceinline__ void store4(void* base, int64_t elem, const f32x16& a
   *reinterpret_cast<s16x4*>(static_cast<short*>(base) + elem) = v;
 }
 
-// The waves' partial S and dP meet in LDS.  Wave w adds up, in wave order,
-// the registers i with i % kWaves == w, turns them into P and dS with
+// The waves' partial S and dP meet in LDS, four registers (one group) to a
+// 16-byte word.  Wave w adds up, in wave order, the groups q with
+// q % kWaves == w, turns their registers i = 4q .. 4q+3 into P and dS with
 // f(i, s, dp, p, ds), and stores them rounded to the input dtype in the
 // layout of B operands; after a barrier every wave reads back the operands
 // of both k-steps: pb[t] (P, when kP; pb may be null otherwise) and sb[t]
-// (dS).  Each wave reads a quarter of the partials rather than all of them.
+// (dS).  Each wave reads only the groups it adds up.
 template <typename T, int D, bool kP, typename F>
 __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f32x16& s,
                                            const f32x16& dp, s16x8* pb, s16x8 (&sb)[2], F&& f) {
   using W = Wide<D>;
-  float* x = reinterpret_cast<float*>(xbase);                 // [wave][S, dP][register][lane]
-  short* y = reinterpret_cast<short*>(x + W::kWaves * 2 * 16 * 64);  // [dS, P][k-step][lane][8]
+  f32x4* x = reinterpret_cast<f32x4*>(xbase);                // [wave][S, dP][group][lane]
+  short* y = reinterpret_cast<short*>(x + W::kWaves * 2 * 4 * 64);  // [dS, P][k-step][lane][8]
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[((2 * w) * 16 + i) * 64 + lane] = s[i];
-    x[((2 * w + 1) * 16 + i) * 64 + lane] = dp[i];
+  for (int q = 0; q < 4; ++q) {
+    x[((2 * w) * 4 + q) * 64 + lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+    x[((2 * w + 1) * 4 + q) * 64 + lane] =
+        f32x4{dp[4 * q], dp[4 * q + 1], dp[4 * q + 2], dp[4 * q + 3]};
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (i % W::kWaves == w) {
-      float ss = 0.0f, dd = 0.0f;
+  for (int q = 0; q < 4; ++q) {
+    if (q % W::kWaves == w) {
+      f32x4 ss = x[(0 * 4 + q) * 64 + lane], dd = x[(1 * 4 + q) * 64 + lane];
 #pragma unroll
-      for (int ww = 0; ww < W::kWaves; ++ww) {
-        ss += x[((2 * ww) * 16 + i) * 64 + lane];
-        dd += x[((2 * ww + 1) * 16 + i) * 64 + lane];
+      for (int ww = 1; ww < W::kWaves; ++ww) {
+        ss += x[((2 * ww) * 4 + q) * 64 + lane];
+        dd += x[((2 * ww + 1) * 4 + q) * 64 + lane];
       }
-      float pp, dss;
-      f(i, ss, dd, pp, dss);
-      // register i is element i % 8 of the B operand of k-step i / 8
-      y[(((i >> 3) * 64) + lane) * 8 + (i & 7)] = T::cvt(dss);
-      if constexpr (kP) y[(((2 + (i >> 3)) * 64) + lane) * 8 + (i & 7)] = T::cvt(pp);
+      s16x4 po, so;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pp, dss;
+        f(4 * q + e, ss[e], dd[e], pp, dss);
+        so[e] = T::cvt(dss);
+        po[e] = T::cvt(pp);
+      }
+      // registers 4q .. 4q+3 are elements 4(q%2) .. +3 of the B operand of k-step q/2
+      *reinterpret_cast<s16x4*>(y + (((q >> 1) * 64) + lane) * 8 + 4 * (q & 1)) = so;
+      if constexpr (kP) *reinterpret_cast<s16x4*>(y + (((2 + (q >> 1)) * 64) + lane) * 8 + 4 * (q & 1)) = po;
     }
   }
   __syncthreads();
