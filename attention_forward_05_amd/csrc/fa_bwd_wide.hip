@@ -63,6 +63,9 @@ struct WideArgs {
   float scale;
 };
 
+// s_waitcnt vmcnt(0), the other counters left at their maxima
+constexpr int kVmcnt0 = 0x0F70;
+
 template <int D>
 struct Wide {
   static constexpr int kWaves = D / 64;               // wave w owns dims 64w .. 64w+63
@@ -179,26 +182,41 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
   const int per_head = (j0 < a.Skv && i_first < a.Sq) ? nib - ib0 : 0;
   const int nsteps = per_head * a.g;
 
+  // The thread's chunks of a tile: row rr[u] (the same in every tile) and
+  // element offset coff[u] within that row.  Rows past Sq read row Sq - 1
+  // again: finite data whose P and dS the mask sets to 0, so they add nothing
+  // to dK and dV.  Offsets from the tile's first row fit 32 bits: the rows
+  // stay inside one batch slice of q, below 2 GiB (the entry point checks).
+  int rr[W::kNC];
+  uint32_t coff[W::kNC];
+#pragma unroll
+  for (int u = 0; u < W::kNC; ++u) {
+    const int c = tid + W::kThreads * u;
+    rr[u] = c / W::kCPR;
+    coff[u] = 8 * (c % W::kCPR);
+  }
   u32x4 qr[W::kNC], dr[W::kNC];
   float stat = 0.0f;
-  auto load = [&](int s) {
-    const int hq = hk * a.g + s / per_head;
-    const int ib = ib0 + s % per_head;
-    const int64_t base = ((int64_t)b * a.Sq) * qrow + (int64_t)hq * D;
+  // (q-head, row block) of the next tile to load, advanced after each load
+  int lhq = hk * a.g, lib = ib0;
+  auto load = [&]() {
+    const int64_t base = ((int64_t)b * a.Sq + 32 * lib) * qrow + (int64_t)lhq * D;
+    const short* qp = static_cast<const short*>(a.q) + base;
+    const short* dp = static_cast<const short*>(a.dout) + base;
+    const int last = a.Sq - 1 - 32 * lib;  // last row of the tile inside Sq
 #pragma unroll
     for (int u = 0; u < W::kNC; ++u) {
-      const int c = tid + W::kThreads * u;
-      const int r = c / W::kCPR, ch = c % W::kCPR;
-      const int i = 32 * ib + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const int64_t e = base + (int64_t)(i < a.Sq ? i : 0) * qrow + 8 * ch;
-      qr[u] = i < a.Sq ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.q) + e) : z;
-      dr[u] = i < a.Sq ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.dout) + e) : z;
+      const uint32_t e = (uint32_t)min(rr[u], last) * (uint32_t)qrow + coff[u];
+      qr[u] = *reinterpret_cast<const u32x4*>(qp + e);
+      dr[u] = *reinterpret_cast<const u32x4*>(dp + e);
     }
     if (tid < 64) {  // l2 (lanes 0-31) and delta (32-63) of the 32 rows
-      const int i = 32 * ib + l32;
-      const int64_t row = ((int64_t)b * a.Hq + hq) * a.Sq + (i < a.Sq ? i : 0);
-      stat = i < a.Sq ? (h == 0 ? a.l2[row] : a.delta[row]) : 0.0f;
+      const int64_t row = ((int64_t)b * a.Hq + lhq) * a.Sq + 32 * lib + min(l32, last);
+      stat = h == 0 ? a.l2[row] : a.delta[row];
+    }
+    if (++lib == nib) {
+      lib = ib0;
+      ++lhq;
     }
   };
   auto store = [&](int stage) {
@@ -214,17 +232,21 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
   };
 
   if (nsteps > 0) {
-    load(0);
+    load();
     store(0);
   }
+  // Every load so far has landed (the resident operands included).  Said
+  // explicitly, so that the loop's first products do not wait for the
+  // next tile's loads, which the compiler cannot count across the branches.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   char* xbase = lds + W::kStage;
+  int ib = ib0;  // row block of the tile in LDS
   for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) load(s + 1);
+    if (s + 1 < nsteps) load();
     const char* qt = lds;
     const char* dt = qt + W::kTileBytes;
     const float* st = reinterpret_cast<const float*>(qt + 2 * W::kTileBytes);
-    const int ib = ib0 + s % per_head;
 
     // partial S and dP over the wave's dimensions, C[rows][keys]
     f32x16 sv = zero16(), dpv = zero16();
@@ -233,6 +255,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
       sv = T::mma(read_rows<D>(qt, 0, 4 * w + t, lane), kB[t], sv);
       dpv = T::mma(read_rows<D>(dt, 0, 4 * w + t, lane), vB[t], dpv);
     }
+    sched_reads_ahead<8, 4, 0>();
     // P and dS: lane = key j, register i = row 8(i/4) + 4h + i%4 of the block
     s16x8 pb[2], sb[2];
     reduce_pds<T, D, true>(xbase, w, lane, sv, dpv, pb, sb,
@@ -252,12 +275,14 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
         dv[d] = T::mma(read_a_rows<D>(dt, 0, ts, 64 * w + 32 * d, lane), pb[ts], dv[d]);
         dk[d] = T::mma(read_a_rows<D>(qt, 0, ts, 64 * w + 32 * d, lane), sb[ts], dk[d]);
       }
+    sched_reads_ahead<8, 3, 1, 2, 4>();  // after the four reads of P and dS
 
     if (s + 1 < nsteps) {
       __syncthreads();  // every wave is done with this block's tiles
       store(0);
     }
     __syncthreads();
+    if (++ib == nib) ib = ib0;
   }
 
   // dK = scale * (dK^T)^T, dV: lane = key, register i = dim 8(i/4) + 4h + i%4 of a 32-dim block
@@ -319,18 +344,30 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
   if (a.causal && last_row + off + 1 < kend) kend = last_row + off + 1;
   const int nsteps = kend > 0 ? (kend + 31) / 32 : 0;
 
+  // The thread's chunks of a tile: key row rr[u] of the tile and element
+  // offset coff[u] within that row.  Keys past Skv read key Skv - 1 again:
+  // finite data whose dS the mask sets to 0, so they add nothing to dQ.
+  // Offsets from the tile's first key fit 32 bits: the keys stay inside one
+  // batch slice of k, below 2 GiB (the entry point checks).
+  int rr[W::kNC];
+  uint32_t coff[W::kNC];
+#pragma unroll
+  for (int u = 0; u < W::kNC; ++u) {
+    const int c = tid + W::kThreads * u;
+    rr[u] = c / W::kCPR;
+    coff[u] = 8 * (c % W::kCPR);
+  }
   u32x4 kr[W::kNC], vr[W::kNC];
   auto load = [&](int s) {
-    const int64_t base = ((int64_t)b * a.Skv) * kvrow + (int64_t)hk * D;
+    const int64_t base = ((int64_t)b * a.Skv + 32 * s) * kvrow + (int64_t)hk * D;
+    const short* kp = static_cast<const short*>(a.k) + base;
+    const short* vp = static_cast<const short*>(a.v) + base;
+    const int last = a.Skv - 1 - 32 * s;  // last key of the tile inside Skv
 #pragma unroll
     for (int u = 0; u < W::kNC; ++u) {
-      const int c = tid + W::kThreads * u;
-      const int r = c / W::kCPR, ch = c % W::kCPR;
-      const int jj = 32 * s + r;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const int64_t e = base + (int64_t)(jj < a.Skv ? jj : 0) * kvrow + 8 * ch;
-      kr[u] = jj < a.Skv ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.k) + e) : z;
-      vr[u] = jj < a.Skv ? *reinterpret_cast<const u32x4*>(static_cast<const short*>(a.v) + e) : z;
+      const uint32_t e = (uint32_t)min(rr[u], last) * (uint32_t)kvrow + coff[u];
+      kr[u] = *reinterpret_cast<const u32x4*>(kp + e);
+      vr[u] = *reinterpret_cast<const u32x4*>(vp + e);
     }
   };
   auto store = [&](int stage) {
@@ -348,6 +385,10 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
     load(0);
     store(0);
   }
+  // Every load so far has landed (the resident operands included).  Said
+  // explicitly, so that the loop's first products do not wait for the
+  // next tile's loads, which the compiler cannot count across the branches.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   char* xbase = lds + W::kStage;
   for (int s = 0; s < nsteps; ++s) {
@@ -362,6 +403,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
       sv = T::mma(read_rows<D>(kt, 0, 4 * w + t, lane), qB[t], sv);
       dpv = T::mma(read_rows<D>(vt, 0, 4 * w + t, lane), oB[t], dpv);
     }
+    sched_reads_ahead<8, 4, 0>();
     // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
     s16x8 sb[2];
     reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, nullptr, sb,
@@ -378,6 +420,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
 #pragma unroll
       for (int ts = 0; ts < 2; ++ts)
         dq[d] = T::mma(read_a_rows<D>(kt, 0, ts, 64 * w + 32 * d, lane), sb[ts], dq[d]);
+    sched_reads_ahead<4, 3, 1, 2, 2>();  // after the two reads of dS
 
     if (s + 1 < nsteps) {
       __syncthreads();  // every wave is done with this block's tiles

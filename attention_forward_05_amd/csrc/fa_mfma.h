@@ -120,11 +120,13 @@ __device__ __forceinline__ s16x8 read_rows(const char* tile, int row0, int t, in
 // order a chain of N MFMAs whose operands come from N*R LDS reads so that
 // the reads of the first AHEAD MFMAs are issued before the first MFMA and
 // each MFMA is followed by the reads of a later one (the reads' latency then
-// hides behind the MFMAs instead of stalling each one).
-template <int N, int AHEAD, int GROUP, int R = 1>
+// hides behind the MFMAs instead of stalling each one).  EXTRA more reads of
+// the block (operands read before the chain) go first.
+template <int N, int AHEAD, int GROUP, int R = 1, int EXTRA = 0>
 __device__ __forceinline__ void sched_reads_ahead() {
   // masks of __builtin_amdgcn_sched_group_barrier: 0x008 MFMA, 0x100 DS read;
   // R reads per MFMA, AHEAD MFMAs' worth of reads issued first
+  if constexpr (EXTRA > 0) __builtin_amdgcn_sched_group_barrier(0x100, EXTRA, GROUP);
 #pragma unroll
   for (int i = 0; i < AHEAD && i < N; ++i) __builtin_amdgcn_sched_group_barrier(0x100, R, GROUP);
 #pragma unroll
