@@ -309,12 +309,15 @@ def cpu_baseline(w: workloads.Workload, q, k, v, target_s: float = 12.0):
 
     # widen once (not timed: the oracle's inputs are fp64 arrays)
     qd, kd, vd = oracle._f64(q), oracle._f64(k), oracle._f64(v)
-    pilot = 64
-    r, fl = rows_and_flops(pilot)
-    t0 = time.perf_counter()
-    oracle.attn_rows(qd, kd, vd, w.causal, w.scale, r)
-    t_pilot = max(time.perf_counter() - t0, 1e-3)
-    n = int(min(n_rows_total, max(pilot, pilot * target_s / t_pilot)))
+    # two pilots size the sample: 64 rows, then about a second's worth (the
+    # first overstates the time per row: thread start-up dominates it)
+    n = 64
+    for budget in (1.0, target_s):
+        r, fl = rows_and_flops(n)
+        t0 = time.perf_counter()
+        oracle.attn_rows(qd, kd, vd, w.causal, w.scale, r)
+        t_pilot = max(time.perf_counter() - t0, 1e-3)
+        n = int(min(n_rows_total, max(64, n * budget / t_pilot)))
     r, fl = rows_and_flops(n)
     t0 = time.perf_counter()
     oracle.attn_rows(qd, kd, vd, w.causal, w.scale, r)
