@@ -95,7 +95,8 @@ __device__ __forceinline__ void store4(void* base, int64_t elem, const f32x16& a
 // f(i, s, dp, p, ds), and stores them rounded to the input dtype in the
 // layout of B operands; after a barrier every wave reads back the operands
 // of both k-steps: pb[t] (P, when kP; pb may be null otherwise) and sb[t]
-// (dS).  Each wave reads only the groups it adds up.
+// (dS).  A wave stores only the groups other waves add up and reads only
+// the other waves' parts of its own groups.
 template <typename T, int D, bool kP, typename F>
 __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f32x16& s,
                                            const f32x16& dp, s16x8* pb, s16x8 (&sb)[2], F&& f) {
@@ -104,19 +105,24 @@ __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f
   short* y = reinterpret_cast<short*>(x + W::kWaves * 2 * 4 * 64);  // [dS, P][k-step][lane][8]
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    x[((2 * w) * 4 + q) * 64 + lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-    x[((2 * w + 1) * 4 + q) * 64 + lane] =
-        f32x4{dp[4 * q], dp[4 * q + 1], dp[4 * q + 2], dp[4 * q + 3]};
+    if (q % W::kWaves != w) {
+      x[((2 * w) * 4 + q) * 64 + lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+      x[((2 * w + 1) * 4 + q) * 64 + lane] =
+          f32x4{dp[4 * q], dp[4 * q + 1], dp[4 * q + 2], dp[4 * q + 3]};
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (q % W::kWaves == w) {
-      f32x4 ss = x[(0 * 4 + q) * 64 + lane], dd = x[(1 * 4 + q) * 64 + lane];
+      const f32x4 ms = {s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+      const f32x4 md = {dp[4 * q], dp[4 * q + 1], dp[4 * q + 2], dp[4 * q + 3]};
+      f32x4 ss = w == 0 ? ms : x[(0 * 4 + q) * 64 + lane];
+      f32x4 dd = w == 0 ? md : x[(1 * 4 + q) * 64 + lane];
 #pragma unroll
       for (int ww = 1; ww < W::kWaves; ++ww) {
-        ss += x[((2 * ww) * 4 + q) * 64 + lane];
-        dd += x[((2 * ww + 1) * 4 + q) * 64 + lane];
+        ss += ww == w ? ms : x[((2 * ww) * 4 + q) * 64 + lane];
+        dd += ww == w ? md : x[((2 * ww + 1) * 4 + q) * 64 + lane];
       }
       s16x4 po, so;
 #pragma unroll
