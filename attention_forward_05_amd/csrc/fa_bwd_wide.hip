@@ -264,15 +264,31 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
     sched_reads_ahead<8, 4, 0>();
     // P and dS: lane = key j, register i = row 8(i/4) + 4h + i%4 of the block
     s16x8 pb[2], sb[2];
-    reduce_pds<T, D, true>(xbase, w, lane, sv, dpv, pb, sb,
-                  [&](int i, float s_, float dp_, float& p_, float& ds_) {
-                    const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
-                    const int row = 32 * ib + rl;
-                    const bool vis = key_ok & (row < a.Sq) & (!a.causal | (j <= row + off));
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -st[rl]));
-                    p_ = vis ? e : 0.0f;
-                    ds_ = p_ * (dp_ - st[32 + rl]);
-                  });
+    // the block is fully visible (every key to every row): no mask
+    const bool full = (j0 + 31 < a.Skv) & (32 * ib + 31 < a.Sq) &
+                      (!a.causal | (j0 + 31 <= 32 * ib + off));
+    auto pds = [&](int i, float s_, float dp_, float& p_, float& ds_, bool masked) {
+      const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -st[rl]));
+      if (masked) {
+        const int row = 32 * ib + rl;
+        const bool vis = key_ok & (row < a.Sq) & (!a.causal | (j <= row + off));
+        p_ = vis ? e : 0.0f;
+      } else {
+        p_ = e;
+      }
+      ds_ = p_ * (dp_ - st[32 + rl]);
+    };
+    if (full)
+      reduce_pds<T, D, true>(xbase, w, lane, sv, dpv, pb, sb,
+                             [&](int i, float s_, float dp_, float& p_, float& ds_) {
+                               pds(i, s_, dp_, p_, ds_, false);
+                             });
+    else
+      reduce_pds<T, D, true>(xbase, w, lane, sv, dpv, pb, sb,
+                             [&](int i, float s_, float dp_, float& p_, float& ds_) {
+                               pds(i, s_, dp_, p_, ds_, true);
+                             });
     // dV^T += dO^T.P and dK^T += Q^T.dS over the wave's dimensions
 #pragma unroll
     for (int d = 0; d < 2; ++d)
@@ -412,14 +428,30 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
     sched_reads_ahead<8, 4, 0>();
     // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
     s16x8 sb[2];
-    reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, nullptr, sb,
-                  [&](int r, float s_, float dp_, float& p_, float& ds_) {
-                    const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -l2v));
-                    p_ = vis ? e : 0.0f;
-                    ds_ = p_ * (dp_ - dlv);
-                  });
+    // the block is fully visible (every key to every row): no mask
+    const bool full = (32 * s + 31 < a.Skv) & (i0 + 31 < a.Sq) &
+                      (!a.causal | (32 * s + 31 <= i0 + off));
+    auto pds = [&](int r, float s_, float dp_, float& p_, float& ds_, bool masked) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -l2v));
+      if (masked) {
+        const int key = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool vis = row_ok & (key < a.Skv) & (!a.causal | (key <= i + off));
+        p_ = vis ? e : 0.0f;
+      } else {
+        p_ = e;
+      }
+      ds_ = p_ * (dp_ - dlv);
+    };
+    if (full)
+      reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, nullptr, sb,
+                              [&](int r, float s_, float dp_, float& p_, float& ds_) {
+                                pds(r, s_, dp_, p_, ds_, false);
+                              });
+    else
+      reduce_pds<T, D, false>(xbase, w, lane, sv, dpv, nullptr, sb,
+                              [&](int r, float s_, float dp_, float& p_, float& ds_) {
+                                pds(r, s_, dp_, p_, ds_, true);
+                              });
     // dQ^T += K^T.dS^T over the wave's dimensions
 #pragma unroll
     for (int d = 0; d < 2; ++d)
