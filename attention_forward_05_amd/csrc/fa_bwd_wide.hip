@@ -146,21 +146,28 @@ __device__ __forceinline__ void reduce_pds(char* xbase, int w, int lane, const f
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: a workgroup per (32-key block, batch, kv-head), the key blocks in
+// dK / dV: a workgroup per (64-key block, batch, kv-head), the key blocks in
 // order (under a causal mask the first see the most rows); it streams every
-// 32-row block of every q-head of its group that sees one of its keys.
+// 32-row block of every q-head of its group that sees one of its keys.  Its
+// two halves of D/64 waves each take one 32-key block and share the tiles
+// (under a causal mask the second half's first row block is hidden from it).
 template <typename T, int D>
-__global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
+__global__ void __launch_bounds__(2 * Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
   using W = Wide<D>;
-  __shared__ __attribute__((aligned(16))) char lds[W::kLds];
+  constexpr int kThr = 2 * W::kThreads;             // two key blocks share the tiles
+  constexpr int kNC2 = 32 * W::kCPR / kThr;
+  constexpr int kExch = W::kWaves * W::kPart + W::kPds;
+  __shared__ __attribute__((aligned(16))) char lds[W::kStage + 2 * kExch];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int kb = wv / W::kWaves, w = wv % W::kWaves;
 
   int idx = blockIdx.x;
   const int hk = idx % a.Hkv;
   idx /= a.Hkv;
   const int b = idx % a.B;
-  const int j0 = 32 * (idx / a.B);
+  const int jp = 64 * (idx / a.B);
+  const int j0 = jp + 32 * kb;
   const int off = a.Skv - a.Sq;
   const int64_t kvrow = (int64_t)a.Hkv * D, qrow = (int64_t)a.Hq * D;
 
@@ -182,10 +189,10 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
 
   // the 32-row blocks that see a key of the block: from the first row that
   // sees key j0 to the last row, for each q-head of the group
-  const int i_first = a.causal ? (j0 - off > 0 ? j0 - off : 0) : 0;
+  const int i_first = a.causal ? (jp - off > 0 ? jp - off : 0) : 0;
   const int nib = (a.Sq + 31) / 32;
   const int ib0 = i_first / 32;
-  const int per_head = (j0 < a.Skv && i_first < a.Sq) ? nib - ib0 : 0;
+  const int per_head = (jp < a.Skv && i_first < a.Sq) ? nib - ib0 : 0;
   const int nsteps = per_head * a.g;
 
   // The thread's chunks of a tile: row rr[u] (the same in every tile) and
@@ -193,15 +200,15 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
   // again: finite data whose P and dS the mask sets to 0, so they add nothing
   // to dK and dV.  Offsets from the tile's first row fit 32 bits: the rows
   // stay inside one batch slice of q, below 2 GiB (the entry point checks).
-  int rr[W::kNC];
-  uint32_t coff[W::kNC];
+  int rr[kNC2];
+  uint32_t coff[kNC2];
 #pragma unroll
-  for (int u = 0; u < W::kNC; ++u) {
-    const int c = tid + W::kThreads * u;
+  for (int u = 0; u < kNC2; ++u) {
+    const int c = tid + kThr * u;
     rr[u] = c / W::kCPR;
     coff[u] = 8 * (c % W::kCPR);
   }
-  u32x4 qr[W::kNC], dr[W::kNC];
+  u32x4 qr[kNC2], dr[kNC2];
   float stat = 0.0f;
   // (q-head, row block) of the next tile to load, advanced after each load
   int lhq = hk * a.g, lib = ib0;
@@ -211,7 +218,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
     const short* dp = static_cast<const short*>(a.dout) + base;
     const int last = a.Sq - 1 - 32 * lib;  // last row of the tile inside Sq
 #pragma unroll
-    for (int u = 0; u < W::kNC; ++u) {
+    for (int u = 0; u < kNC2; ++u) {
       const uint32_t e = (uint32_t)min(rr[u], last) * (uint32_t)qrow + coff[u];
       qr[u] = *reinterpret_cast<const u32x4*>(qp + e);
       dr[u] = *reinterpret_cast<const u32x4*>(dp + e);
@@ -228,8 +235,8 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
   auto store = [&](int stage) {
     char* qt = lds + stage * W::kStage;
 #pragma unroll
-    for (int u = 0; u < W::kNC; ++u) {
-      const int c = tid + W::kThreads * u;
+    for (int u = 0; u < kNC2; ++u) {
+      const int c = tid + kThr * u;
       const int r = c / W::kCPR, ch = c % W::kCPR;
       *reinterpret_cast<u32x4*>(qt + lds_off<D>(r, ch)) = qr[u];
       *reinterpret_cast<u32x4*>(qt + W::kTileBytes + lds_off<D>(r, ch)) = dr[u];
@@ -246,7 +253,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
   // next tile's loads, which the compiler cannot count across the branches.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  char* xbase = lds + W::kStage;
+  char* xbase = lds + W::kStage + kb * kExch;
   int ib = ib0;  // row block of the tile in LDS
   for (int s = 0; s < nsteps; ++s) {
     if (s + 1 < nsteps) load();
@@ -265,8 +272,9 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dkv_wide(WideArgs a) {
     // P and dS: lane = key j, register i = row 8(i/4) + 4h + i%4 of the block
     s16x8 pb[2], sb[2];
     // the block is fully visible (every key to every row): no mask
-    const bool full = (j0 + 31 < a.Skv) & (32 * ib + 31 < a.Sq) &
-                      (!a.causal | (j0 + 31 <= 32 * ib + off));
+    // (judged for both key blocks, so that the workgroup takes one branch)
+    const bool full = (jp + 63 < a.Skv) & (32 * ib + 31 < a.Sq) &
+                      (!a.causal | (jp + 63 <= 32 * ib + off));
     auto pds = [&](int i, float s_, float dp_, float& p_, float& ds_, bool masked) {
       const int rl = 8 * (i >> 2) + 4 * h + (i & 3);
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -st[rl]));
@@ -482,9 +490,9 @@ hipError_t launch_wide_d(const WideArgs& in, hipStream_t stream) {
   using W = Wide<D>;
   WideArgs a = in;
   void* args[] = {&a};
-  const unsigned nkb = (unsigned)((a.Skv + 31) / 32), nib = (unsigned)((a.Sq + 31) / 32);
+  const unsigned nkp = (unsigned)((a.Skv + 63) / 64), nib = (unsigned)((a.Sq + 31) / 32);
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkv_wide<T, D>),
-                                 dim3(nkb * (unsigned)a.B * (unsigned)a.Hkv), dim3(W::kThreads), args,
+                                 dim3(nkp * (unsigned)a.B * (unsigned)a.Hkv), dim3(2 * W::kThreads), args,
                                  0, stream);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_wide<T, D>),
