@@ -31,10 +31,11 @@
 //     S^T = K.Q^T and dP^T = V.dO^T as C[keys][rows]: A = K (V) rows read from
 //     LDS, B = the wave's Q^T (dO^T) slice, resident;
 //     dQ^T += K^T.dS^T as C[dims][rows].
-// Q / dO (K / V) tiles go global -> registers -> LDS (XOR-swizzled rows,
-// D = 192 padded to 256 dimensions), one stage, so that two workgroups
-// share a compute unit; barriers around the partial sums' reduction and
-// the next block's store.
+// A workgroup has two halves of D/64 waves: each takes one 32-key (dK/dV)
+// or 32-row (dQ) block, and both read the same streamed tiles.  Q / dO
+// (K / V) tiles go global -> registers -> LDS (XOR-swizzled rows, D = 192
+// padded to 256 dimensions), one stage; barriers around the partial sums'
+// reduction and the next block's store.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -77,7 +78,9 @@ struct Wide {
   static constexpr int kStage = 2 * kTileBytes + kStats;
   static constexpr int kPart = 2 * 64 * 16 * 4;       // one wave's partial S and dP
   static constexpr int kPds = 2 * 2 * 64 * 16;        // P and dS operands after the reduction
-  static constexpr int kLds = kStage + kWaves * kPart + kPds;  // two workgroups fit a CU
+  // a workgroup: two halves of kWaves waves, one stage of tiles and an
+  // exchange area (kWaves * kPart + kPds) per half: 88 KB of LDS at D = 192,
+  // 104 KB at D = 256
   static_assert(D % 64 == 0 && 32 * kCPR % kThreads == 0, "tile chunks per thread");
 };
 
@@ -329,22 +332,29 @@ __global__ void __launch_bounds__(2 * Wide<D>::kThreads) bwd_dkv_wide(WideArgs a
 }
 
 // ---------------------------------------------------------------------------
-// dQ: a workgroup per (32-row block, batch, q-head), the row blocks from the
+// dQ: a workgroup per (64-row block, batch, q-head), the row blocks from the
 // last (under a causal mask the last rows see the most keys); it streams the
-// 32-key blocks of K and V its rows see.
+// 32-key blocks of K and V its rows see.  Its two halves of D/64 waves each
+// take one 32-row block and share the tiles (under a causal mask the first
+// half's last key block is hidden from it).
 template <typename T, int D>
-__global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
+__global__ void __launch_bounds__(2 * Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
   using W = Wide<D>;
-  __shared__ __attribute__((aligned(16))) char lds[W::kLds];
+  constexpr int kThr = 2 * W::kThreads;             // two row blocks share the tiles
+  constexpr int kNC2 = 32 * W::kCPR / kThr;
+  constexpr int kExch = W::kWaves * W::kPart + W::kPds;
+  __shared__ __attribute__((aligned(16))) char lds[W::kStage + 2 * kExch];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int kb = wv / W::kWaves, w = wv % W::kWaves;
 
   int idx = blockIdx.x;
   const int hq = idx % a.Hq;
   idx /= a.Hq;
   const int b = idx % a.B;
-  const int nib = (a.Sq + 31) / 32;
-  const int i0 = 32 * (nib - 1 - idx / a.B);
+  const int nip = (a.Sq + 63) / 64;
+  const int ip = 64 * (nip - 1 - idx / a.B);  // first row of the pair
+  const int i0 = ip + 32 * kb;
   const int hk = hq / a.g;
   const int off = a.Skv - a.Sq;
   const int64_t kvrow = (int64_t)a.Hkv * D, qrow = (int64_t)a.Hq * D;
@@ -368,8 +378,8 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
   const float dlv = row_ok ? a.delta[srow] : 0.0f;
   f32x16 dq[2] = {zero16(), zero16()};
 
-  // the key blocks up to the last key a row of the block sees
-  const int last_row = (i0 + 31 < a.Sq ? i0 + 31 : a.Sq - 1);
+  // the key blocks up to the last key a row of the pair sees
+  const int last_row = (ip + 63 < a.Sq ? ip + 63 : a.Sq - 1);
   int kend = a.Skv;
   if (a.causal && last_row + off + 1 < kend) kend = last_row + off + 1;
   const int nsteps = kend > 0 ? (kend + 31) / 32 : 0;
@@ -379,22 +389,22 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
   // finite data whose dS the mask sets to 0, so they add nothing to dQ.
   // Offsets from the tile's first key fit 32 bits: the keys stay inside one
   // batch slice of k, below 2 GiB (the entry point checks).
-  int rr[W::kNC];
-  uint32_t coff[W::kNC];
+  int rr[kNC2];
+  uint32_t coff[kNC2];
 #pragma unroll
-  for (int u = 0; u < W::kNC; ++u) {
-    const int c = tid + W::kThreads * u;
+  for (int u = 0; u < kNC2; ++u) {
+    const int c = tid + kThr * u;
     rr[u] = c / W::kCPR;
     coff[u] = 8 * (c % W::kCPR);
   }
-  u32x4 kr[W::kNC], vr[W::kNC];
+  u32x4 kr[kNC2], vr[kNC2];
   auto load = [&](int s) {
     const int64_t base = ((int64_t)b * a.Skv + 32 * s) * kvrow + (int64_t)hk * D;
     const short* kp = static_cast<const short*>(a.k) + base;
     const short* vp = static_cast<const short*>(a.v) + base;
     const int last = a.Skv - 1 - 32 * s;  // last key of the tile inside Skv
 #pragma unroll
-    for (int u = 0; u < W::kNC; ++u) {
+    for (int u = 0; u < kNC2; ++u) {
       const uint32_t e = (uint32_t)min(rr[u], last) * (uint32_t)kvrow + coff[u];
       kr[u] = *reinterpret_cast<const u32x4*>(kp + e);
       vr[u] = *reinterpret_cast<const u32x4*>(vp + e);
@@ -403,8 +413,8 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
   auto store = [&](int stage) {
     char* kt = lds + stage * W::kStage;
 #pragma unroll
-    for (int u = 0; u < W::kNC; ++u) {
-      const int c = tid + W::kThreads * u;
+    for (int u = 0; u < kNC2; ++u) {
+      const int c = tid + kThr * u;
       const int r = c / W::kCPR, ch = c % W::kCPR;
       *reinterpret_cast<u32x4*>(kt + lds_off<D>(r, ch)) = kr[u];
       *reinterpret_cast<u32x4*>(kt + W::kTileBytes + lds_off<D>(r, ch)) = vr[u];
@@ -420,7 +430,7 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
   // next tile's loads, which the compiler cannot count across the branches.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  char* xbase = lds + W::kStage;
+  char* xbase = lds + W::kStage + kb * kExch;
   for (int s = 0; s < nsteps; ++s) {
     if (s + 1 < nsteps) load(s + 1);
     const char* kt = lds;
@@ -437,8 +447,9 @@ __global__ void __launch_bounds__(Wide<D>::kThreads) bwd_dq_wide(WideArgs a) {
     // dS^T: lane = row i, register r = key 8(r/4) + 4h + r%4 of the block
     s16x8 sb[2];
     // the block is fully visible (every key to every row): no mask
-    const bool full = (32 * s + 31 < a.Skv) & (i0 + 31 < a.Sq) &
-                      (!a.causal | (32 * s + 31 <= i0 + off));
+    // (judged for both row blocks, so that the workgroup takes one branch)
+    const bool full = (32 * s + 31 < a.Skv) & (ip + 63 < a.Sq) &
+                      (!a.causal | (32 * s + 31 <= ip + off));
     auto pds = [&](int r, float s_, float dp_, float& p_, float& ds_, bool masked) {
       const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_, a.c, -l2v));
       if (masked) {
@@ -490,13 +501,13 @@ hipError_t launch_wide_d(const WideArgs& in, hipStream_t stream) {
   using W = Wide<D>;
   WideArgs a = in;
   void* args[] = {&a};
-  const unsigned nkp = (unsigned)((a.Skv + 63) / 64), nib = (unsigned)((a.Sq + 31) / 32);
+  const unsigned nkp = (unsigned)((a.Skv + 63) / 64), nip = (unsigned)((a.Sq + 63) / 64);
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkv_wide<T, D>),
                                  dim3(nkp * (unsigned)a.B * (unsigned)a.Hkv), dim3(2 * W::kThreads), args,
                                  0, stream);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_wide<T, D>),
-                         dim3(nib * (unsigned)a.B * (unsigned)a.Hq), dim3(W::kThreads), args, 0,
+                         dim3(nip * (unsigned)a.B * (unsigned)a.Hq), dim3(2 * W::kThreads), args, 0,
                          stream);
 }
 
