@@ -85,6 +85,12 @@ BWD_CASES = [
     (1, 333, 1000, 6, 3, 192, False, "bf16"),  # non-causal, GQA 2
     (2, 1, 4000, 16, 2, 256, True, "bf16"),    # one query row per sequence, GQA 8
     (3, 77, 130, 2, 2, 192, False, "f16"),
+    # workgroups of two 32-key (dK/dV) or 32-row (dQ) halves: fewer keys and
+    # rows than one half, exact multiples of a pair, and a pair whose second
+    # half is past the end
+    (1, 20, 12, 2, 1, 256, True, "bf16"),      # Sq, Skv < 32: one half idle
+    (2, 128, 128, 4, 4, 192, False, "f16"),    # whole pairs
+    (1, 160, 96, 8, 2, 256, True, "f16"),      # last pair half empty, GQA 4
 ]
 
 
